@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the im2win forward convolution on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input, through the
+C ABI on one HIP stream: the im2win repack (conv_im2win_transform) and the
+windowed contraction with its bias epilogue (conv2d_fwd / conv2d_dw_fwd on the
+ready window tensor).  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line: TFLOP/s of the step (2*N*K*(C/G)*R*S*P*Q per second),
+the dominant kernel's roofline position (timed with HIP events on its launch
+stream), and the CPU oracle's throughput on the host cores.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers]
+
+--workload picks one of the five synthetic layers (default: the 1x512x13x13
+-> 1024, 3x3 layer); --layers adds a per-layer summary of all five.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "conv2d fwd TFLOP/s (2NKCRSPQ/s) and % of MI355X MFMA/HBM roofline"
+
+# MI355X published peaks (dense)
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"mfma_f16": 2516.6, "mfma_bf16": 2516.6, "valu_f32": 157.3}
+# The OpenCL-Benchmarks page times exactly the 1x512x13x13 -> 1024 3x3 layer
+# (direct convolution, Mali T860): 913.301 ms run time.  Context only.
+PAGE_BASELINE = {"mid_3x3_fp32": 2 * 1024 * 512 * 9 * 169 / 913.301e-3 / 1e12}
+
+DEFAULT_WORKLOAD = "mid_3x3_fp32"
+
+
+def describe(L: workloads.Layer) -> str:
+    return (f"{L.name}: N={L.N} C={L.C} H={L.H} W={L.W} K={L.K} {L.R}x{L.S} "
+            f"stride={L.stride[0]} pad={L.pad[0]} groups={L.groups} {L.dtype}->{L.out_dtype}"
+            f"{' bias' if L.b_dist is not None else ''}")
+
+
+class Step:
+    """Pre-marshalled C-ABI calls for one layer (argument marshalling happens
+    once, outside the timed region)."""
+
+    def __init__(self, L: workloads.Layer):
+        import numpy as np  # noqa: F401
+        import torch
+        import cnn_convolution_im2win_amd as ciw
+        from cnn_convolution_im2win_amd import _lib
+
+        self.L = L
+        self.ciw = ciw
+        self.lib = _lib.load()
+        code = {"f32": ciw.CIW_F32, "f16": ciw.CIW_F16, "bf16": ciw.CIW_BF16}
+        self.in_code, self.out_code = code[L.dtype], code[L.out_dtype]
+        x, w, b = workloads.make_inputs(L)
+
+        def dev(a):
+            if a is None:
+                return None
+            t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if L.dtype == "bf16" else a))
+            t = t.to("cuda")
+            return t.view(torch.bfloat16) if L.dtype == "bf16" else t
+
+        self.x, self.w, self.b = dev(x), dev(w), dev(b)
+        self.desc = ciw.make_desc(L.x_shape, L.w_shape, L.stride, L.pad, L.dil, L.groups)
+        self.depthwise = L.groups > 1
+        self.layout = ciw.CIW_WIN_HWC if (L.dtype != "f32" and not self.depthwise) else ciw.CIW_WIN_CHW
+        self.P, self.Q = ciw.conv_im2win_output_dims(self.desc)
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+        self.y = torch.empty((L.N, L.K, self.P, self.Q), dtype=tdt[L.out_dtype], device="cuda")
+        self.ws_bytes = ciw.conv2d_workspace_bytes(self.desc, self.in_code, L.N)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        self.win_bytes = ciw.conv_im2win_window_bytes(self.desc, self.in_code, self.layout, L.N)
+        self.stream = torch.cuda.current_stream()
+        self.sp = self.stream.cuda_stream
+        self.fn = self.lib.conv2d_dw_fwd if self.depthwise else self.lib.conv2d_fwd
+        self.dref = ctypes.byref(self.desc)
+        self.args_fwd = (self.dref, self.in_code, self.out_code, None, self.w.data_ptr(),
+                         None if self.b is None else self.b.data_ptr(), self.y.data_ptr(),
+                         self.ws.data_ptr(), self.ws_bytes, ciw.CIW_FLAG_WINDOW_READY, self.sp)
+        self.args_tr = (self.dref, self.in_code, self.layout, self.x.data_ptr(),
+                        self.ws.data_ptr(), self.sp)
+
+    def transform(self):
+        st = self.lib.conv_im2win_transform(*self.args_tr)
+        if st != 0:
+            raise RuntimeError(f"conv_im2win_transform: status {st}")
+
+    def contract(self):
+        st = self.fn(*self.args_fwd)
+        if st != 0:
+            raise RuntimeError(f"conv2d_fwd: status {st}")
+
+    # ---- algorithmic work
+    def flops(self) -> int:
+        L = self.L
+        return 2 * L.N * L.K * (L.C // L.groups) * L.R * L.S * self.P * self.Q
+
+    def bytes_x(self):
+        return self.x.numel() * self.x.element_size()
+
+    def bytes_w(self):
+        return self.w.numel() * self.w.element_size()
+
+    def bytes_b(self):
+        return 0 if self.b is None else self.b.numel() * self.b.element_size()
+
+    def bytes_y(self):
+        return self.y.numel() * self.y.element_size()
+
+    def contraction_bytes(self):
+        # window tensor read once, filters and bias once, output written once
+        return self.win_bytes + self.bytes_w() + self.bytes_b() + self.bytes_y()
+
+    def transform_bytes(self):
+        return self.bytes_x() + self.win_bytes
+
+    def contraction_roofline(self, kernel_ms: float) -> dict:
+        """Roofline position of the contraction kernel: compute-bound when its
+        arithmetic intensity is above the ridge, else bound by HBM."""
+        L = self.L
+        if self.depthwise:
+            peak_c, unit_c = PEAK_TFLOPS["valu_f32"], "alu"
+        elif L.dtype == "f32":
+            peak_c, unit_c = PEAK_TFLOPS["valu_f32"], "alu"
+        else:
+            peak_c, unit_c = PEAK_TFLOPS["mfma_" + L.dtype], "mfma"
+        ai = self.flops() / self.contraction_bytes()
+        ridge = peak_c * 1e12 / (PEAK_HBM_GBS * 1e9)
+        s = kernel_ms * 1e-3
+        if ai >= ridge:
+            ach = self.flops() / s / 1e12
+            return {"bound": unit_c, "achieved": round(ach, 3), "peak": peak_c,
+                    "unit": "TFLOP/s", "frac": round(ach / peak_c, 4), "traffic": None}
+        ach = self.contraction_bytes() / s / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+
+
+def time_steps(step: Step, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        step.transform()
+        step.contract()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        e = ev[i]
+        e[0].record(step.stream)
+        step.transform()
+        e[1].record(step.stream)
+        step.contract()
+        e[2].record(step.stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tr = [e[0].elapsed_time(e[1]) for e in ev]
+    co = [e[1].elapsed_time(e[2]) for e in ev]
+    return (t1 - t0) * 1e3 / steps, tr, co
+
+
+def cpu_baseline(L: workloads.Layer, seconds: float) -> dict:
+    """The CPU oracle (fp64 direct convolution, OpenMP over (n, k)) on a
+    bounded sample of the layer: whole images, as many as fit ~`seconds`."""
+    import numpy as np
+    import oracle
+    x, w, b = workloads.make_inputs(L)
+    f = lambda a: None if a is None else workloads.to_f64(a, L.dtype)
+    x, w, b = f(x), f(w), f(b)
+    P, Q = oracle.out_dims(L.x_shape, L.w_shape, L.stride, L.pad, L.dil, L.groups)
+    flops_img = 2 * L.K * (L.C // L.groups) * L.R * L.S * P * Q
+    t0 = time.perf_counter()
+    oracle.conv2d(x[:1], w, b, L.stride, L.pad, L.dil, L.groups)
+    one = time.perf_counter() - t0
+    reps, n_img = 1, 1
+    if one < seconds:
+        want = max(1, int(seconds / max(one, 1e-6)))
+        n_img = min(L.N, want)
+        reps = max(1, want // n_img)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.conv2d(x[:n_img], w, b, L.stride, L.pad, L.dil, L.groups)
+    dt = time.perf_counter() - t0
+    tflops = flops_img * n_img * reps / dt / 1e12
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_img} of {L.N} images x {reps} repeats ({dt:.1f} s wall); "
+                      f"fp64 seven-loop direct convolution"}
+
+
+def measure_layer(L: workloads.Layer, steps: int, warmup: int) -> dict:
+    import statistics
+    step = Step(L)
+    ms, tr, co = time_steps(step, steps, warmup)
+    tr_ms, co_ms = statistics.mean(tr), statistics.mean(co)
+    res = {
+        "step_ms": round(ms, 5),
+        "tflops": round(step.flops() / (ms * 1e-3) / 1e12, 3),
+        "transform_ms": round(tr_ms, 5),
+        "transform_gbs": round(step.transform_bytes() / (tr_ms * 1e-3) / 1e9, 1),
+        "contract_ms": round(co_ms, 5),
+        "contract_min_ms": round(min(co), 5),
+        "contract_tflops": round(step.flops() / (co_ms * 1e-3) / 1e12, 3),
+        "contract_gbs": round(step.contraction_bytes() / (co_ms * 1e-3) / 1e9, 1),
+        "roofline": step.contraction_roofline(co_ms),
+    }
+    if not step.depthwise and L.dtype != "f32":
+        res["mfma_frac"] = round(res["contract_tflops"] / PEAK_TFLOPS["mfma_" + L.dtype], 4)
+    return res, step
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=workloads.LAYER_ORDER)
+    ap.add_argument("--layers", action="store_true", help="also summarise all five layers")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): this "
+              "library has no multi-GPU path; the per-GPU throughput at N=1 is the figure.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    L = workloads.LAYERS[args.workload]
+    print(f"# measuring {describe(L)}: {args.warmup} warmup + {args.steps} steps", file=sys.stderr,
+          flush=True)
+    res, step = measure_layer(L, args.steps, args.warmup)
+    print(f"# {json.dumps(res)}", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        bb = torch.empty_like(a)
+        for _ in range(3):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+
+    layers = None
+    if args.layers:
+        layers = {}
+        for name in workloads.LAYER_ORDER:
+            if name == args.workload:
+                layers[name] = res
+                continue
+            print(f"# measuring {name}", file=sys.stderr, flush=True)
+            r, _ = measure_layer(workloads.LAYERS[name], max(10, args.steps // 5), 5)
+            layers[name] = r
+            print(f"# {name}: {json.dumps(r)}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(L, args.cpu_seconds)
+
+    value = step.flops() / (res["step_ms"] * 1e-3) / 1e12
+    page = PAGE_BASELINE.get(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / page, 1) if page else None,
+        "dtype": L.dtype,
+        "data": "synthetic",
+        "config": {"workload": describe(L), "global_batch": L.N,
+                   "step": "conv_im2win_transform + conv2d_fwd(window ready)",
+                   "transform_ms": res["transform_ms"], "contract_ms": res["contract_ms"]},
+        "roofline": res["roofline"],
+        "cpu_baseline": cpu,
+    }
+    if layers is not None:
+        out["layers"] = layers
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,102 @@
+"""ctypes view of the C ABI in include/conv_im2win.h (no logic of its own).
+
+The shared library is ``libconv_im2win.so`` next to this file, built by
+``cnn_convolution_im2win_amd.build``.  There is no fallback: if it is
+missing, every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconv_im2win.so")
+
+CIW_OK = 0
+CIW_ERR_INVALID_ARG = -1
+CIW_ERR_UNSUPPORTED = -2
+CIW_ERR_WORKSPACE = -3
+CIW_ERR_HIP = -4
+
+CIW_F32, CIW_F16, CIW_BF16 = 0, 1, 2
+CIW_WIN_CHW, CIW_WIN_HWC = 0, 1
+
+CIW_FLAG_WINDOW_READY = 0x1
+CIW_FLAG_NO_SPLIT = 0x2
+CIW_FLAG_GENERIC = 0x4
+
+# the exported entry points, in header order
+ENTRY_POINTS = (
+    "conv_im2win_output_dims",
+    "conv_im2win_window_geometry",
+    "conv_im2win_window_bytes",
+    "conv_im2win_transform",
+    "conv2d_workspace_bytes",
+    "conv2d_fwd",
+    "conv2d_dw_fwd",
+    "conv_im2win_status_string",
+)
+
+
+class ConvDesc(ctypes.Structure):
+    """Mirror of ciw_conv_desc."""
+    _fields_ = [
+        ("N", ctypes.c_int64), ("C", ctypes.c_int64), ("H", ctypes.c_int64),
+        ("W", ctypes.c_int64), ("K", ctypes.c_int64), ("R", ctypes.c_int64),
+        ("S", ctypes.c_int64),
+        ("stride_h", ctypes.c_int32), ("stride_w", ctypes.c_int32),
+        ("pad_h", ctypes.c_int32), ("pad_w", ctypes.c_int32),
+        ("dil_h", ctypes.c_int32), ("dil_w", ctypes.c_int32),
+        ("groups", ctypes.c_int32),
+    ]
+
+
+class Im2winError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load():
+    """Open the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m cnn_convolution_im2win_amd.build` "
+            "(or __graft_entry__.build()); there is no CPU fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(ConvDesc)
+    i32, u32, i64 = ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64
+    pi64 = ctypes.POINTER(ctypes.c_int64)
+    psz = ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "conv_im2win_output_dims": [D, pi64, pi64],
+        "conv_im2win_window_geometry": [D, i32, i32, pi64, pi64, pi64],
+        "conv_im2win_window_bytes": [D, i32, i32, i64, psz],
+        "conv_im2win_transform": [D, i32, i32, P, P, P],
+        "conv2d_workspace_bytes": [D, i32, i64, psz],
+        "conv2d_fwd": [D, i32, i32, P, P, P, P, P, ctypes.c_size_t, u32, P],
+        "conv2d_dw_fwd": [D, i32, i32, P, P, P, P, P, ctypes.c_size_t, u32, P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.conv_im2win_status_string.argtypes = [ctypes.c_int]
+    lib.conv_im2win_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().conv_im2win_status_string(int(status)).decode()
+
+
+def check(status: int, where: str) -> None:
+    if status != CIW_OK:
+        raise Im2winError(status, where)

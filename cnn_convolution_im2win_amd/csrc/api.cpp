@@ -1,0 +1,263 @@
+// api.cpp -- the C ABI of include/conv_im2win.h: argument validation, shape
+// and workspace arithmetic, batch chunking and kernel dispatch.
+//
+// Every check runs before the first launch, so an error status means nothing
+// was enqueued.  The library holds no mutable state.
+#include <cstdint>
+#include <cstring>
+
+#include "internal.hpp"
+
+using namespace ciw;
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;   // int32 indexing in the kernels
+
+// Output extent along one axis (floor formula); <= 0 when the dilated
+// window does not fit the padded input.
+int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d) {
+    int64_t span = d * (k - 1) + 1;
+    int64_t padded = in + 2 * p;
+    if (padded < span) return 0;
+    return (padded - span) / s + 1;
+}
+
+bool dtype_ok(int t) { return t == CIW_F32 || t == CIW_F16 || t == CIW_BF16; }
+
+// a1: validate a descriptor and resolve the geometry.  Problems whose
+// tensors exceed int32 indexing, or whose dilated filter is taller than the
+// repack's LDS tile can hold (more than 4096 input rows), are unsupported.
+ciw_status resolve(const ciw_conv_desc* d, ciw_dtype dt, Geom* g) {
+    if (!d || !dtype_ok(dt)) return CIW_ERR_INVALID_ARG;
+    if (d->N < 0 || d->C < 1 || d->H < 1 || d->W < 1 || d->K < 1 || d->R < 1 || d->S < 1)
+        return CIW_ERR_INVALID_ARG;
+    if (d->stride_h < 1 || d->stride_w < 1 || d->pad_h < 0 || d->pad_w < 0 || d->dil_h < 1 ||
+        d->dil_w < 1 || d->groups < 1)
+        return CIW_ERR_INVALID_ARG;
+    if (d->C % d->groups || d->K % d->groups) return CIW_ERR_INVALID_ARG;
+    const int64_t limit = kMaxElems - 1;
+    if (d->N > limit || d->C > limit || d->H > limit || d->W > limit || d->K > limit ||
+        d->R > limit || d->S > limit)
+        return CIW_ERR_UNSUPPORTED;
+    int64_t P = out_extent(d->H, d->R, d->stride_h, d->pad_h, d->dil_h);
+    int64_t Q = out_extent(d->W, d->S, d->stride_w, d->pad_w, d->dil_w);
+    if (P < 1 || Q < 1) return CIW_ERR_INVALID_ARG;
+    if ((int64_t)d->dil_h * (d->R - 1) + 1 > 4096) return CIW_ERR_UNSUPPORTED;
+    const int64_t eb = elem_bytes(dt);
+    const int64_t wwin = (Q - 1) * d->stride_w + (int64_t)d->dil_w * (d->S - 1) + 1;
+    const int64_t lenA = wwin * d->R;
+    const int64_t lenB = lenA * d->C;
+    const int64_t pitchA = round_up(lenA, 16 / eb);
+    const int64_t pitchB = round_up(lenB, 16 / eb);
+    // every tensor the kernels index must stay below 2^31 elements
+    const int64_t N = d->N > 0 ? d->N : 1;
+    if (N * d->C * d->H * d->W >= kMaxElems || d->K * (d->C / d->groups) * d->R * d->S >= kMaxElems ||
+        N * d->K * P * Q >= kMaxElems || N * d->C * P * pitchA >= kMaxElems ||
+        N * P * pitchB >= kMaxElems || wwin >= kMaxElems)
+        return CIW_ERR_UNSUPPORTED;
+    g->N = (int)d->N; g->C = (int)d->C; g->H = (int)d->H; g->W = (int)d->W;
+    g->K = (int)d->K; g->R = (int)d->R; g->S = (int)d->S; g->P = (int)P; g->Q = (int)Q;
+    g->sh = d->stride_h; g->sw = d->stride_w; g->ph = d->pad_h; g->pw = d->pad_w;
+    g->dh = d->dil_h; g->dw = d->dil_w; g->G = d->groups;
+    g->Wwin = (int)wwin;
+    g->elem = (int)eb;
+    g->lenA = (int)lenA; g->pitchA = (int)pitchA;
+    g->lenB = (int)lenB; g->pitchB = (int)pitchB;
+    return CIW_OK;
+}
+
+int64_t window_bytes_per_image(const Geom& g, ciw_win_layout lay) {
+    return lay == CIW_WIN_CHW ? (int64_t)g.C * g.P * g.pitchA * g.elem
+                              : (int64_t)g.P * g.pitchB * g.elem;
+}
+
+enum Path { PATH_FP32, PATH_MFMA, PATH_DW };
+
+Path path_of(const Geom& g, ciw_dtype in, bool depthwise) {
+    if (depthwise) return PATH_DW;
+    return in == CIW_F32 ? PATH_FP32 : PATH_MFMA;
+}
+
+ciw_win_layout layout_of(Path p) { return p == PATH_MFMA ? CIW_WIN_HWC : CIW_WIN_CHW; }
+
+// a8: workspace of one chunk of n images = its window tensor (+ fp32 partial sums).
+int64_t chunk_workspace(const Geom& g, Path p, int64_t n) {
+    int64_t bytes = round_up(window_bytes_per_image(g, layout_of(p)) * n, 256);
+    if (p == PATH_FP32) {
+        int s = fp32_splits(g, (int)n);
+        if (s > 1) bytes += (int64_t)s * n * g.K * g.P * g.Q * 4;
+    }
+    return bytes;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+ciw_status from_hip(hipError_t e) { return e == hipSuccess ? CIW_OK : CIW_ERR_HIP; }
+
+ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, const void* x,
+                    const void* w, const void* bias, void* y, void* ws, size_t ws_bytes,
+                    uint32_t flags, void* stream, bool depthwise) {
+    Geom g;
+    ciw_status s = resolve(desc, in, &g);
+    if (s != CIW_OK) return s;
+    if (!dtype_ok(out)) return CIW_ERR_INVALID_ARG;
+    // allowed (in -> out) pairs
+    if (in == CIW_F32 ? out != CIW_F32 : (out != in && out != CIW_F32)) return CIW_ERR_INVALID_ARG;
+    if (flags & ~(CIW_FLAG_WINDOW_READY | CIW_FLAG_NO_SPLIT | CIW_FLAG_GENERIC))
+        return CIW_ERR_INVALID_ARG;
+    if (depthwise) {
+        if (!(g.G == g.C && g.K == g.C)) return g.G == 1 ? CIW_ERR_INVALID_ARG : CIW_ERR_UNSUPPORTED;
+    } else if (g.G != 1) {
+        return CIW_ERR_UNSUPPORTED;
+    }
+    if (g.N == 0) return CIW_OK;   // empty batch: nothing to do
+    const bool ready = (flags & CIW_FLAG_WINDOW_READY) != 0;
+    if ((!ready && !x) || !w || !y || !ws) return CIW_ERR_INVALID_ARG;
+    if ((x && !aligned(x, 16)) || !aligned(w, 16) || !aligned(y, 16) || !aligned(ws, 16) ||
+        (bias && !aligned(bias, elem_bytes(in))))
+        return CIW_ERR_INVALID_ARG;
+
+    const Path p = path_of(g, in, depthwise);
+    const ciw_win_layout lay = layout_of(p);
+    const bool no_split = (flags & CIW_FLAG_NO_SPLIT) != 0;
+    const bool generic = (flags & CIW_FLAG_GENERIC) != 0;
+
+    // chunk size: the most images whose workspace fits (the full batch if it does)
+    int64_t nc = 0;
+    if (ready) {
+        if ((int64_t)ws_bytes < chunk_workspace(g, p, g.N)) return CIW_ERR_WORKSPACE;
+        nc = g.N;
+    } else {
+        int64_t per = window_bytes_per_image(g, lay);
+        int64_t hi = per > 0 ? (int64_t)ws_bytes / per : 0;
+        if (hi > g.N) hi = g.N;
+        for (int64_t n = hi; n >= 1; --n)
+            if (chunk_workspace(g, p, n) <= (int64_t)ws_bytes) {
+                nc = n;
+                break;
+            }
+        if (nc == 0) return CIW_ERR_WORKSPACE;
+    }
+
+    hipStream_t st = (hipStream_t)stream;
+    (void)hipGetLastError();   // clear a stale error so launch checks report our own
+    const int64_t x_img = (int64_t)g.C * g.H * g.W * g.elem;
+    const int64_t y_img = (int64_t)g.K * g.P * g.Q * elem_bytes(out);
+    unsigned char* wsb = (unsigned char*)ws;
+    for (int64_t n0 = 0; n0 < g.N; n0 += nc) {
+        const int n = (int)((g.N - n0) < nc ? (g.N - n0) : nc);
+        const unsigned char* xc = x ? (const unsigned char*)x + n0 * x_img : nullptr;
+        unsigned char* yc = (unsigned char*)y + n0 * y_img;
+        if (!ready) {
+            hipError_t e = launch_transform(g, in, lay, xc, wsb, n, st);
+            if (e != hipSuccess) return from_hip(e);
+        }
+        hipError_t e;
+        if (p == PATH_FP32) {
+            // one slice count for every chunk, sized for the largest chunk, so a
+            // smaller last chunk's partial sums fit where the first chunk's did
+            int splits = no_split ? 1 : fp32_splits(g, (int)nc);
+            float* partials = (float*)(wsb + round_up(window_bytes_per_image(g, lay) * nc, 256));
+            e = launch_conv_fp32(g, (const float*)wsb, (const float*)w, (const float*)bias,
+                                 (float*)yc, n, partials, splits, generic, st);
+        } else if (p == PATH_MFMA) {
+            e = launch_conv_mfma(g, in, out, wsb, w, bias, yc, n, generic, st);
+        } else {
+            e = launch_conv_dw(g, in, out, wsb, w, bias, yc, n, generic, st);
+        }
+        if (e != hipSuccess) return from_hip(e);
+    }
+    return CIW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ciw_status conv_im2win_output_dims(const ciw_conv_desc* desc, int64_t* P, int64_t* Q) {
+    Geom g;
+    ciw_status s = resolve(desc, CIW_F32, &g);
+    if (s != CIW_OK) return s;
+    if (P) *P = g.P;
+    if (Q) *Q = g.Q;
+    return CIW_OK;
+}
+
+ciw_status conv_im2win_window_geometry(const ciw_conv_desc* desc, ciw_dtype dtype,
+                                       ciw_win_layout layout, int64_t* rows_per_image,
+                                       int64_t* row_elems, int64_t* row_pitch) {
+    if (layout != CIW_WIN_CHW && layout != CIW_WIN_HWC) return CIW_ERR_INVALID_ARG;
+    Geom g;
+    ciw_status s = resolve(desc, dtype, &g);
+    if (s != CIW_OK) return s;
+    const bool chw = layout == CIW_WIN_CHW;
+    if (rows_per_image) *rows_per_image = chw ? (int64_t)g.C * g.P : g.P;
+    if (row_elems) *row_elems = chw ? g.lenA : g.lenB;
+    if (row_pitch) *row_pitch = chw ? g.pitchA : g.pitchB;
+    return CIW_OK;
+}
+
+ciw_status conv_im2win_window_bytes(const ciw_conv_desc* desc, ciw_dtype dtype,
+                                    ciw_win_layout layout, int64_t n_images, size_t* bytes) {
+    if (layout != CIW_WIN_CHW && layout != CIW_WIN_HWC) return CIW_ERR_INVALID_ARG;
+    if (!bytes || n_images < 0) return CIW_ERR_INVALID_ARG;
+    Geom g;
+    ciw_status s = resolve(desc, dtype, &g);
+    if (s != CIW_OK) return s;
+    *bytes = (size_t)(window_bytes_per_image(g, layout) * n_images);
+    return CIW_OK;
+}
+
+ciw_status conv_im2win_transform(const ciw_conv_desc* desc, ciw_dtype dtype,
+                                 ciw_win_layout layout, const void* x, void* x_win,
+                                 void* stream) {
+    if (layout != CIW_WIN_CHW && layout != CIW_WIN_HWC) return CIW_ERR_INVALID_ARG;
+    Geom g;
+    ciw_status s = resolve(desc, dtype, &g);
+    if (s != CIW_OK) return s;
+    if (g.N == 0) return CIW_OK;
+    if (!x || !x_win || !aligned(x, 16) || !aligned(x_win, 16)) return CIW_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return from_hip(launch_transform(g, dtype, layout, x, x_win, g.N, (hipStream_t)stream));
+}
+
+ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
+                                  int64_t n_images, size_t* bytes) {
+    if (!bytes || n_images < 1) return CIW_ERR_INVALID_ARG;
+    Geom g;
+    ciw_status s = resolve(desc, in_dtype, &g);
+    if (s != CIW_OK) return s;
+    bool dw = g.G > 1;
+    if (dw && !(g.G == g.C && g.K == g.C)) return CIW_ERR_UNSUPPORTED;
+    *bytes = (size_t)chunk_workspace(g, path_of(g, in_dtype, dw), n_images);
+    return CIW_OK;
+}
+
+ciw_status conv2d_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype out_dtype,
+                      const void* x, const void* w, const void* bias, void* y, void* workspace,
+                      size_t workspace_bytes, uint32_t flags, void* stream) {
+    return run_conv(desc, in_dtype, out_dtype, x, w, bias, y, workspace, workspace_bytes, flags,
+                    stream, false);
+}
+
+ciw_status conv2d_dw_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype out_dtype,
+                         const void* x, const void* w, const void* bias, void* y,
+                         void* workspace, size_t workspace_bytes, uint32_t flags,
+                         void* stream) {
+    return run_conv(desc, in_dtype, out_dtype, x, w, bias, y, workspace, workspace_bytes, flags,
+                    stream, true);
+}
+
+const char* conv_im2win_status_string(ciw_status status) {
+    switch (status) {
+        case CIW_OK: return "success";
+        case CIW_ERR_INVALID_ARG: return "invalid argument";
+        case CIW_ERR_UNSUPPORTED: return "unsupported convolution";
+        case CIW_ERR_WORKSPACE: return "workspace too small";
+        case CIW_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

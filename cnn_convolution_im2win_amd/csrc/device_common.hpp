@@ -1,0 +1,51 @@
+// device_common.hpp -- element types and conversions used by the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace ciw {
+
+typedef _Float16 half_t;
+
+// bf16 is carried as its 16-bit pattern.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(half_t v) { return (float)v; }
+__device__ __forceinline__ float to_f32(bf16_t v) {
+    return __uint_as_float(((uint32_t)v.bits) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+
+// fp32 -> fp16, round to nearest even (the hardware conversion's default mode).
+template <>
+__device__ __forceinline__ half_t from_f32<half_t>(float v) { return (half_t)v; }
+
+// fp32 -> bf16, round to nearest even on the bit pattern; NaN stays NaN.
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
+    uint32_t u = __float_as_uint(v);
+    bf16_t r;
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+        r.bits = (uint16_t)((u >> 16) | 0x40u);
+    } else {
+        u += 0x7fffu + ((u >> 16) & 1u);
+        r.bits = (uint16_t)(u >> 16);
+    }
+    return r;
+}
+
+template <typename T>
+__device__ __forceinline__ T zero_elem() {
+    return from_f32<T>(0.0f);
+}
+
+}  // namespace ciw

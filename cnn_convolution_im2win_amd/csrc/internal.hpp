@@ -1,0 +1,80 @@
+// internal.hpp -- shared declarations of the im2win library (host + device).
+//
+// Geometry, kernel argument blocks and the launchers each kernel file
+// exports.  Nothing here is part of the C ABI (include/conv_im2win.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "conv_im2win.h"
+
+namespace ciw {
+
+// Unsigned division by a divisor fixed at launch time, as a multiply-high and
+// a shift (Granlund & Montgomery, "Division by Invariant Integers using
+// Multiplication", 1994, the round-up variant).  Valid for n < 2^31.
+// The host precomputes (m, s) once per launch -- the "index precomputation"
+// of the im2win paper §III-E1 -- so kernels never issue an integer divide.
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f{d, 0u, 0u};
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    f.s = s;
+    f.m = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1ull);
+    return f;
+}
+
+__host__ __device__ inline uint32_t fdiv(uint32_t n, const FastDiv& f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t hi = __umulhi(n, f.m);
+#else
+    uint32_t hi = (uint32_t)(((uint64_t)n * f.m) >> 32);
+#endif
+    return (hi + n) >> f.s;
+}
+
+// Resolved convolution geometry (all extents fit in int32; checked on entry).
+struct Geom {
+    int N, C, H, W, K, R, S, P, Q;
+    int sh, sw, ph, pw, dh, dw, G;
+    int Wwin;          // columns of the padded input one output row touches
+    int elem;          // bytes per input element
+    int lenA, pitchA;  // CHW window row: Wwin*R elements, pitch (16-byte multiple)
+    int lenB, pitchB;  // HWC window row: Wwin*R*C elements, pitch
+};
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+inline int elem_bytes(ciw_dtype t) { return t == CIW_F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the error of the launch.  Pointers are already
+// offset to the chunk; n_images is the chunk's image count.
+
+hipError_t launch_transform(const Geom& g, ciw_dtype dt, ciw_win_layout lay, const void* x,
+                            void* xw, int n_images, hipStream_t st);
+
+// fp32 dense contraction over a CHW window tensor.  splits > 1 sums the
+// channels in `splits` slices into `partials` ([splits][n][K][P][Q] fp32)
+// and a second kernel reduces them in slice order (deterministic).
+int fp32_splits(const Geom& g, int n_images);
+hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, const float* bias,
+                            float* y, int n_images, float* partials, int splits, bool generic,
+                            hipStream_t st);
+
+// fp16/bf16 dense contraction over an HWC window tensor on the matrix cores.
+hipError_t launch_conv_mfma(const Geom& g, ciw_dtype in, ciw_dtype out, const void* xw,
+                            const void* w, const void* bias, void* y, int n_images,
+                            bool generic, hipStream_t st);
+
+// Depthwise contraction over a CHW window tensor.
+hipError_t launch_conv_dw(const Geom& g, ciw_dtype in, ciw_dtype out, const void* xw,
+                          const void* w, const void* bias, void* y, int n_images,
+                          bool generic, hipStream_t st);
+
+}  // namespace ciw

@@ -1,0 +1,152 @@
+/*
+ * conv_im2win.h -- C ABI of the im2win forward-convolution library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is the im2win ("image to window") paradigm of "Enabling
+ * Memory-efficient Im2win Convolution with Multi-precision Support on GPU
+ * CUDA and Tensor Cores" (below: the im2win paper):
+ *   1. the input is repacked once into a window tensor in which the inputs
+ *      of every output row sit in one contiguous row (§III-B, §III-C);
+ *   2. a windowed dot product contracts each output's contiguous window with
+ *      the filter (§III-C), on the vector ALUs in fp32 and on the matrix
+ *      cores in fp16/bf16 with fp32 accumulation (§III-D, §III-F).
+ * The problem statement (N, C, H, W, K, R, S, stride, padding, dilation,
+ * bias; zero padding; cross-correlation; bias added after the sum) is the one
+ * of the OpenCL-Benchmarks page's direct "conv2d" kernel ("Setting: normal").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *   never allocates, frees or synchronises; work is enqueued on `stream`
+ *   (a hipStream_t; NULL means the null stream) and completes
+ *   asynchronously.  No mutable global state: calls on different streams may
+ *   run concurrently if their buffers do not overlap.
+ * - Arguments are validated BEFORE anything is enqueued; on any error status
+ *   nothing has been launched and no buffer has been touched.
+ * - Tensors are dense and contiguous: x is NCHW [N][C][H][W]; the filters w
+ *   are KCRS [K][C/groups][R][S] (R = filter height, S = filter width); bias
+ *   is [K] and may be NULL; y is NCHW [N][K][P][Q].
+ * - x, w, y and workspace must be 16-byte aligned; bias must be aligned to
+ *   its element size.  Every tensor must hold fewer than 2^31 elements.
+ * - Element types: input, filter and bias share `in_dtype`.  Allowed
+ *   (in -> out) pairs: F32->F32, F16->F16, F16->F32, BF16->BF16, BF16->F32.
+ *   Products are accumulated in fp32, the bias is added in fp32, and the
+ *   result is rounded once (round-to-nearest-even) to the output type.
+ */
+#ifndef CONV_IM2WIN_H
+#define CONV_IM2WIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CIW_OK = 0,
+    CIW_ERR_INVALID_ARG = -1,   /* bad descriptor, NULL/misaligned pointer, bad dtype pair */
+    CIW_ERR_UNSUPPORTED = -2,   /* valid convolution this library does not run (e.g. groups
+                                   other than 1 or C, a tensor with >= 2^31 elements) */
+    CIW_ERR_WORKSPACE = -3,     /* workspace smaller than one image needs */
+    CIW_ERR_HIP = -4            /* a HIP launch or runtime call failed */
+} ciw_status;
+
+typedef enum { CIW_F32 = 0, CIW_F16 = 1, CIW_BF16 = 2 } ciw_dtype;
+
+/* Window-tensor layouts.
+ * CIW_WIN_CHW (channel-planar): one row per (n, c, output row h):
+ *     xw[n][c][h][x*R + r]
+ * CIW_WIN_HWC (channel-innermost, the NHWC-based variant the im2win paper
+ *     uses on tensor cores, §III-D): one row per (n, output row h):
+ *     xw[n][h][(x*R + r)*C + c]
+ * with value x[n][c][h*stride_h - pad_h + r*dil_h][x - pad_w] (zero outside
+ * the input) for columns x in [0, Wwin), Wwin = (Q-1)*stride_w +
+ * dil_w*(S-1) + 1.  Rows are padded with zeros to a pitch that is a multiple
+ * of 16 bytes.  The window of output (h, w) is, for each filter column q, the
+ * R (CHW) or R*C (HWC) contiguous elements at column w*stride_w + q*dil_w;
+ * with dil_w = 1 the whole window is one contiguous run ("height before
+ * width", §III-C). */
+typedef enum { CIW_WIN_CHW = 0, CIW_WIN_HWC = 1 } ciw_win_layout;
+
+/* Convolution descriptor.  groups must divide C and K; the library runs
+ * groups == 1 (dense) and groups == C == K (depthwise). */
+typedef struct {
+    int64_t N, C, H, W;        /* input batch, channels, height, width */
+    int64_t K, R, S;           /* output channels, filter height, filter width */
+    int32_t stride_h, stride_w;
+    int32_t pad_h, pad_w;      /* zero padding on each side */
+    int32_t dil_h, dil_w;      /* dilation (>= 1) */
+    int32_t groups;
+} ciw_conv_desc;
+
+/* conv2d_fwd / conv2d_dw_fwd flags. */
+#define CIW_FLAG_WINDOW_READY 0x1u  /* workspace already holds the full-batch window tensor
+                                       of x (made by conv_im2win_transform with the layout
+                                       the call uses); the repack is skipped, x may be NULL */
+#define CIW_FLAG_NO_SPLIT     0x2u  /* fp32 dense: never split the channel sum across
+                                       workgroups (a single pass, no partial sums) */
+#define CIW_FLAG_GENERIC      0x4u  /* use the shape-generic kernels only (testing aid) */
+
+/* Output extent: P = floor((H + 2 pad_h - dil_h (R-1) - 1) / stride_h) + 1,
+ * Q likewise.  Returns CIW_ERR_INVALID_ARG if the descriptor is invalid or
+ * the window does not fit the padded input. */
+ciw_status conv_im2win_output_dims(const ciw_conv_desc* desc, int64_t* P, int64_t* Q);
+
+/* Geometry of the window tensor of ONE image: number of rows (C*P for CHW,
+ * P for HWC), elements per row before padding, and the row pitch in
+ * elements.  Any output pointer may be NULL. */
+ciw_status conv_im2win_window_geometry(const ciw_conv_desc* desc, ciw_dtype dtype,
+                                       ciw_win_layout layout, int64_t* rows_per_image,
+                                       int64_t* row_elems, int64_t* row_pitch);
+
+/* Bytes of the window tensor of n_images images (pitch included). */
+ciw_status conv_im2win_window_bytes(const ciw_conv_desc* desc, ciw_dtype dtype,
+                                    ciw_win_layout layout, int64_t n_images, size_t* bytes);
+
+/* im2win repack (the im2win paper §III-B, §III-C; §III-D for the HWC
+ * layout).  Writes the full-batch window tensor of x, pitch tails zeroed, to
+ * x_win (conv_im2win_window_bytes(desc, dtype, layout, N) bytes, 16-byte
+ * aligned).  A pure data movement: the result is bit-exact. */
+ciw_status conv_im2win_transform(const ciw_conv_desc* desc, ciw_dtype dtype,
+                                 ciw_win_layout layout, const void* x, void* x_win,
+                                 void* stream);
+
+/* Workspace conv2d_fwd / conv2d_dw_fwd need to process n_images images per
+ * chunk (the window tensor of the chunk plus any partial sums).  Passing
+ * n_images = N gives the single-chunk (full-batch) size; the minimum usable
+ * workspace is the n_images = 1 size. */
+ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
+                                  int64_t n_images, size_t* bytes);
+
+/* Dense forward convolution (groups == 1), im2win method: for each batch
+ * chunk, the repack into `workspace` followed by the windowed contraction
+ * (the im2win paper §III-C..§III-F).  fp32 uses the CHW window layout and
+ * the vector ALUs; fp16/bf16 use the HWC layout and the matrix cores with
+ * fp32 accumulation.  The chunk size is the largest number of images whose
+ * workspace (conv2d_workspace_bytes) fits in workspace_bytes, capped at N;
+ * CIW_ERR_WORKSPACE if not even one image fits.  With
+ * CIW_FLAG_WINDOW_READY the workspace must hold the full-batch window
+ * tensor at offset 0 and be at least conv2d_workspace_bytes(desc, in, N). */
+ciw_status conv2d_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype out_dtype,
+                      const void* x, const void* w, const void* bias, void* y,
+                      void* workspace, size_t workspace_bytes, uint32_t flags,
+                      void* stream);
+
+/* Depthwise forward convolution (groups == C == K, one filter per channel):
+ * the CHW window tensor, then a per-channel windowed dot product
+ * (bandwidth-bound).  Same arguments, workspace and flag rules as
+ * conv2d_fwd; w is [C][1][R][S]. */
+ciw_status conv2d_dw_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype out_dtype,
+                         const void* x, const void* w, const void* bias, void* y,
+                         void* workspace, size_t workspace_bytes, uint32_t flags,
+                         void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* conv_im2win_status_string(ciw_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV_IM2WIN_H */
