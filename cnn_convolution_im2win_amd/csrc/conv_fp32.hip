@@ -7,10 +7,26 @@
 // w*stride_w + q*dil_w -- with the filter read height before width; the bias
 // is added after the sum.  Accumulation is fp32.
 //
-// When one image's outputs are too few to fill the chip (a 13x13 layer with
-// N = 1 has 169 pixels), the channel sum is split into slices whose partial
-// sums a second kernel adds in slice order, so results do not depend on
+// Fast kernel (small filters, dil_w = 1).  The 64 lanes of a wave are 64
+// output channels; each lane accumulates TN consecutive output columns of
+// one output row.  For one input channel the window-row segment those TN
+// columns read is the same for every lane, so it is loaded once per wave
+// into scalar registers and every multiply-add takes it as its scalar
+// operand; the lane's own R*S filter taps sit in vector registers.  Per
+// input channel a lane therefore issues TN*R*S multiply-adds against R*S
+// vector loads -- the reuse of overlapping windows that the paper credits
+// to the cache ("elements loaded in a previous window remain in cache",
+// §III-C) happens here in registers.
+//
+// The channel sum is split two ways so that small layers (one 13x13 image)
+// still fill 256 compute units: the four waves of a workgroup take
+// interleaved channels and add their sums in LDS, and `splits` workgroups
+// take disjoint channel slices whose partial sums a second kernel adds in
+// slice order.  Both orders are fixed, so results do not depend on
 // scheduling.
+//
+// Generic kernel: any filter size, stride and dilation; one thread computes
+// kTK output channels of one pixel.
 #include "internal.hpp"
 #include "device_common.hpp"
 
@@ -18,8 +34,10 @@ namespace ciw {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTK = 4;   // output channels per thread (generic kernel)
+constexpr int kTK = 4;          // output channels per thread (generic kernel)
+constexpr int kWaves = 4;       // waves per workgroup (fast kernel)
 
+// ------------------------------------------------------------ generic kernel
 struct Fp32Args {
     int C, K, R, S, P, Q, sw, dw, pitch;
     int n_images, splits, c_per_split, kgroups;
@@ -27,7 +45,6 @@ struct Fp32Args {
     int64_t total;   // threads doing work
 };
 
-// Generic: one thread computes kTK consecutive output channels of one pixel.
 __global__ __launch_bounds__(kThreads) void conv_fp32_generic_kernel(
     const float* __restrict__ xw, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ out, Fp32Args a) {
@@ -81,6 +98,111 @@ __global__ __launch_bounds__(kThreads) void conv_fp32_generic_kernel(
     }
 }
 
+// --------------------------------------------------------------- fast kernel
+struct KlArgs {
+    int C, K, P, Q, pitch;
+    int col_tiles, kblocks, splits, c_per_split;
+    FastDiv fdSplit, fdKb, fdTiles, fdP;
+    int n_images;
+};
+
+// Window-row elements the TN output columns of one tile read: columns
+// w0*SW .. (w0+TN-1)*SW + S-1 of the padded input, R values each.
+template <int R, int S, int SW, int TN>
+struct KlShape {
+    static constexpr int kLen = ((TN - 1) * SW + S) * R;
+    static constexpr int kTaps = R * S;
+};
+
+template <int R, int S, int SW, int TN>
+__global__ __launch_bounds__(kThreads) void conv_fp32_klanes_kernel(
+    const float* __restrict__ xw, const float* __restrict__ w, const float* __restrict__ bias,
+    float* __restrict__ out, KlArgs a) {
+    using Sh = KlShape<R, S, SW, TN>;
+    constexpr int L = Sh::kLen;
+    constexpr int T = Sh::kTaps;
+    __shared__ float red[kWaves - 1][TN][64];
+
+    // block -> (n, h, column tile, k block, channel slice); the slice index
+    // varies fastest so that workgroups sharing a window row run together
+    uint32_t bid = blockIdx.x;
+    uint32_t t1 = fdiv(bid, a.fdSplit);
+    const int sidx = bid - t1 * a.splits;
+    uint32_t t2 = fdiv(t1, a.fdKb);
+    const int kb = t1 - t2 * a.kblocks;
+    uint32_t t3 = fdiv(t2, a.fdTiles);
+    const int tile = t2 - t3 * a.col_tiles;
+    uint32_t n = fdiv(t3, a.fdP);
+    const int h = t3 - n * a.P;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int k = kb * 64 + lane;
+    const int kk = min(k, a.K - 1);
+
+    // the last tile is shifted left so it ends at column Q (its leading
+    // columns repeat the previous tile's and are not stored)
+    const int w_store = tile * TN;
+    const int w0 = min(w_store, a.Q - TN);
+
+    const int c_begin = sidx * a.c_per_split;
+    const int c_end = min(a.C, c_begin + a.c_per_split);
+
+    float acc[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) acc[t] = 0.f;
+
+    // window row (n, c, h) starts at this element offset; uniform per wave
+    const int row_step = a.P * a.pitch;
+    int xoff = ((n * a.C + c_begin + wave) * a.P + h) * a.pitch + w0 * SW * R;
+    xoff = __builtin_amdgcn_readfirstlane(xoff);
+    const float* wk = w + (size_t)kk * a.C * T;
+
+    for (int c = c_begin + wave; c < c_end; c += kWaves) {
+        float f[T];
+#pragma unroll
+        for (int j = 0; j < T; ++j) f[j] = wk[c * T + j];
+        float xv[L];
+#pragma unroll
+        for (int i = 0; i < L; ++i) xv[i] = xw[xoff + i];
+#pragma unroll
+        for (int q = 0; q < S; ++q)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float fv = f[r * S + q];
+#pragma unroll
+                for (int t = 0; t < TN; ++t) acc[t] = fmaf(xv[(t * SW + q) * R + r], fv, acc[t]);
+            }
+        xoff += kWaves * row_step;
+    }
+
+    // add the four waves' sums in wave order
+    if (wave > 0) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t) red[wave - 1][t][lane] = acc[t];
+    }
+    __syncthreads();
+    if (wave != 0 || k >= a.K) return;
+#pragma unroll
+    for (int i = 0; i < kWaves - 1; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t) acc[t] += red[i][t][lane];
+
+    const int PQ = a.P * a.Q;
+    if (a.splits == 1) {
+        const float b = bias ? bias[k] : 0.f;
+        float* yp = out + ((size_t)n * a.K + k) * PQ + h * a.Q + w0;
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+            if (w0 + t >= w_store) yp[t] = acc[t] + b;
+    } else {
+        float* pp = out + (((size_t)sidx * a.n_images + n) * a.K + k) * PQ + h * a.Q + w0;
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+            if (w0 + t >= w_store) pp[t] = acc[t];
+    }
+}
+
 // y = bias + sum over slices, in slice order.
 __global__ __launch_bounds__(kThreads) void split_reduce_kernel(const float* __restrict__ part,
                                                                 const float* __restrict__ bias,
@@ -95,9 +217,54 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(const float* __r
     y[i] = v;
 }
 
-}  // namespace
+// ------------------------------------------------------------------ planning
+typedef void (*KlKernel)(const float*, const float*, const float*, float*, KlArgs);
 
-int fp32_splits(const Geom& g, int n_images) {
+struct KlVariant {
+    int R, S, SW, TN;
+    KlKernel fn;
+};
+
+#define CIW_KL(R, S, SW, TN) {R, S, SW, TN, conv_fp32_klanes_kernel<R, S, SW, TN>}
+// Column-tile widths per filter shape: the scalar window segment
+// ((TN-1)*SW + S)*R stays at or below 60 registers.
+const KlVariant kKlVariants[] = {
+    CIW_KL(1, 1, 1, 16), CIW_KL(1, 1, 1, 14), CIW_KL(1, 1, 1, 13), CIW_KL(1, 1, 1, 8),
+    CIW_KL(1, 1, 1, 7),
+    CIW_KL(1, 1, 2, 16), CIW_KL(1, 1, 2, 14), CIW_KL(1, 1, 2, 13), CIW_KL(1, 1, 2, 8),
+    CIW_KL(1, 1, 2, 7),
+    CIW_KL(3, 3, 1, 16), CIW_KL(3, 3, 1, 14), CIW_KL(3, 3, 1, 13), CIW_KL(3, 3, 1, 8),
+    CIW_KL(3, 3, 1, 7),
+    CIW_KL(3, 3, 2, 8), CIW_KL(3, 3, 2, 7), CIW_KL(3, 3, 2, 4),
+    CIW_KL(5, 5, 1, 8), CIW_KL(5, 5, 1, 7), CIW_KL(5, 5, 1, 4),
+};
+#undef CIW_KL
+
+struct Fp32Plan {
+    const KlVariant* kl;   // null: generic kernel
+    int col_tiles, kblocks;
+    int splits;            // channel slices across workgroups (partial-sum passes)
+    int c_per_split;
+};
+
+// The fast kernel's variant for this shape: the tile width that wastes the
+// fewest recomputed columns (ties: the widest).
+const KlVariant* pick_variant(const Geom& g) {
+    if (g.dw != 1) return nullptr;
+    const KlVariant* best = nullptr;
+    int64_t best_cols = 0;
+    for (const KlVariant& v : kKlVariants) {
+        if (v.R != g.R || v.S != g.S || v.SW != g.sw || v.TN > g.Q) continue;
+        int64_t cols = (int64_t)((g.Q + v.TN - 1) / v.TN) * v.TN;
+        if (!best || cols < best_cols || (cols == best_cols && v.TN > best->TN)) {
+            best = &v;
+            best_cols = cols;
+        }
+    }
+    return best;
+}
+
+int generic_splits(const Geom& g, int n_images) {
     // aim for >= 128K threads of work; keep >= 16 channels per slice
     int64_t base = (int64_t)n_images * ((g.K + kTK - 1) / kTK) * g.P * g.Q;
     int64_t want = (131072 + base - 1) / base;
@@ -106,33 +273,92 @@ int fp32_splits(const Geom& g, int n_images) {
     return s < 1 ? 1 : (int)s;
 }
 
+Fp32Plan plan(const Geom& g, int n_images, bool generic) {
+    Fp32Plan p{};
+    p.kl = generic ? nullptr : pick_variant(g);
+    if (!p.kl) {
+        p.splits = generic_splits(g, n_images);
+        p.c_per_split = (g.C + p.splits - 1) / p.splits;
+        return p;
+    }
+    p.col_tiles = (g.Q + p.kl->TN - 1) / p.kl->TN;
+    p.kblocks = (g.K + 63) / 64;
+    // Enough workgroups for ~8 waves per SIMD on 256 CUs, keeping at least
+    // 4 channels per wave (16 per workgroup).
+    const int64_t base = (int64_t)n_images * g.P * p.col_tiles * p.kblocks;
+    const int64_t want_wg = 2048;
+    int64_t s = (want_wg + base - 1) / base;
+    int64_t maxs = g.C / (kWaves * 4);
+    if (s > maxs) s = maxs;
+    if (s < 1) s = 1;
+    p.c_per_split = (int)((g.C + s - 1) / s);
+    p.splits = (int)((g.C + p.c_per_split - 1) / p.c_per_split);
+    return p;
+}
+
+}  // namespace
+
+int fp32_splits(const Geom& g, int n_images) {
+    // partial-sum slices the workspace must hold: the larger of the two
+    // kernels' plans, so either may run in a workspace sized by this
+    int a = plan(g, n_images, false).splits;
+    int b = plan(g, n_images, true).splits;
+    return a > b ? a : b;
+}
+
 hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, const float* bias,
-                            float* y, int n_images, float* partials, int splits, bool generic,
-                            hipStream_t st) {
-    (void)generic;
-    Fp32Args a;
-    a.C = g.C; a.K = g.K; a.R = g.R; a.S = g.S; a.P = g.P; a.Q = g.Q;
-    a.sw = g.sw; a.dw = g.dw; a.pitch = g.pitchA;
-    a.n_images = n_images;
-    a.splits = splits;
-    a.c_per_split = (g.C + splits - 1) / splits;
-    a.kgroups = (g.K + kTK - 1) / kTK;
-    a.fdPQ = make_fastdiv(g.P * g.Q);
-    a.fdKg = make_fastdiv(a.kgroups);
-    a.fdQ = make_fastdiv(g.Q);
-    a.fdSplit = make_fastdiv(splits);
-    a.total = (int64_t)n_images * splits * a.kgroups * g.P * g.Q;
-    if (a.total == 0) return hipSuccess;
-    if (a.total >= (1ll << 31)) return hipErrorInvalidValue;
-    uint32_t blocks = (uint32_t)((a.total + kThreads - 1) / kThreads);
-    float* dst = splits == 1 ? y : partials;
-    hipLaunchKernelGGL(conv_fp32_generic_kernel, dim3(blocks), dim3(kThreads), 0, st, xw, w,
-                       bias, dst, a);
+                            float* y, int n_images, float* partials, int max_splits,
+                            bool generic, hipStream_t st) {
+    if (n_images == 0) return hipSuccess;
+    Fp32Plan p = plan(g, n_images, generic);
+    if (max_splits <= 1) {   // single pass requested
+        p.splits = 1;
+        p.c_per_split = g.C;
+    }
+    if (p.splits > max_splits) {   // a smaller last chunk wants more slices than fit
+        p.c_per_split = (g.C + max_splits - 1) / max_splits;
+        p.splits = (g.C + p.c_per_split - 1) / p.c_per_split;
+    }
+    float* dst = p.splits == 1 ? y : partials;
+    if (p.kl) {
+        KlArgs a;
+        a.C = g.C; a.K = g.K; a.P = g.P; a.Q = g.Q; a.pitch = g.pitchA;
+        a.col_tiles = p.col_tiles;
+        a.kblocks = p.kblocks;
+        a.splits = p.splits;
+        a.c_per_split = p.c_per_split;
+        a.fdSplit = make_fastdiv(p.splits);
+        a.fdKb = make_fastdiv(p.kblocks);
+        a.fdTiles = make_fastdiv(p.col_tiles);
+        a.fdP = make_fastdiv(g.P);
+        a.n_images = n_images;
+        int64_t blocks = (int64_t)n_images * g.P * p.col_tiles * p.kblocks * p.splits;
+        if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(p.kl->fn, dim3((uint32_t)blocks), dim3(kThreads), 0, st, xw, w, bias,
+                           dst, a);
+    } else {
+        Fp32Args a;
+        a.C = g.C; a.K = g.K; a.R = g.R; a.S = g.S; a.P = g.P; a.Q = g.Q;
+        a.sw = g.sw; a.dw = g.dw; a.pitch = g.pitchA;
+        a.n_images = n_images;
+        a.splits = p.splits;
+        a.c_per_split = p.c_per_split;
+        a.kgroups = (g.K + kTK - 1) / kTK;
+        a.fdPQ = make_fastdiv(g.P * g.Q);
+        a.fdKg = make_fastdiv(a.kgroups);
+        a.fdQ = make_fastdiv(g.Q);
+        a.fdSplit = make_fastdiv(p.splits);
+        a.total = (int64_t)n_images * p.splits * a.kgroups * g.P * g.Q;
+        if (a.total >= (1ll << 31)) return hipErrorInvalidValue;
+        uint32_t blocks = (uint32_t)((a.total + kThreads - 1) / kThreads);
+        hipLaunchKernelGGL(conv_fp32_generic_kernel, dim3(blocks), dim3(kThreads), 0, st, xw, w,
+                           bias, dst, a);
+    }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || splits == 1) return e;
+    if (e != hipSuccess || p.splits == 1) return e;
     int64_t per_split = (int64_t)n_images * g.K * g.P * g.Q;
     hipLaunchKernelGGL(split_reduce_kernel, dim3((uint32_t)((per_split + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, st, partials, bias, y, per_split, splits, g.P * g.Q,
+                       dim3(kThreads), 0, st, partials, bias, y, per_split, p.splits, g.P * g.Q,
                        g.K);
     return hipGetLastError();
 }
