@@ -27,6 +27,9 @@
 //
 // Generic kernel: any filter size, stride and dilation; one thread computes
 // kTK output channels of one pixel.
+#include <algorithm>
+#include <cmath>
+
 #include "internal.hpp"
 #include "device_common.hpp"
 
@@ -93,17 +96,20 @@ __global__ __launch_bounds__(kThreads) void conv_fp32_generic_kernel(
             if (bias) v += bias[k];
             out[(((size_t)n * a.K + k) * PQ) + pix] = v;
         } else {
-            out[((((size_t)sidx * a.n_images + n) * a.K + k) * PQ) + pix] = acc[i];
+            out[((((size_t)sidx * a.n_images + n) * PQ) + pix) * a.K + k] = acc[i];
         }
     }
 }
 
 // --------------------------------------------------------------- fast kernel
+constexpr int kRW = 4;          // output rows per wave (fast kernel)
+
 struct KlArgs {
     int C, K, P, Q, pitch;
-    int col_tiles, kblocks, splits, c_per_split;
-    FastDiv fdSplit, fdKb, fdTiles, fdP;
+    int col_tiles, kblocks, splits, c_per_split, row_groups;
+    FastDiv fdN, fdKb, fdTiles, fdRg;
     int n_images;
+    uint32_t xcd_per, xcd_rem;   // blocks / 8 and blocks % 8
 };
 
 // Window-row elements the TN output columns of one tile read: columns
@@ -114,6 +120,11 @@ struct KlShape {
     static constexpr int kTaps = R * S;
 };
 
+// One workgroup: 64 output channels (one per lane) x up to kRW output rows
+// x TN output columns, over one slice of input channels that its four
+// waves share out (wave w takes every fourth channel).  A lane loads its
+// R*S filter taps of a channel once and applies them to all its rows, so
+// the filter stream is read once per row group rather than once per row.
 template <int R, int S, int SW, int TN>
 __global__ __launch_bounds__(kThreads) void conv_fp32_klanes_kernel(
     const float* __restrict__ xw, const float* __restrict__ w, const float* __restrict__ bias,
@@ -121,24 +132,34 @@ __global__ __launch_bounds__(kThreads) void conv_fp32_klanes_kernel(
     using Sh = KlShape<R, S, SW, TN>;
     constexpr int L = Sh::kLen;
     constexpr int T = Sh::kTaps;
-    __shared__ float red[kWaves - 1][TN][64];
+    __shared__ float red[(kWaves - 1) * TN * 64];
 
-    // block -> (n, h, column tile, k block, channel slice); the slice index
-    // varies fastest so that workgroups sharing a window row run together
-    uint32_t bid = blockIdx.x;
-    uint32_t t1 = fdiv(bid, a.fdSplit);
-    const int sidx = bid - t1 * a.splits;
-    uint32_t t2 = fdiv(t1, a.fdKb);
-    const int kb = t1 - t2 * a.kblocks;
-    uint32_t t3 = fdiv(t2, a.fdTiles);
-    const int tile = t2 - t3 * a.col_tiles;
-    uint32_t n = fdiv(t3, a.fdP);
-    const int h = t3 - n * a.P;
+    // Workgroups are dispatched round-robin over the 8 XCDs (bid % 8), each
+    // with its own L2.  Renumber so that each XCD gets a contiguous range
+    // of logical indices, and order the logical index (row group fastest,
+    // then column tile, image, k block, channel slice) so the workgroups
+    // that read one filter slice sit on one XCD and share its L2.
+    const uint32_t bid = blockIdx.x;
+    const uint32_t xcd = bid & 7u, slot = bid >> 3;
+    const uint32_t lid = xcd < a.xcd_rem ? xcd * (a.xcd_per + 1) + slot
+                                         : a.xcd_rem * (a.xcd_per + 1) + (xcd - a.xcd_rem) * a.xcd_per + slot;
+    uint32_t t1 = fdiv(lid, a.fdRg);
+    const int rg = lid - t1 * a.row_groups;
+    uint32_t t2 = fdiv(t1, a.fdTiles);
+    const int tile = t1 - t2 * a.col_tiles;
+    uint32_t t3 = fdiv(t2, a.fdN);
+    const uint32_t n = t2 - t3 * a.n_images;
+    uint32_t sidx = fdiv(t3, a.fdKb);
+    const int kb = t3 - sidx * a.kblocks;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int k = kb * 64 + lane;
     const int kk = min(k, a.K - 1);
+
+    // rows [h0, h0 + nrows): the P rows split evenly over the row groups
+    const int h0 = rg * a.P / a.row_groups;
+    const int nrows = (rg + 1) * a.P / a.row_groups - h0;   // 1 .. kRW
 
     // the last tile is shifted left so it ends at column Q (its leading
     // columns repeat the previous tile's and are not stored)
@@ -148,13 +169,15 @@ __global__ __launch_bounds__(kThreads) void conv_fp32_klanes_kernel(
     const int c_begin = sidx * a.c_per_split;
     const int c_end = min(a.C, c_begin + a.c_per_split);
 
-    float acc[TN];
+    float acc[kRW][TN];
 #pragma unroll
-    for (int t = 0; t < TN; ++t) acc[t] = 0.f;
+    for (int rr = 0; rr < kRW; ++rr)
+#pragma unroll
+        for (int t = 0; t < TN; ++t) acc[rr][t] = 0.f;
 
     // window row (n, c, h) starts at this element offset; uniform per wave
     const int row_step = a.P * a.pitch;
-    int xoff = ((n * a.C + c_begin + wave) * a.P + h) * a.pitch + w0 * SW * R;
+    int xoff = ((n * a.C + c_begin + wave) * a.P + h0) * a.pitch + w0 * SW * R;
     xoff = __builtin_amdgcn_readfirstlane(xoff);
     const float* wk = w + (size_t)kk * a.C * T;
 
@@ -162,59 +185,88 @@ __global__ __launch_bounds__(kThreads) void conv_fp32_klanes_kernel(
         float f[T];
 #pragma unroll
         for (int j = 0; j < T; ++j) f[j] = wk[c * T + j];
-        float xv[L];
 #pragma unroll
-        for (int i = 0; i < L; ++i) xv[i] = xw[xoff + i];
+        for (int rr = 0; rr < kRW; ++rr) {
+            if (rr < nrows) {
+                float xv[L];
 #pragma unroll
-        for (int q = 0; q < S; ++q)
+                for (int e = 0; e < L; ++e) xv[e] = xw[xoff + rr * a.pitch + e];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float fv = f[r * S + q];
+                for (int q = 0; q < S; ++q)
 #pragma unroll
-                for (int t = 0; t < TN; ++t) acc[t] = fmaf(xv[(t * SW + q) * R + r], fv, acc[t]);
+                    for (int r = 0; r < R; ++r) {
+                        const float fv = f[r * S + q];
+#pragma unroll
+                        for (int t = 0; t < TN; ++t)
+                            acc[rr][t] = fmaf(xv[(t * SW + q) * R + r], fv, acc[rr][t]);
+                    }
             }
+        }
         xoff += kWaves * row_step;
     }
 
-    // add the four waves' sums in wave order
-    if (wave > 0) {
-#pragma unroll
-        for (int t = 0; t < TN; ++t) red[wave - 1][t][lane] = acc[t];
-    }
-    __syncthreads();
-    if (wave != 0 || k >= a.K) return;
-#pragma unroll
-    for (int i = 0; i < kWaves - 1; ++i)
-#pragma unroll
-        for (int t = 0; t < TN; ++t) acc[t] += red[i][t][lane];
-
+    // add the four waves' sums in wave order, one output row at a time
     const int PQ = a.P * a.Q;
-    if (a.splits == 1) {
-        const float b = bias ? bias[k] : 0.f;
-        float* yp = out + ((size_t)n * a.K + k) * PQ + h * a.Q + w0;
 #pragma unroll
-        for (int t = 0; t < TN; ++t)
-            if (w0 + t >= w_store) yp[t] = acc[t] + b;
-    } else {
-        float* pp = out + (((size_t)sidx * a.n_images + n) * a.K + k) * PQ + h * a.Q + w0;
+    for (int rr = 0; rr < kRW; ++rr) {
+        if (rr >= nrows) break;
+        if (wave > 0) {
 #pragma unroll
-        for (int t = 0; t < TN; ++t)
-            if (w0 + t >= w_store) pp[t] = acc[t];
+            for (int t = 0; t < TN; ++t) red[((wave - 1) * TN + t) * 64 + lane] = acc[rr][t];
+        }
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int i = 0; i < kWaves - 1; ++i)
+#pragma unroll
+                for (int t = 0; t < TN; ++t) acc[rr][t] += red[(i * TN + t) * 64 + lane];
+            const int h = h0 + rr;
+            if (k < a.K) {
+                if (a.splits == 1) {
+                    const float b = bias ? bias[k] : 0.f;
+                    float* yp = out + ((size_t)n * a.K + k) * PQ + h * a.Q + w0;
+#pragma unroll
+                    for (int t = 0; t < TN; ++t)
+                        if (w0 + t >= w_store) yp[t] = acc[rr][t] + b;
+                } else {
+                    // partial sums [slice][n][h][w][k]: output channels
+                    // innermost, so the 64 lanes store one contiguous run
+                    float* pp = out + ((((size_t)sidx * a.n_images + n) * a.P + h) * a.Q + w0) * a.K + k;
+#pragma unroll
+                    for (int t = 0; t < TN; ++t)
+                        if (w0 + t >= w_store) pp[(size_t)t * a.K] = acc[rr][t];
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 
-// y = bias + sum over slices, in slice order.
-__global__ __launch_bounds__(kThreads) void split_reduce_kernel(const float* __restrict__ part,
-                                                                const float* __restrict__ bias,
-                                                                float* __restrict__ y,
-                                                                int64_t per_split, int splits,
-                                                                int PQ, int K) {
-    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+// y[n][k][pix] = bias[k] + sum over slices s (in order) of part[s][n][pix][k].
+__global__ __launch_bounds__(kThreads) void split_reduce_kernel(
+    const float* __restrict__ part, const float* __restrict__ bias, float* __restrict__ y,
+    uint32_t per_split, int splits, int PQ, int K, FastDiv fdK, FastDiv fdPQ) {
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
     if (i >= per_split) return;
     float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += part[(size_t)s * per_split + i];
-    if (bias) v += bias[(i / PQ) % K];
-    y[i] = v;
+    int s = 0;
+    for (; s + 4 <= splits; s += 4) {
+        float p0 = part[(size_t)s * per_split + i];
+        float p1 = part[(size_t)(s + 1) * per_split + i];
+        float p2 = part[(size_t)(s + 2) * per_split + i];
+        float p3 = part[(size_t)(s + 3) * per_split + i];
+        v += p0;
+        v += p1;
+        v += p2;
+        v += p3;
+    }
+    for (; s < splits; ++s) v += part[(size_t)s * per_split + i];
+    const uint32_t t = fdiv(i, fdK);
+    const int k = i - t * K;
+    const uint32_t n = fdiv(t, fdPQ);
+    const int pix = t - n * PQ;
+    if (bias) v += bias[k];
+    y[((size_t)n * K + k) * PQ + pix] = v;
 }
 
 // ------------------------------------------------------------------ planning
@@ -242,7 +294,7 @@ const KlVariant kKlVariants[] = {
 
 struct Fp32Plan {
     const KlVariant* kl;   // null: generic kernel
-    int col_tiles, kblocks;
+    int col_tiles, kblocks, row_groups;
     int splits;            // channel slices across workgroups (partial-sum passes)
     int c_per_split;
 };
@@ -273,6 +325,40 @@ int generic_splits(const Geom& g, int n_images) {
     return s < 1 ? 1 : (int)s;
 }
 
+// Channel-slice count for the fast kernel from a small cost model, in
+// cycles of one SIMD: each workgroup puts one wave on each SIMD of its CU,
+// at most 8 waves are resident per SIMD, and a wave spends about 4*TN*R*S
+// cycles of multiply-adds per stage plus a fixed latency that other
+// resident waves hide; every extra slice adds one pass over the partial
+// sums.  Smallest cost wins (ties: fewer slices).
+int fast_splits(const Geom& g, const KlVariant& v, int n_images, int col_tiles, int kblocks,
+                int row_groups) {
+    const double units = (double)n_images * row_groups * col_tiles * kblocks;
+    const double stage_cycles = 4.0 * v.TN * v.R * v.S * ((double)g.P / row_groups);
+    const double latency = 2500.0;
+    const double outputs = (double)n_images * g.K * g.P * g.Q;
+    const int smax = g.C / kWaves > 1 ? g.C / kWaves : 1;
+    int best = 1;
+    double best_cost = 0.0;
+    for (int s = 1; s <= smax; ++s) {
+        const int cps = (g.C + s - 1) / s;
+        if (s > 1 && (g.C + cps - 1) / cps != s) continue;   // not a distinct slicing
+        const double wgs_per_cu = std::ceil(units * s / 256.0);
+        const double stages = std::ceil(cps / (double)kWaves);
+        double cost = 0.0;
+        for (double left = wgs_per_cu; left > 0; left -= 8) {
+            const double w = left < 8 ? left : 8;
+            cost += stages * std::max(w * stage_cycles, stage_cycles + latency);
+        }
+        if (s > 1) cost += 2000.0 + s * outputs * 4.0 / 2000.0;   // second pass
+        if (s == 1 || cost < best_cost) {
+            best = s;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 Fp32Plan plan(const Geom& g, int n_images, bool generic) {
     Fp32Plan p{};
     p.kl = generic ? nullptr : pick_variant(g);
@@ -283,16 +369,10 @@ Fp32Plan plan(const Geom& g, int n_images, bool generic) {
     }
     p.col_tiles = (g.Q + p.kl->TN - 1) / p.kl->TN;
     p.kblocks = (g.K + 63) / 64;
-    // Enough workgroups for ~8 waves per SIMD on 256 CUs, keeping at least
-    // 4 channels per wave (16 per workgroup).
-    const int64_t base = (int64_t)n_images * g.P * p.col_tiles * p.kblocks;
-    const int64_t want_wg = 2048;
-    int64_t s = (want_wg + base - 1) / base;
-    int64_t maxs = g.C / (kWaves * 4);
-    if (s > maxs) s = maxs;
-    if (s < 1) s = 1;
-    p.c_per_split = (int)((g.C + s - 1) / s);
-    p.splits = (int)((g.C + p.c_per_split - 1) / p.c_per_split);
+    p.row_groups = (g.P + kRW - 1) / kRW;
+    const int s = fast_splits(g, *p.kl, n_images, p.col_tiles, p.kblocks, p.row_groups);
+    p.c_per_split = (g.C + s - 1) / s;
+    p.splits = (g.C + p.c_per_split - 1) / p.c_per_split;
     return p;
 }
 
@@ -327,13 +407,16 @@ hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, cons
         a.kblocks = p.kblocks;
         a.splits = p.splits;
         a.c_per_split = p.c_per_split;
-        a.fdSplit = make_fastdiv(p.splits);
+        a.row_groups = p.row_groups;
+        a.fdN = make_fastdiv(n_images);
         a.fdKb = make_fastdiv(p.kblocks);
         a.fdTiles = make_fastdiv(p.col_tiles);
-        a.fdP = make_fastdiv(g.P);
+        a.fdRg = make_fastdiv(p.row_groups);
         a.n_images = n_images;
-        int64_t blocks = (int64_t)n_images * g.P * p.col_tiles * p.kblocks * p.splits;
+        int64_t blocks = (int64_t)n_images * p.row_groups * p.col_tiles * p.kblocks * p.splits;
         if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
+        a.xcd_per = (uint32_t)(blocks / 8);
+        a.xcd_rem = (uint32_t)(blocks % 8);
         hipLaunchKernelGGL(p.kl->fn, dim3((uint32_t)blocks), dim3(kThreads), 0, st, xw, w, bias,
                            dst, a);
     } else {
@@ -356,10 +439,10 @@ hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, cons
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
-    int64_t per_split = (int64_t)n_images * g.K * g.P * g.Q;
+    const int64_t per_split = (int64_t)n_images * g.K * g.P * g.Q;
     hipLaunchKernelGGL(split_reduce_kernel, dim3((uint32_t)((per_split + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, st, partials, bias, y, per_split, p.splits, g.P * g.Q,
-                       g.K);
+                       dim3(kThreads), 0, st, partials, bias, y, (uint32_t)per_split, p.splits,
+                       g.P * g.Q, g.K, make_fastdiv(g.K), make_fastdiv(g.P * g.Q));
     return hipGetLastError();
 }
 
