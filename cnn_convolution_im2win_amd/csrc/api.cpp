@@ -87,6 +87,8 @@ int64_t chunk_workspace(const Geom& g, Path p, int64_t n) {
     if (p == PATH_FP32) {
         int s = fp32_splits(g, (int)n);
         if (s > 1) bytes += (int64_t)s * n * g.K * g.P * g.Q * 4;
+    } else if (p == PATH_MFMA) {
+        bytes += round_up((int64_t)mfma_prep_bytes(g), 256);   // re-laid-out filter
     }
     return bytes;
 }
@@ -142,6 +144,14 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
 
     hipStream_t st = (hipStream_t)stream;
     (void)hipGetLastError();   // clear a stale error so launch checks report our own
+    // the matrix-core kernel's filter copy sits after the window tensor of
+    // the largest chunk; written once, used by every chunk
+    unsigned char* aperm = nullptr;
+    if (p == PATH_MFMA && !generic && mfma_prep_bytes(g) > 0) {
+        aperm = (unsigned char*)ws + round_up(window_bytes_per_image(g, lay) * nc, 256);
+        hipError_t e = launch_mfma_prep(g, out, w, aperm, st);
+        if (e != hipSuccess) return from_hip(e);
+    }
     const int64_t x_img = (int64_t)g.C * g.H * g.W * g.elem;
     const int64_t y_img = (int64_t)g.K * g.P * g.Q * elem_bytes(out);
     unsigned char* wsb = (unsigned char*)ws;
@@ -162,7 +172,7 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
             e = launch_conv_fp32(g, (const float*)wsb, (const float*)w, (const float*)bias,
                                  (float*)yc, n, partials, splits, generic, st);
         } else if (p == PATH_MFMA) {
-            e = launch_conv_mfma(g, in, out, wsb, w, bias, yc, n, generic, st);
+            e = launch_conv_mfma(g, in, out, wsb, w, aperm, bias, yc, n, generic, st);
         } else {
             e = launch_conv_dw(g, in, out, wsb, w, bias, yc, n, generic, st);
         }

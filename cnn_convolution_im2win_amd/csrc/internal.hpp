@@ -68,9 +68,15 @@ hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, cons
                             hipStream_t st);
 
 // fp16/bf16 dense contraction over an HWC window tensor on the matrix cores.
+// The row kernel multiplies a re-laid-out copy of the filter (`aperm`,
+// mfma_prep_bytes(g) bytes, written by launch_mfma_prep once per call);
+// mfma_prep_bytes is 0 when the layer takes the generic kernel.
+size_t mfma_prep_bytes(const Geom& g);
+hipError_t launch_mfma_prep(const Geom& g, ciw_dtype out, const void* w, void* aperm,
+                            hipStream_t st);
 hipError_t launch_conv_mfma(const Geom& g, ciw_dtype in, ciw_dtype out, const void* xw,
-                            const void* w, const void* bias, void* y, int n_images,
-                            bool generic, hipStream_t st);
+                            const void* w, const void* aperm, const void* bias, void* y,
+                            int n_images, bool generic, hipStream_t st);
 
 // Depthwise contraction over a CHW window tensor.
 hipError_t launch_conv_dw(const Geom& g, ciw_dtype in, ciw_dtype out, const void* xw,
