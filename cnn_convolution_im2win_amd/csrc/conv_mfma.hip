@@ -198,11 +198,18 @@ __device__ __forceinline__ f32x16 mfma32<bf16_t>(const uint4& a, const uint4& b,
                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 
-// LDS chunk position of 16-byte chunk ch (XOR of its low three bits with the
-// next three: consecutive pixels whose windows are a multiple of 128 bytes
-// apart then land on different banks).  Self-inverse.
-__device__ __forceinline__ int swz_chunk(int ch, int on) {
-    return on ? (ch ^ ((ch >> 3) & 7)) : ch;
+// LDS position of 16-byte chunk ch when swizzled: its low four bits XORed
+// with bits 3..6, a permutation of each group of 16 chunks (256 bytes) that
+// spreads window starts 24 or 72 chunks apart over distinct banks.
+__device__ __forceinline__ int swz_pos(int ch, int on) {
+    return on ? (ch ^ ((ch >> 3) & 15)) : ch;
+}
+
+// The chunk stored at LDS position p (inverse of swz_pos).
+__device__ __forceinline__ int swz_chunk_at(int p, int on) {
+    if (!on) return p;
+    const int z = p ^ (((p >> 4) & 7) << 1);
+    return z ^ ((z >> 3) & 1);
 }
 
 // Mask of the 8 elements [t0, t0 + 8) that lie inside [lo, hi).
@@ -231,9 +238,9 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
     const int npb = a.nph * a.mblocks;
     constexpr int Tp = STEPS * 16;
 
-    uint16_t* rowbuf = lds;                                          // 2 x buf_elems
-    TOut* otile = reinterpret_cast<TOut*>(lds + 2 * a.buf_elems);    // 2 x K x ostride
-    float* bias_l = reinterpret_cast<float*>(otile + 2 * a.K * a.ostride);   // 64 floats
+    uint16_t* rowbuf = lds;                                              // 2 x buf_elems
+    float* otile = reinterpret_cast<float*>(lds + 2 * a.buf_elems);      // K x ostride fp32
+    float* bias_l = otile + a.K * a.ostride;                             // 64 floats
 
     // ---- A fragments, from the filter the prep kernel laid out as
     // aperm[phase][64 output channels][Tp] (phase-shifted, zero-padded):
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
         for (int j = 0; j < kMfMaxChunks; ++j) {
             if (j * kThreads < a.copy_chunks) {
                 const int p = min(tid + j * kThreads, a.copy_chunks - 1);
-                const int ch = min(swz_chunk(p, a.swz), a.nchunks - 1);
+                const int ch = min(swz_chunk_at(p, a.swz), a.nchunks - 1);
                 stg[j] = src[ch];
             }
         }
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
         for (int j = 0; j < kMfMaxChunks; ++j) {
             const int p = tid + j * kThreads;
             if (p < a.copy_chunks)
-                dst[p] = swz_chunk(p, a.swz) < a.nchunks ? stg[j] : make_uint4(0u, 0u, 0u, 0u);
+                dst[p] = swz_chunk_at(p, a.swz) < a.nchunks ? stg[j] : make_uint4(0u, 0u, 0u, 0u);
         }
     };
 
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
         if (next < a.rows) load_row(next);
 
         const uint16_t* lb = rowbuf + buf * a.buf_elems;
-        TOut* ot = otile + buf * a.K * a.ostride;
+        float* ot = otile;
         // blocks pb0 + 2 j; block j uses the fragments of set j % NSET
         for (int base = 0; pb0 + 2 * base < npb; base += NSET)
 #pragma unroll
@@ -308,9 +315,13 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
             const int mb = pb / a.nph;
             const int delta = (ph * a.D) & 7;
             const int wpix = a.nph * (32 * mb + ml) + ph;
+            // pixels past the row end (never stored) read the last pixel of
+            // their phase instead, so reads stay inside the row buffer
+            const int wlast = a.Q - 1 >= ph ? a.Q - 1 - (a.Q - 1 - ph) % a.nph : ph;
+            const int wread = min(wpix, wlast);
             // first element of the run this lane reads: window start minus
             // delta (a multiple of 8), then 16 per step
-            const int chunk0 = (wpix * a.D - delta) / 8 + g;
+            const int chunk0 = (wread * a.D - delta) / 8 + g;
             // steps [1, s_full) hold only window entries; with MASK the
             // first step (when delta > 0) and the steps from s_full on are
             // masked (without MASK the plan guarantees there are none)
@@ -320,13 +331,13 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
             for (int i = 0; i < 16; ++i) acc[i] = 0.f;
             // B fragments double-buffered in registers: the read of step
             // s + 1 is in flight while step s multiplies
-            uint4 bn = *reinterpret_cast<const uint4*>(lb + 8 * swz_chunk(chunk0, a.swz));
+            uint4 bn = *reinterpret_cast<const uint4*>(lb + 8 * swz_pos(chunk0, a.swz));
 #pragma unroll
             for (int s2 = 0; s2 < STEPS; ++s2) {
                 uint4 b = bn;
                 if (s2 + 1 < STEPS)
                     bn = *reinterpret_cast<const uint4*>(
-                        lb + 8 * swz_chunk(chunk0 + 2 * (s2 + 1), a.swz));
+                        lb + 8 * swz_pos(chunk0 + 2 * (s2 + 1), a.swz));
                 if (MASK && ((s2 == 0 && delta > 0) || s2 >= s_full)) {
                     const uint4 mk = elem_mask(16 * s2 + 8 * g, delta, delta + a.T);
                     b.x &= mk.x; b.y &= mk.y; b.z &= mk.z; b.w &= mk.w;
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int k = kh * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                    if (k < a.K) ot[k * a.ostride + wpix] = from_f32<TOut>(acc[i] + bias_l[k]);
+                    if (k < a.K) ot[k * a.ostride + wpix] = acc[i];
                 }
             }
         }
@@ -350,21 +361,29 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
         const int h = row - n * a.P;
         TOut* yrow = y + (size_t)n * a.K * PQ + (size_t)h * a.Q;
         if (a.vec_store) {
-            constexpr int V = 16 / sizeof(TOut);
+            constexpr int V = 16 / sizeof(TOut);   // outputs per 16-byte store
             const int vq = a.Q / V;
             for (int i = tid; i < a.K * vq; i += kThreads) {
                 const int k = i / vq;
                 const int v = i - k * vq;
-                *reinterpret_cast<uint4*>(yrow + (size_t)k * PQ + v * V) =
-                    *reinterpret_cast<const uint4*>(ot + k * a.ostride + v * V);
+                const float b = bias_l[k];
+                const float* src = ot + k * a.ostride + v * V;
+                union {
+                    uint4 u;
+                    TOut e[V];
+                } pk;
+#pragma unroll
+                for (int e = 0; e < V; ++e) pk.e[e] = from_f32<TOut>(src[e] + b);
+                *reinterpret_cast<uint4*>(yrow + (size_t)k * PQ + v * V) = pk.u;
             }
         } else {
             for (int i = tid; i < a.K * a.Q; i += kThreads) {
                 const int k = i / a.Q;
                 const int wq = i - k * a.Q;
-                yrow[(size_t)k * PQ + wq] = ot[k * a.ostride + wq];
+                yrow[(size_t)k * PQ + wq] = from_f32<TOut>(ot[k * a.ostride + wq] + bias_l[k]);
             }
         }
+        __syncthreads();   // the output tile is rewritten by the next row
     }
 }
 
@@ -438,36 +457,47 @@ bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl) {
     const int mcount = (g.Q + nph - 1) / nph;
     const int mblocks = (mcount + 31) / 32;
     const int nchunks = g.pitchB / 8;
-    // bank spread of one 8-lane group of fragment reads: lanes are D*nph
-    // elements (D*nph/8 chunks) apart; odd chunk spacing needs no swizzle
+    // bank conflicts of the fragment reads: the 32 lanes of a half-wave read
+    // chunks D*nph/8 apart; count 16-lane groups that miss one of 16 bank
+    // groups (64 banks) and 8-lane groups that miss one of 8 (32 banks),
+    // without and with the swizzle, and keep the better layout
     const int sp = D * nph / 8;
-    int swz = 0;
-    if (sp % 2 == 0) {
-        bool ok = true;
-        for (int base = 0; base < 64 && ok; ++base) {
-            int seen = 0;
-            for (int m = 0; m < 8; ++m) {
+    auto conflicts = [&](int on) {
+        int bad = 0;
+        for (int base = 0; base < 64; ++base) {
+            int pos[32];
+            for (int m = 0; m < 32; ++m) {
                 const int ch = base + m * sp;
-                const int b = (ch ^ ((ch >> 3) & 7)) & 7;
-                if (seen & (1 << b)) ok = false;
-                seen |= 1 << b;
+                pos[m] = on ? (ch ^ ((ch >> 3) & 15)) : ch;
+            }
+            for (int ph = 0; ph < 32; ph += 16) {
+                int seen = 0;
+                for (int m = ph; m < ph + 16; ++m) seen |= 1 << (pos[m] & 15);
+                bad += seen != 0xffff;
+            }
+            for (int ph = 0; ph < 32; ph += 8) {
+                int seen = 0;
+                for (int m = ph; m < ph + 8; ++m) seen |= 1 << (pos[m] & 7);
+                bad += seen != 0xff;
             }
         }
-        swz = ok ? 1 : 0;
-    }
-    const int copy_chunks = swz ? (nchunks + 7) / 8 * 8 : nchunks;
+        return bad;
+    };
+    const int swz = conflicts(1) < conflicts(0) ? 1 : 0;
+    const int copy_chunks = swz ? (nchunks + 15) / 16 * 16 : nchunks;
     if (copy_chunks > kMfMaxChunks * kThreads) return false;
-    // the furthest chunk any fragment read touches (pixels up to the end of
-    // the last block, the whole padded reduction), rounded to 128 bytes
-    const int wmax = nph * (32 * mblocks - 1) + (nph - 1);
+    // the furthest chunk any fragment read touches (the last pixel's window
+    // over the whole padded reduction), rounded to 256 bytes
+    const int wmax = std::max(g.Q - 1, nph - 1);   // furthest pixel whose window is read
     const int last_chunk = (wmax * D) / 8 + 2 * steps + 1;
     int buf_chunks = std::max(copy_chunks, last_chunk + 1);
-    buf_chunks = (buf_chunks + 7) / 8 * 8;
+    buf_chunks = (buf_chunks + 15) / 16 * 16;
     const int buf = buf_chunks * 8;
-    const int ostride = (g.Q + 7) / 8 * 8;
-    const size_t lds = (size_t)2 * buf * 2 + (size_t)2 * g.K * ostride * out_bytes + 64 * 4;
+    const int ostride = (g.Q + 3) / 4 * 4;
+    const size_t lds = (size_t)2 * buf * 2 + (size_t)g.K * ostride * 4 + 64 * 4;
     const int crs = g.C * g.R * g.S;
-    if (lds > 65536 || (size_t)32 * crs * 2 > (size_t)2 * buf * 2 || (32 * crs) % 8) return false;
+    if (lds > 65536) return false;
+    (void)crs;
     a.C = g.C; a.K = g.K; a.R = g.R; a.S = g.S; a.P = g.P; a.Q = g.Q;
     a.pitch = g.pitchB;
     a.D = D; a.T = T;
