@@ -192,6 +192,235 @@ __global__ __launch_bounds__(kThreads) void im2win_hwc_kernel(const T* __restric
     }
 }
 
+// ------------------------------------------------- CHW layout, whole planes
+// One workgroup: `ppb` consecutive input planes (n, c), which are one
+// contiguous run of x, and their window rows, one contiguous run of the
+// window tensor.  Each plane is staged in LDS as the zero-padded tile of the
+// padded-input rows and columns its windows touch; the window rows are then
+// written with 16-byte stores in memory order.
+struct PlaneArgs {
+    int H, W, P, sh, ph, pw, dh, R;
+    int Wwin, len, pitch, Hp;      // Hp: padded input rows the windows touch
+    int planes, ppb, vec_in;
+    FastDiv fdHW, fdW, fdPP, fdPitch, fdR;
+};
+
+constexpr int kPlaneLds = 16384;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void im2win_chw_planes_kernel(const T* __restrict__ x,
+                                                                     T* __restrict__ xw,
+                                                                     PlaneArgs a) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T* tile = reinterpret_cast<T*>(smem_raw);
+    constexpr int V = 16 / sizeof(T);
+    const int tid = threadIdx.x;
+    const int p0 = blockIdx.x * a.ppb;
+    const int np = min(a.ppb, a.planes - p0);
+    const int tsz = a.Hp * a.Wwin;
+    const int HW = a.H * a.W;
+
+    for (int i = tid; i < np * tsz; i += kThreads) tile[i] = T(0);
+    __syncthreads();
+
+    // input element (plane, ih, iw) -> padded tile position (ih + ph, iw + pw)
+    auto put = [&](int e, T v) {
+        const uint32_t pl = fdiv(e, a.fdHW);
+        const int rem = e - pl * HW;
+        const uint32_t ih = fdiv(rem, a.fdW);
+        const int iw = rem - ih * a.W;
+        const int tr = ih + a.ph, tc = iw + a.pw;
+        if (tr < a.Hp && tc < a.Wwin) tile[pl * tsz + tr * a.Wwin + tc] = v;
+    };
+    const T* src = x + (size_t)p0 * HW;
+    const int nin = np * HW;
+    if (a.vec_in) {   // HW % V == 0: the planes start on 16-byte boundaries
+        for (int v = tid; v < nin / V; v += kThreads) {
+            union {
+                uint4 u;
+                T e[V];
+            } pk;
+            pk.u = reinterpret_cast<const uint4*>(src)[v];
+#pragma unroll
+            for (int i = 0; i < V; ++i) put(v * V + i, pk.e[i]);
+        }
+    } else {
+        for (int e = tid; e < nin; e += kThreads) put(e, src[e]);
+    }
+    __syncthreads();
+
+    // window rows of the block: np * P rows of `pitch` elements; element j
+    // of row (plane, h) is column x = j / R, filter row r = j % R, i.e. the
+    // padded input at (h*sh + r*dh, x); zero in the pitch tail
+    T* dst = xw + (size_t)p0 * a.P * a.pitch;
+    const int nvec = np * a.P * a.pitch / V;
+    for (int v = tid; v < nvec; v += kThreads) {
+        const int e0 = v * V;
+        const uint32_t rowi = fdiv(e0, a.fdPitch);
+        const int j0 = e0 - rowi * a.pitch;
+        const uint32_t pl = fdiv(rowi, a.fdPP);
+        const int h = rowi - pl * a.P;
+        const T* tp = tile + pl * tsz + h * a.sh * a.Wwin;
+        uint32_t xx = fdiv(j0, a.fdR);
+        int r = j0 - xx * a.R;
+        union {
+            uint4 u;
+            T e[V];
+        } pk;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            pk.e[i] = (j0 + i < a.len) ? tp[r * a.dh * a.Wwin + xx] : T(0);
+            if (++r == a.R) {
+                r = 0;
+                ++xx;
+            }
+        }
+        reinterpret_cast<uint4*>(dst)[v] = pk.u;
+    }
+}
+
+template <typename T>
+bool launch_chw_planes(const Geom& g, const void* x, void* xw, int n_images, hipStream_t st,
+                       hipError_t* err) {
+    PlaneArgs a;
+    a.H = g.H; a.W = g.W; a.P = g.P; a.sh = g.sh; a.ph = g.ph; a.pw = g.pw; a.dh = g.dh; a.R = g.R;
+    a.Wwin = g.Wwin; a.len = g.lenA; a.pitch = g.pitchA;
+    a.Hp = (g.P - 1) * g.sh + (g.R - 1) * g.dh + 1;
+    const int64_t tile_bytes = (int64_t)a.Hp * a.Wwin * sizeof(T);
+    if (tile_bytes > kPlaneLds) return false;
+    const int64_t planes = (int64_t)n_images * g.C;
+    if (planes >= (1ll << 31) || planes * g.H * g.W >= (1ll << 31)) return false;
+    a.planes = (int)planes;
+    int ppb = (int)(kPlaneLds / tile_bytes);
+    // keep at least ~1024 workgroups when there are enough planes
+    const int64_t cap = (planes + 1023) / 1024;
+    if (ppb > cap) ppb = (int)cap;
+    if (ppb < 1) ppb = 1;
+    a.ppb = ppb;
+    a.vec_in = ((int64_t)g.H * g.W) % (16 / (int)sizeof(T)) == 0 ? 1 : 0;
+    a.fdHW = make_fastdiv(g.H * g.W);
+    a.fdW = make_fastdiv(g.W);
+    a.fdPP = make_fastdiv(g.P);
+    a.fdPitch = make_fastdiv(g.pitchA);
+    a.fdR = make_fastdiv(g.R);
+    const int64_t blocks = (planes + ppb - 1) / ppb;
+    hipLaunchKernelGGL((im2win_chw_planes_kernel<T>), dim3((uint32_t)blocks), dim3(kThreads),
+                       (size_t)ppb * tile_bytes, st, (const T*)x, (T*)xw, a);
+    *err = hipGetLastError();
+    return true;
+}
+
+// ------------------------------------------------- HWC layout, whole rows
+// One workgroup: one window row (n, h) with all channels.  LDS holds the
+// row in output order, [x][r][c], with each column x padded so that
+// 16-byte accesses of neighbouring columns fall on different banks.  Loads
+// run along input rows (consecutive lanes, consecutive x) and gather 8
+// channels per lane; the row then leaves with 16-byte stores.  Used when C
+// is a multiple of the 16-byte vector width.  Consecutive rows h of an image
+// read overlapping input rows, so they are kept on one XCD (its L2).
+struct HwcRowArgs {
+    int C, H, W, P, sh, ph, pw, dh, R;
+    int Wwin, len, pitch;
+    int xs;                        // LDS column stride (elements)
+    int rows;
+    FastDiv fdP, fdCv, fdRC, fdWwin;
+    uint32_t xcd_per, xcd_rem;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void im2win_hwc_rows_kernel(const T* __restrict__ x,
+                                                                   T* __restrict__ xw,
+                                                                   HwcRowArgs a) {
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T* tile = reinterpret_cast<T*>(smem_raw);
+    constexpr int V = 16 / sizeof(T);
+    const int tid = threadIdx.x;
+    const uint32_t bid = blockIdx.x;
+    const uint32_t xcd = bid & 7u, slot = bid >> 3;
+    const uint32_t row = xcd < a.xcd_rem ? xcd * (a.xcd_per + 1) + slot
+                                         : a.xcd_rem * (a.xcd_per + 1) + (xcd - a.xcd_rem) * a.xcd_per + slot;
+    const uint32_t n = fdiv(row, a.fdP);
+    const int h = row - n * a.P;
+    const int HW = a.H * a.W;
+    const int cv = a.C / V;                 // channel groups of V
+
+    // load: item (column xx, channel group gq, filter row r), xx fastest so
+    // that consecutive lanes read consecutive input columns
+    const int items = a.Wwin * a.R * cv;
+    for (int it = tid; it < items; it += kThreads) {
+        const uint32_t q = fdiv(it, a.fdWwin);
+        const int xx = it - q * a.Wwin;
+        const uint32_t r = fdiv(q, a.fdCv);
+        const int gq = q - r * cv;
+        const int ih = h * a.sh - a.ph + r * a.dh;
+        const int iw = xx - a.pw;
+        union {
+            uint4 u;
+            T e[V];
+        } pk;
+        if (ih >= 0 && ih < a.H && iw >= 0 && iw < a.W) {
+            const T* sp = x + ((size_t)n * a.C + gq * V) * HW + ih * a.W + iw;
+#pragma unroll
+            for (int i = 0; i < V; ++i) pk.e[i] = sp[(size_t)i * HW];
+        } else {
+            pk.u = make_uint4(0u, 0u, 0u, 0u);
+        }
+        *reinterpret_cast<uint4*>(tile + xx * a.xs + r * a.C + gq * V) = pk.u;
+    }
+    __syncthreads();
+
+    // store: the row's `pitch` elements as 16-byte vectors (zero past len)
+    T* dst = xw + (size_t)row * a.pitch;
+    const int rc = a.R * a.C;
+    for (int v = tid; v < a.pitch / V; v += kThreads) {
+        const int e0 = v * V;
+        uint4 u = make_uint4(0u, 0u, 0u, 0u);
+        if (e0 < a.len) {
+            const uint32_t xx = fdiv(e0, a.fdRC);
+            u = *reinterpret_cast<const uint4*>(tile + xx * a.xs + (e0 - xx * rc));
+        }
+        reinterpret_cast<uint4*>(dst)[v] = u;
+    }
+}
+
+template <typename T>
+bool launch_hwc_rows(const Geom& g, const void* x, void* xw, int n_images, hipStream_t st,
+                     hipError_t* err) {
+    constexpr int V = 16 / sizeof(T);
+    if (g.C % V) return false;
+    HwcRowArgs a;
+    a.C = g.C; a.H = g.H; a.W = g.W; a.P = g.P; a.sh = g.sh; a.ph = g.ph; a.pw = g.pw;
+    a.dh = g.dh; a.R = g.R;
+    a.Wwin = g.Wwin; a.len = g.lenB; a.pitch = g.pitchB;
+    // column stride: R*C plus a pad that makes it 4 mod 8 dwords, so the
+    // 16-byte writes of 8 consecutive columns hit distinct bank groups
+    const int rc = g.R * g.C;
+    int xs = rc;
+    for (int pad = 0; pad < 8 * V; pad += V) {
+        const int words = (rc + pad) * (int)sizeof(T) / 4;
+        if (words % 8 == 4) {
+            xs = rc + pad;
+            break;
+        }
+    }
+    a.xs = xs;
+    const int64_t lds = (int64_t)g.Wwin * xs * sizeof(T);
+    if (lds > 32768) return false;
+    const int64_t rows = (int64_t)n_images * g.P;
+    if (rows >= (1ll << 31)) return false;
+    a.rows = (int)rows;
+    a.fdP = make_fastdiv(g.P);
+    a.fdCv = make_fastdiv(g.C / V);
+    a.fdRC = make_fastdiv(rc);
+    a.fdWwin = make_fastdiv(g.Wwin);
+    a.xcd_per = (uint32_t)(rows / 8);
+    a.xcd_rem = (uint32_t)(rows % 8);
+    hipLaunchKernelGGL((im2win_hwc_rows_kernel<T>), dim3((uint32_t)rows), dim3(kThreads),
+                       (size_t)lds, st, (const T*)x, (T*)xw, a);
+    *err = hipGetLastError();
+    return true;
+}
+
 template <typename T>
 hipError_t launch_chw(const Geom& g, const void* x, void* xw, int n_images, hipStream_t st) {
     ChwArgs a;
@@ -275,9 +504,18 @@ hipError_t launch_transform(const Geom& g, ciw_dtype dt, ciw_win_layout lay, con
                             void* xw, int n_images, hipStream_t st) {
     // the repack copies element bit patterns (as unsigned integers of the
     // element's width), so fp16 and bf16 share a kernel
-    if (lay == CIW_WIN_CHW)
+    if (n_images == 0) return hipSuccess;
+    hipError_t e = hipSuccess;
+    if (lay == CIW_WIN_CHW) {
+        if (dt == CIW_F32 ? launch_chw_planes<uint32_t>(g, x, xw, n_images, st, &e)
+                          : launch_chw_planes<uint16_t>(g, x, xw, n_images, st, &e))
+            return e;
         return dt == CIW_F32 ? launch_chw<uint32_t>(g, x, xw, n_images, st)
                              : launch_chw<uint16_t>(g, x, xw, n_images, st);
+    }
+    if (dt == CIW_F32 ? launch_hwc_rows<uint32_t>(g, x, xw, n_images, st, &e)
+                      : launch_hwc_rows<uint16_t>(g, x, xw, n_images, st, &e))
+        return e;
     return dt == CIW_F32 ? launch_hwc<uint32_t>(g, x, xw, n_images, st)
                          : launch_hwc<uint16_t>(g, x, xw, n_images, st);
 }
