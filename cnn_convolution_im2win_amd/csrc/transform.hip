@@ -314,20 +314,24 @@ bool launch_chw_planes(const Geom& g, const void* x, void* xw, int n_images, hip
 // One workgroup: one window row (n, h) with all channels.  LDS holds the
 // row in output order, [x][r][c], with each column x padded so that
 // 16-byte accesses of neighbouring columns fall on different banks.  Loads
-// run along input rows (consecutive lanes, consecutive x) and gather 8
-// channels per lane; the row then leaves with 16-byte stores.  Used when C
-// is a multiple of the 16-byte vector width.  Consecutive rows h of an image
+// run along input rows (consecutive lanes, consecutive x) and gather a
+// vector of channels per lane (or one channel when C is not a multiple of
+// the vector width); the row then leaves with 16-byte stores.  Consecutive
+// rows h of an image
 // read overlapping input rows, so they are kept on one XCD (its L2).
 struct HwcRowArgs {
     int C, H, W, P, sh, ph, pw, dh, R;
     int Wwin, len, pitch;
     int xs;                        // LDS column stride (elements)
-    int rows;
-    FastDiv fdP, fdCv, fdRC, fdWwin;
+    int rows, vec_w;               // vec_w: input rows are whole 16-byte vectors
+    FastDiv fdP, fdCv, fdRC, fdWwin, fdWv, fdR;
     uint32_t xcd_per, xcd_rem;
 };
 
-template <typename T>
+// CV channels per load item: the 16-byte vector width when C is a multiple
+// of it, else 1 (then the LDS row is exactly the output row, xs = R*C, and
+// its tail up to a whole vector is zeroed).
+template <typename T, int CV>
 __global__ __launch_bounds__(kThreads) void im2win_hwc_rows_kernel(const T* __restrict__ x,
                                                                    T* __restrict__ xw,
                                                                    HwcRowArgs a) {
@@ -342,11 +346,43 @@ __global__ __launch_bounds__(kThreads) void im2win_hwc_rows_kernel(const T* __re
     const uint32_t n = fdiv(row, a.fdP);
     const int h = row - n * a.P;
     const int HW = a.H * a.W;
-    const int cv = a.C / V;                 // channel groups of V
+    const int cv = a.C / CV;                // channel groups of CV
+    if (CV == 1 && a.vec_w) {
+        // input rows are whole 16-byte vectors: zero the LDS row, then each
+        // item moves 16 bytes of one input row (channel c, filter row r)
+        const int len_v = (a.len + V - 1) / V * V;
+        for (int i = tid; i < len_v / V; i += kThreads)
+            reinterpret_cast<uint4*>(tile)[i] = make_uint4(0u, 0u, 0u, 0u);
+        __syncthreads();
+        const int wv = a.W / V;
+        const int vitems = a.C * a.R * wv;
+        for (int it = tid; it < vitems; it += kThreads) {
+            const uint32_t q = fdiv(it, a.fdWv);
+            const int jv = it - q * wv;
+            const uint32_t c = fdiv(q, a.fdR);
+            const int r = q - c * a.R;
+            const int ih = h * a.sh - a.ph + r * a.dh;
+            if (ih < 0 || ih >= a.H) continue;
+            union {
+                uint4 u;
+                T e[V];
+            } pk;
+            pk.u = reinterpret_cast<const uint4*>(x + (((size_t)n * a.C + c) * a.H + ih) * a.W)[jv];
+            T* tp = tile + (jv * V + a.pw) * a.xs + r * a.C + c;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                if (jv * V + i + a.pw < a.Wwin) tp[i * a.xs] = pk.e[i];
+            }
+        }
+        __syncthreads();
+    } else if (CV == 1) {
+        const int len_v = (a.len + V - 1) / V * V;
+        for (int i = a.len + tid; i < len_v; i += kThreads) tile[i] = T(0);
+    }
 
     // load: item (column xx, channel group gq, filter row r), xx fastest so
     // that consecutive lanes read consecutive input columns
-    const int items = a.Wwin * a.R * cv;
+    const int items = (CV == 1 && a.vec_w) ? 0 : a.Wwin * a.R * cv;
     for (int it = tid; it < items; it += kThreads) {
         const uint32_t q = fdiv(it, a.fdWwin);
         const int xx = it - q * a.Wwin;
@@ -354,18 +390,22 @@ __global__ __launch_bounds__(kThreads) void im2win_hwc_rows_kernel(const T* __re
         const int gq = q - r * cv;
         const int ih = h * a.sh - a.ph + r * a.dh;
         const int iw = xx - a.pw;
-        union {
-            uint4 u;
-            T e[V];
-        } pk;
-        if (ih >= 0 && ih < a.H && iw >= 0 && iw < a.W) {
-            const T* sp = x + ((size_t)n * a.C + gq * V) * HW + ih * a.W + iw;
-#pragma unroll
-            for (int i = 0; i < V; ++i) pk.e[i] = sp[(size_t)i * HW];
+        const bool inside = ih >= 0 && ih < a.H && iw >= 0 && iw < a.W;
+        const T* sp = x + ((size_t)n * a.C + gq * CV) * HW + ih * a.W + iw;
+        if (CV == 1) {
+            tile[xx * a.xs + r * a.C + gq] = inside ? sp[0] : T(0);
         } else {
+            union {
+                uint4 u;
+                T e[V];
+            } pk;
             pk.u = make_uint4(0u, 0u, 0u, 0u);
+            if (inside) {
+#pragma unroll
+                for (int i = 0; i < V; ++i) pk.e[i] = sp[(size_t)i * HW];
+            }
+            *reinterpret_cast<uint4*>(tile + xx * a.xs + r * a.C + gq * V) = pk.u;
         }
-        *reinterpret_cast<uint4*>(tile + xx * a.xs + r * a.C + gq * V) = pk.u;
     }
     __syncthreads();
 
@@ -387,7 +427,7 @@ template <typename T>
 bool launch_hwc_rows(const Geom& g, const void* x, void* xw, int n_images, hipStream_t st,
                      hipError_t* err) {
     constexpr int V = 16 / sizeof(T);
-    if (g.C % V) return false;
+    const bool vec = g.C % V == 0;
     HwcRowArgs a;
     a.C = g.C; a.H = g.H; a.W = g.W; a.P = g.P; a.sh = g.sh; a.ph = g.ph; a.pw = g.pw;
     a.dh = g.dh; a.R = g.R;
@@ -396,7 +436,7 @@ bool launch_hwc_rows(const Geom& g, const void* x, void* xw, int n_images, hipSt
     // 16-byte writes of 8 consecutive columns hit distinct bank groups
     const int rc = g.R * g.C;
     int xs = rc;
-    for (int pad = 0; pad < 8 * V; pad += V) {
+    for (int pad = 0; vec && pad < 8 * V; pad += V) {
         const int words = (rc + pad) * (int)sizeof(T) / 4;
         if (words % 8 == 4) {
             xs = rc + pad;
@@ -404,19 +444,26 @@ bool launch_hwc_rows(const Geom& g, const void* x, void* xw, int n_images, hipSt
         }
     }
     a.xs = xs;
-    const int64_t lds = (int64_t)g.Wwin * xs * sizeof(T);
+    const int64_t lds = ((int64_t)g.Wwin * xs + V) * sizeof(T);
     if (lds > 32768) return false;
     const int64_t rows = (int64_t)n_images * g.P;
     if (rows >= (1ll << 31)) return false;
     a.rows = (int)rows;
     a.fdP = make_fastdiv(g.P);
-    a.fdCv = make_fastdiv(g.C / V);
+    a.fdCv = make_fastdiv(vec ? g.C / V : g.C);
     a.fdRC = make_fastdiv(rc);
     a.fdWwin = make_fastdiv(g.Wwin);
+    a.vec_w = (g.W % V == 0) ? 1 : 0;
+    a.fdWv = make_fastdiv(g.W / V > 0 ? g.W / V : 1);
+    a.fdR = make_fastdiv(g.R);
     a.xcd_per = (uint32_t)(rows / 8);
     a.xcd_rem = (uint32_t)(rows % 8);
-    hipLaunchKernelGGL((im2win_hwc_rows_kernel<T>), dim3((uint32_t)rows), dim3(kThreads),
-                       (size_t)lds, st, (const T*)x, (T*)xw, a);
+    if (vec)
+        hipLaunchKernelGGL((im2win_hwc_rows_kernel<T, V>), dim3((uint32_t)rows), dim3(kThreads),
+                           (size_t)lds, st, (const T*)x, (T*)xw, a);
+    else
+        hipLaunchKernelGGL((im2win_hwc_rows_kernel<T, 1>), dim3((uint32_t)rows), dim3(kThreads),
+                           (size_t)lds, st, (const T*)x, (T*)xw, a);
     *err = hipGetLastError();
     return true;
 }
