@@ -147,6 +147,36 @@ class Step:
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the HIP/C++ sources of the library (which kernels the
+    stored counter readings belong to)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "cnn_convolution_im2win_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cpp", ".hpp")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per contraction call from profiles/traffic.json (rocprofv3
+    FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or None when
+    the file is missing or was measured on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("source_sha256") != kernel_source_hash():
+        return None
+    entry = data.get("workloads", {}).get(workload)
+    return None if entry is None else entry.get("bytes_per_call")
+
+
 def time_steps(step: Step, steps: int, warmup: int):
     import torch
     for _ in range(warmup):
@@ -214,6 +244,7 @@ def measure_layer(L: workloads.Layer, steps: int, warmup: int) -> dict:
         "contract_gbs": round(step.contraction_bytes() / (co_ms * 1e-3) / 1e9, 1),
         "roofline": step.contraction_roofline(co_ms),
     }
+    res["roofline"]["traffic"] = stored_traffic(L.name)
     if not step.depthwise and L.dtype != "f32":
         res["mfma_frac"] = round(res["contract_tflops"] / PEAK_TFLOPS["mfma_" + L.dtype], 4)
     return res, step
