@@ -143,43 +143,55 @@ __global__ __launch_bounds__(kThreads) void conv_mfma_generic_kernel(
 // ------------------------------------------------------------ row kernel
 // Persistent kernel for layers whose filter fits in registers (K <= 64,
 // padded reduction <= 640 per phase set).  The GEMM view is the paper's
-// (§III-D): M = output channels, N = output pixels, reduction over the
-// window.  One workgroup owns whole window rows (n, h):
-//   - each of its four waves keeps its A operand -- 32 output channels x
-//     the whole padded reduction, as v_mfma_f32_32x32x16 fragments -- in
-//     registers for the life of the kernel;
-//   - window rows stream through two LDS buffers: while one row is
-//     multiplied the next row's loads are in flight (double buffering and
-//     load/compute overlap, §III-D/§III-E);
-//   - the window of pixel w is the contiguous LDS run at w*D, D =
+// (§III-D), output pixels x output channels reduced over the window.  One
+// workgroup owns whole window rows (n, h):
+//   - each of its four waves keeps the filter fragments of 32 output
+//     channels over the whole padded reduction in registers for the life of
+//     the kernel;
+//   - window rows stream through a ring of LDS buffers, copied from global
+//     memory straight into LDS several rows ahead of the row being
+//     multiplied (load/compute overlap, §III-D/§III-E);
+//   - the window of pixel w is the run of LDS chunks starting at w*D, D =
 //     stride_w*R*C, so consecutive pixels read overlapping runs and each
-//     window element is fetched from HBM once per output row ("elements
-//     loaded in a previous window remain in cache", §III-C);
-//   - results pass through an LDS tile so each output row leaves with
-//     contiguous stores.
-// Alignment: a B fragment is a 16-byte LDS read, so its start must be a
-// multiple of 8 elements.  Pixels are grouped into `nph` phases (w mod nph,
-// nph = 8 / gcd(D, 8)) whose window starts share one misalignment delta;
-// each phase multiplies a copy of the filter shifted right by delta, and
-// reads start delta elements early.  Reduction entries outside the window
-// (the shift, the padding to a multiple of 16) are zero in A and masked to
-// zero in B, so values outside a window never reach a stored output.
+//     window element crosses HBM once per output row ("elements loaded in
+//     a previous window remain in cache", §III-C);
+//   - the window fragment is the MFMA's first operand, so a lane ends up
+//     holding 16 pixels of one output channel, four of them adjacent; they
+//     go through an LDS tile so each output row leaves with whole-vector
+//     stores.
+// Alignment: a window fragment is a 16-byte LDS read, so its start must be
+// a multiple of 8 elements.  Pixels are grouped into `nph` phases (w mod
+// nph, nph = 8 / gcd(D, 8)) whose window starts share one misalignment
+// delta; each phase multiplies a copy of the filter shifted right by delta,
+// and reads start delta elements early.  Reduction entries outside the
+// window (the shift, the padding to a multiple of 16) are zero in the filter
+// and masked to zero in the window fragment, so values outside a window
+// never reach a stored output.
+// Bank conflicts: the 32 pixels of a fragment start G = D*nph/8 chunks
+// apart.  With nph > 1, G is odd and consecutive lanes fall in distinct
+// banks.  With nph = 1 the row is stored with one pad chunk after every PAD
+// chunks (PAD the largest power of two dividing G, at most 8), which makes
+// the lane stride G + G/PAD odd; every run starts on the pad grid, so the
+// offset of each reduction step is a compile-time constant.
 struct MfRowArgs {
     int C, K, R, S, P, Q, pitch;   // pitch: window row pitch (elements)
     int D, T;                      // window start stride, window length
     int nph, mblocks;              // pixel phases, 32-pixel blocks per phase
-    int steps;                     // padded reduction / 16
+    int G;                         // chunks between window starts (nph == 1)
     int nchunks;                   // 16-byte chunks of a window row
-    int copy_chunks;               // chunks copied (nchunks rounded to 8 when swizzled)
-    int swz;                       // XOR-swizzle 16-byte chunks within 128-byte groups
+    int copy_chunks;               // LDS chunk positions of a row (pads included)
     int buf_elems;                 // elements per LDS row buffer
+    int nbuf;                      // row buffers in the LDS ring
+    int nd;                        // row-copy instructions per thread per row
     int ostride;                   // LDS output tile row stride (elements of TOut)
     int vec_store;                 // output rows are whole 16-byte vectors
+    int ns;                        // output store instructions per thread per row
     int rows;                      // N * P
-    FastDiv fdP, fdCp, fdR, fdRS;
+    FastDiv fdP;
 };
 
 constexpr int kMfMaxChunks = 8;    // 16-byte chunks per thread per row copy
+constexpr int kPf = 4;             // window fragments read ahead of the multiplies
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -198,18 +210,20 @@ __device__ __forceinline__ f32x16 mfma32<bf16_t>(const uint4& a, const uint4& b,
                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 
-// LDS position of 16-byte chunk ch when swizzled: its low four bits XORed
-// with bits 3..6, a permutation of each group of 16 chunks (256 bytes) that
-// spreads window starts 24 or 72 chunks apart over distinct banks.
-__device__ __forceinline__ int swz_pos(int ch, int on) {
-    return on ? (ch ^ ((ch >> 3) & 15)) : ch;
+// The window chunk whose copy LDS position q holds: one pad position after
+// every PAD chunks, filled with the chunk before it.
+template <int PAD>
+__device__ __forceinline__ int pad_src(int q) {
+    if (PAD == 1) return q;
+    const int grp = q / (PAD + 1);
+    return grp * PAD + min(q - grp * (PAD + 1), PAD - 1);
 }
 
-// The chunk stored at LDS position p (inverse of swz_pos).
-__device__ __forceinline__ int swz_chunk_at(int p, int on) {
-    if (!on) return p;
-    const int z = p ^ (((p >> 4) & 7) << 1);
-    return z ^ ((z >> 3) & 1);
+// Byte offset of reduction step s within a run: 32 bytes a step plus one
+// pad chunk for every PAD chunks passed.
+template <int PAD>
+__device__ constexpr int step_off(int s) {
+    return PAD == 1 ? 32 * s : 32 * s + 16 * ((2 * s) / PAD);
 }
 
 // Mask of the 8 elements [t0, t0 + 8) that lie inside [lo, hi).
@@ -223,89 +237,164 @@ __device__ __forceinline__ uint4 elem_mask(int t0, int lo, int hi) {
     return make_uint4(m[0], m[1], m[2], m[3]);
 }
 
-template <typename TIn, typename TOut, int NSET, int STEPS, bool MASK>
+// Four adjacent outputs as one LDS write (8 bytes of halves, 16 of floats).
+template <typename TOut>
+__device__ __forceinline__ void put4(TOut* p, float a0, float a1, float a2, float a3);
+
+template <>
+__device__ __forceinline__ void put4<float>(float* p, float a0, float a1, float a2, float a3) {
+    *reinterpret_cast<float4*>(p) = make_float4(a0, a1, a2, a3);
+}
+
+template <typename TOut>
+__device__ __forceinline__ void put4(TOut* p, float a0, float a1, float a2, float a3) {
+    const uint32_t lo = (uint32_t)f32_bits<TOut>(a0) | ((uint32_t)f32_bits<TOut>(a1) << 16);
+    const uint32_t hi = (uint32_t)f32_bits<TOut>(a2) | ((uint32_t)f32_bits<TOut>(a3) << 16);
+    *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+
+// s_waitcnt with a run-time vector-memory count (the instruction takes an
+// immediate): wait until at most n of this wave's vector memory operations
+// are outstanding and all its LDS operations are done.
+__device__ __forceinline__ void wait_vm_lgkm(int n) {
+    asm volatile("" ::: "memory");
+    switch (n < 0 ? 0 : (n > 63 ? 63 : n)) {
+#define CIW_WAIT_CASE(k) \
+    case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | (7 << 4) | (0 << 8)); break;
+#define CIW_WAIT_CASE8(b) CIW_WAIT_CASE(b) CIW_WAIT_CASE(b + 1) CIW_WAIT_CASE(b + 2) CIW_WAIT_CASE(b + 3) \
+    CIW_WAIT_CASE(b + 4) CIW_WAIT_CASE(b + 5) CIW_WAIT_CASE(b + 6) CIW_WAIT_CASE(b + 7)
+        CIW_WAIT_CASE8(0) CIW_WAIT_CASE8(8) CIW_WAIT_CASE8(16) CIW_WAIT_CASE8(24)
+        CIW_WAIT_CASE8(32) CIW_WAIT_CASE8(40) CIW_WAIT_CASE8(48) CIW_WAIT_CASE8(56)
+#undef CIW_WAIT_CASE8
+#undef CIW_WAIT_CASE
+    }
+    asm volatile("" ::: "memory");
+}
+
+// Wait for this wave's LDS operations only.
+__device__ __forceinline__ void wait_vm_lgkm_lds_only() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier without the memory fence __syncthreads adds (the waits
+// above are placed by hand so row copies can stay in flight across it).
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wg_barrier_lds() {
+    wait_vm_lgkm_lds_only();
+    wg_barrier();
+}
+
+template <typename TIn, typename TOut, int NSET, int STEPS, bool MASK, int PAD>
 __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
     const uint16_t* __restrict__ xw, const uint16_t* __restrict__ aperm,
     const TIn* __restrict__ bias, TOut* __restrict__ y, MfRowArgs a) {
     extern __shared__ __align__(16) uint16_t lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int kh = wave & 1;          // output channels [32 kh, 32 kh + 32)
     const int pb0 = wave >> 1;        // pixel blocks pb0, pb0 + 2, ...
     const int g = lane >> 5;          // which 8 of a fragment's 16 reduction entries
-    const int ml = lane & 31;         // fragment column
+    const int ml = lane & 31;         // fragment row (pixel) / column (channel)
     const int npb = a.nph * a.mblocks;
-    constexpr int Tp = STEPS * 16;
 
-    uint16_t* rowbuf = lds;                                              // 2 x buf_elems
-    float* otile = reinterpret_cast<float*>(lds + 2 * a.buf_elems);      // K x ostride fp32
-    float* bias_l = otile + a.K * a.ostride;                             // 64 floats
+    uint16_t* ring = lds;                                                 // nbuf x buf_elems
+    TOut* otile = reinterpret_cast<TOut*>(lds + a.nbuf * a.buf_elems);   // K x ostride
+    float* bias_l = reinterpret_cast<float*>(otile + a.K * a.ostride);   // 64 floats
 
-    // ---- A fragments, from the filter the prep kernel laid out as
-    // aperm[phase][64 output channels][Tp] (phase-shifted, zero-padded):
-    // lane holds A[m = lane % 32][16 s + 8 (lane / 32) + 0..7]
-    uint4 A[NSET][STEPS];
+    // ---- filter fragments, laid out by the prep kernel in fragment order
+    // (phase-shifted, zero-padded): lane holds F[t = 16 s + 8 (lane / 32)
+    // + 0..7][k = 32 kh + lane % 32], the second MFMA operand
+    uint4 F[NSET][STEPS];
 #pragma unroll
     for (int j = 0; j < NSET; ++j) {
         const int pb = min(pb0 + 2 * j, npb - 1);
-        const uint16_t* ap = aperm + ((size_t)(pb % a.nph) * 64 + kh * 32 + ml) * Tp + 8 * g;
+        const uint16_t* fp = aperm + ((size_t)((pb % a.nph) * 2 + kh) * STEPS * 64 + lane) * 8;
 #pragma unroll
         for (int s2 = 0; s2 < STEPS; ++s2)
-            A[j][s2] = *reinterpret_cast<const uint4*>(ap + 16 * s2);
+            F[j][s2] = *reinterpret_cast<const uint4*>(fp + 512 * s2);
     }
-    // wait for them here, not at their first use inside the row loop (where
-    // the wait would also drain the next row's prefetch)
+    if (tid < 64) bias_l[tid] = (bias && tid < a.K) ? to_f32(bias[tid]) : 0.f;
+    // complete these loads now: the wait counts below cover only row copies
+    // and output stores
 #pragma unroll
     for (int j = 0; j < NSET; ++j)
 #pragma unroll
-        for (int s2 = 0; s2 < STEPS; ++s2) asm volatile("" ::"v"(A[j][s2].x));
+        for (int s2 = 0; s2 < STEPS; ++s2) asm volatile("" ::"v"(F[j][s2].x));
+    wait_vm_lgkm(0);
 
-    // ---- window rows: global -> registers -> LDS (chunk positions swizzled).
-    // Loads are unconditional (clamped addresses) so they all issue at once.
-    uint4 stg[kMfMaxChunks];
-    auto load_row = [&](int row) {
-        const uint4* src = reinterpret_cast<const uint4*>(xw + (size_t)row * a.pitch);
+    // ---- window rows: global -> LDS directly (no registers), into a ring of
+    // nbuf row buffers, nbuf - 1 rows ahead of the row being multiplied.
+    // Every wave issues exactly a.nd copy instructions per row, so the
+    // number of this wave's memory operations after any row's copy is known.
+    // Copy instruction j fills LDS positions [256 j, 256 j + 256); the last
+    // one is moved back to end at the row's last position (positions it
+    // shares with the one before receive the same chunk twice).  A lane's
+    // source offsets do not depend on the row and are computed once.
+    uint32_t src_off[kMfMaxChunks];
+    int pos_base[kMfMaxChunks];
+#pragma unroll
+    for (int j = 0; j < kMfMaxChunks; ++j) {
+        pos_base[j] = (j == a.nd - 1 && a.nd > 1) ? a.copy_chunks - kThreads : j * kThreads;
+        const int q = min(pos_base[j] + tid, a.copy_chunks - 1);
+        src_off[j] = 16u * (uint32_t)min(pad_src<PAD>(q), a.nchunks - 1);
+    }
+    // The copies are issued as inline asm: the compiler then neither counts
+    // them nor makes the LDS reads that follow wait for every copy in flight
+    // (it would drain the ring before each row); the hand-placed waits below
+    // order them instead.  M0 holds the wave's LDS destination (lane i writes
+    // 16 bytes at M0 + 16 i); the source is the row base (scalar) plus a
+    // 32-bit byte offset per lane.
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)ring;
+    auto copy_row = [&](int row, int buf) {
+        const uint16_t* src = xw + (size_t)row * a.pitch;
+        const uint32_t dst0 = ring_lds + 2u * (uint32_t)(buf * a.buf_elems) + 1024u * (uint32_t)wave;
 #pragma unroll
         for (int j = 0; j < kMfMaxChunks; ++j) {
-            if (j * kThreads < a.copy_chunks) {
-                const int p = min(tid + j * kThreads, a.copy_chunks - 1);
-                const int ch = min(swz_chunk_at(p, a.swz), a.nchunks - 1);
-                stg[j] = src[ch];
+            if (j < a.nd) {
+                const uint32_t dst = __builtin_amdgcn_readfirstlane(dst0 + 16u * (uint32_t)pos_base[j]);
+                asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+                             :: "v"(src_off[j]), "s"(dst), "s"(src) : "memory");
             }
         }
     };
-    auto store_row = [&](int buf) {
-        uint4* dst = reinterpret_cast<uint4*>(rowbuf + buf * a.buf_elems);
-#pragma unroll
-        for (int j = 0; j < kMfMaxChunks; ++j) {
-            const int p = tid + j * kThreads;
-            if (p < a.copy_chunks)
-                dst[p] = swz_chunk_at(p, a.swz) < a.nchunks ? stg[j] : make_uint4(0u, 0u, 0u, 0u);
-        }
-    };
 
-    int row = blockIdx.x;
-    if (row >= a.rows) return;
-    // zero the row buffers once: chunks past copy_chunks are read only by
-    // pixels past the end of the row, and must hold finite values
-    for (int i = tid * 8; i < 2 * a.buf_elems; i += kThreads * 8)
-        *reinterpret_cast<uint4*>(rowbuf + i) = make_uint4(0u, 0u, 0u, 0u);
-    if (tid < 64) bias_l[tid] = (bias && tid < a.K) ? to_f32(bias[tid]) : 0.f;
-    __syncthreads();
-    load_row(row);
-    store_row(0);
-    __syncthreads();
+    const int first = blockIdx.x;
+    if (first >= a.rows) return;
+    const int my_rows = (a.rows - 1 - first) / (int)gridDim.x + 1;   // rows r_i = first + i * grid
+    for (int i = 0; i < a.nbuf - 1 && i < my_rows; ++i) copy_row(first + i * gridDim.x, i);
+    wg_barrier_lds();                // bias_l visible
+    const float bias_k = bias_l[kh * 32 + ml];
+
+    // output stores: thread's first (k, column vector) and its step per 256
+    // vectors, fixed for the kernel
+    constexpr int V = 16 / sizeof(TOut);
+    const int E = a.vec_store ? V : 1;          // elements per store
+    const int nq = a.Q / E;                     // stores per output row
+    const int sk0 = tid / nq, sv0 = tid - sk0 * nq;
+    const int dk = kThreads / nq, dv = kThreads - dk * nq;
 
     const int PQ = a.P * a.Q;
-    for (int it = 0; row < a.rows; ++it, row += gridDim.x) {
-        const int buf = it & 1;
-        const int next = row + gridDim.x;
-        if (next < a.rows) load_row(next);
+    for (int it = 0; it < my_rows; ++it) {
+        const int row = first + it * gridDim.x;
+        const int buf = it % a.nbuf;
+        if (it + a.nbuf - 1 < my_rows)
+            copy_row(first + (it + a.nbuf - 1) * gridDim.x, (it + a.nbuf - 1) % a.nbuf);
+        // wait for this row's copy: allow the copies of the rows after it
+        // and the output stores issued since it to stay in flight
+        const int later_rows = min(a.nbuf - 1, my_rows - 1 - it);
+        wait_vm_lgkm(a.nd * later_rows + a.ns * min(it, a.nbuf - 1));
+        wg_barrier();                // every wave's part of the row has landed
 
-        const uint16_t* lb = rowbuf + buf * a.buf_elems;
-        float* ot = otile;
-        // blocks pb0 + 2 j; block j uses the fragments of set j % NSET
+        const uint16_t* lb = ring + buf * a.buf_elems;
+        // blocks pb0 + 2 j; block j uses the filter fragments of set j % NSET
         for (int base = 0; pb0 + 2 * base < npb; base += NSET)
 #pragma unroll
         for (int j = 0; j < NSET; ++j) {
@@ -319,108 +408,149 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
             // their phase instead, so reads stay inside the row buffer
             const int wlast = a.Q - 1 >= ph ? a.Q - 1 - (a.Q - 1 - ph) % a.nph : ph;
             const int wread = min(wpix, wlast);
-            // first element of the run this lane reads: window start minus
-            // delta (a multiple of 8), then 16 per step
-            const int chunk0 = (wread * a.D - delta) / 8 + g;
-            // steps [1, s_full) hold only window entries; with MASK the
-            // first step (when delta > 0) and the steps from s_full on are
-            // masked (without MASK the plan guarantees there are none)
+            // LDS chunk position of the lane's step-0 read: the window start
+            // minus delta (a multiple of 8 elements), plus 8 elements for g
+            const int run = PAD == 1 ? (wread * a.D - delta) / 8 + g
+                                     : wread * (a.G + a.G / PAD) + g;
+            const char* rp = reinterpret_cast<const char*>(lb + 8 * run);
             const int s_full = (delta + a.T) / 16;
             f32x16 acc;
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-            // B fragments double-buffered in registers: the read of step
-            // s + 1 is in flight while step s multiplies
-            uint4 bn = *reinterpret_cast<const uint4*>(lb + 8 * swz_pos(chunk0, a.swz));
+            // window fragments kPf steps ahead of the multiply that uses them
+            uint4 bq[kPf];
+#pragma unroll
+            for (int s2 = 0; s2 < kPf && s2 < STEPS; ++s2)
+                bq[s2] = *reinterpret_cast<const uint4*>(rp + step_off<PAD>(s2));
+            // Edge masks.  Step 0 holds the window start (entries below
+            // delta are masked); step s_full holds its end (entries from
+            // delta + T on are masked); later steps lie wholly past the end
+            // and are zeroed; the steps between need no mask.  The two
+            // masks are rebuilt every row from opaque copies of delta and
+            // s_full rather than kept live across the row loop.
+            uint4 mk_first = make_uint4(~0u, ~0u, ~0u, ~0u), mk_tail = mk_first;
+            int sf = s_full;
+            if (MASK) {
+                int dl = delta;
+                asm volatile("" : "+v"(dl));
+                asm volatile("" : "+s"(sf));
+                mk_first = elem_mask(8 * g, dl, dl + a.T);
+                mk_tail = elem_mask(16 * sf + 8 * g, dl, dl + a.T);
+            }
 #pragma unroll
             for (int s2 = 0; s2 < STEPS; ++s2) {
-                uint4 b = bn;
-                if (s2 + 1 < STEPS)
-                    bn = *reinterpret_cast<const uint4*>(
-                        lb + 8 * swz_pos(chunk0 + 2 * (s2 + 1), a.swz));
-                if (MASK && ((s2 == 0 && delta > 0) || s2 >= s_full)) {
-                    const uint4 mk = elem_mask(16 * s2 + 8 * g, delta, delta + a.T);
-                    b.x &= mk.x; b.y &= mk.y; b.z &= mk.z; b.w &= mk.w;
+                uint4 b = bq[s2 % kPf];
+                if (s2 + kPf < STEPS)
+                    bq[s2 % kPf] = *reinterpret_cast<const uint4*>(rp + step_off<PAD>(s2 + kPf));
+                if (MASK) {
+                    if (s2 == 0) {
+                        b.x &= mk_first.x; b.y &= mk_first.y; b.z &= mk_first.z; b.w &= mk_first.w;
+                    }
+                    // branch-free: keep all before s_full, the tail mask at it
+                    const uint32_t keep = s2 < sf ? ~0u : 0u;
+                    const uint32_t at = s2 == sf ? ~0u : 0u;
+                    b.x &= keep | (at & mk_tail.x); b.y &= keep | (at & mk_tail.y);
+                    b.z &= keep | (at & mk_tail.z); b.w &= keep | (at & mk_tail.w);
                 }
-                acc = mfma32<TIn>(A[j][s2], b, acc);
+                acc = mfma32<TIn>(b, F[j][s2], acc);
             }
-            // lane holds D[m][n] for n = lane % 32, m = 8 (i / 4) + 4 (lane / 32) + i % 4
-            if (wpix < a.Q) {
+            // keep the reads kPf multiplies ahead: the first reads, then one
+            // multiply and one read per step
+            __builtin_amdgcn_sched_group_barrier(0x100, kPf < STEPS ? kPf : STEPS, 0);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int k = kh * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-                    if (k < a.K) ot[k * a.ostride + wpix] = acc[i];
+            for (int s2 = 0; s2 < STEPS; ++s2) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (s2 + kPf < STEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            // lane holds D[m][n] for channel n = lane % 32 and block pixel
+            // m = 8 (i / 4) + 4 (lane / 32) + i % 4; pixels past the row end
+            // land in tile columns that are never stored
+            const int k = kh * 32 + ml;
+            if (k < a.K) {
+                TOut* orow = otile + k * a.ostride + a.nph * 32 * mb + ph;
+                if (a.nph == 1) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        put4<TOut>(orow + 8 * q + 4 * g, acc[4 * q] + bias_k, acc[4 * q + 1] + bias_k,
+                                   acc[4 * q + 2] + bias_k, acc[4 * q + 3] + bias_k);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        orow[a.nph * (8 * (i >> 2) + 4 * g + (i & 3))] = from_f32<TOut>(acc[i] + bias_k);
                 }
             }
         }
-        if (next < a.rows) store_row(buf ^ 1);
-        __syncthreads();
+        wait_vm_lgkm_lds_only();
+        wg_barrier();                // tile complete; this row's buffer is free
 
-        // ---- output row (n, h): K rows of Q contiguous elements
+        // ---- output row (n, h): K rows of Q contiguous elements.  Exactly
+        // a.ns stores per thread (surplus threads repeat the last one).
         const uint32_t n = fdiv(row, a.fdP);
         const int h = row - n * a.P;
         TOut* yrow = y + (size_t)n * a.K * PQ + (size_t)h * a.Q;
-        if (a.vec_store) {
-            constexpr int V = 16 / sizeof(TOut);   // outputs per 16-byte store
-            const int vq = a.Q / V;
-            for (int i = tid; i < a.K * vq; i += kThreads) {
-                const int k = i / vq;
-                const int v = i - k * vq;
-                const float b = bias_l[k];
-                const float* src = ot + k * a.ostride + v * V;
-                union {
-                    uint4 u;
-                    TOut e[V];
-                } pk;
-#pragma unroll
-                for (int e = 0; e < V; ++e) pk.e[e] = from_f32<TOut>(src[e] + b);
-                *reinterpret_cast<uint4*>(yrow + (size_t)k * PQ + v * V) = pk.u;
-            }
-        } else {
-            for (int i = tid; i < a.K * a.Q; i += kThreads) {
-                const int k = i / a.Q;
-                const int wq = i - k * a.Q;
-                yrow[(size_t)k * PQ + wq] = from_f32<TOut>(ot[k * a.ostride + wq] + bias_l[k]);
+        int k = sk0, v = sv0;
+        for (int j = 0; j < a.ns; ++j) {
+            const int kk = min(k, a.K - 1);
+            const int off = kk < k ? (a.Q - E) : v * E;
+            if (a.vec_store)
+                *reinterpret_cast<uint4*>(yrow + (size_t)kk * PQ + off) =
+                    *reinterpret_cast<const uint4*>(otile + kk * a.ostride + off);
+            else
+                yrow[(size_t)kk * PQ + off] = otile[kk * a.ostride + off];
+            k += dk;
+            v += dv;
+            if (v >= nq) {
+                v -= nq;
+                ++k;
             }
         }
-        __syncthreads();   // the output tile is rewritten by the next row
+        // the tile is rewritten by the next row only after its row-ready
+        // barrier, which every thread reaches after finishing these reads
     }
 }
 
-// Filter layout for the row kernel: aperm[ph][k][t'] = F[k][c][r][q] at
-// window-order index t = t' - delta(ph) = (q*R + r)*C + c when 0 <= t < T
-// and k < K, else 0; 64 output channels and Tp = 16*steps entries per phase.
+// Filter layout for the row kernel, in the order the A fragments are
+// loaded: aperm[ph][kh][s][lane][e] holds filter entry (k, t') with
+// k = 32 kh + lane % 32 and t' = 16 s + 8 (lane / 32) + e, so one wave's
+// load of a whole step is 1 KB of consecutive bytes.  Entry (k, t') is
+// F[k][c][r][q] at window-order index t = t' - delta(ph) = (q*R + r)*C + c
+// when 0 <= t < T and k < K, else 0 (phase shift and zero padding).
 struct PermArgs {
-    int C, K, R, S, D, T, nph, Tp;
-    FastDiv fdTp, fdC, fdR;
-    uint32_t total;
+    int C, K, R, S, D, T, steps;
+    FastDiv fdSteps, fdC, fdR;
+    uint32_t total;                // nph * 2 * steps * 512
 };
 
 __global__ __launch_bounds__(kThreads) void mfma_filter_perm_kernel(
     const uint16_t* __restrict__ w, uint16_t* __restrict__ aperm, PermArgs p) {
     const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
     if (i >= p.total) return;
-    const uint32_t pk = fdiv(i, p.fdTp);
-    const int tp = i - pk * p.Tp;
-    const int k = pk & 63;
-    const int ph = pk >> 6;
-    const int t = tp - ((ph * p.D) & 7);
-    uint16_t e = 0;
+    const int e = i & 7;
+    const int lane = (i >> 3) & 63;
+    const uint32_t rest = i >> 9;                 // (ph * 2 + kh) * steps + s
+    const uint32_t phk = fdiv(rest, p.fdSteps);
+    const int s = rest - phk * p.steps;
+    const int kh = phk & 1;
+    const int ph = phk >> 1;
+    const int k = kh * 32 + (lane & 31);
+    const int t = 16 * s + 8 * (lane >> 5) + e - ((ph * p.D) & 7);
+    uint16_t v = 0;
     if (k < p.K && t >= 0 && t < p.T) {
         const uint32_t qr = fdiv(t, p.fdC);
         const int c = t - qr * p.C;
         const uint32_t q = fdiv(qr, p.fdR);
         const int r = qr - q * p.R;
-        e = w[(((size_t)k * p.C + c) * p.R + r) * p.S + q];
+        v = w[(((size_t)k * p.C + c) * p.R + r) * p.S + q];
     }
-    aperm[i] = e;
+    aperm[i] = v;
 }
 
 struct MfRowPlan {
     MfRowArgs a;
-    int nset, steps;
+    int nset, steps, pad;
     bool mask;
     size_t lds_bytes;
+    int wgs_per_cu;
 };
 
 int gcd_int(int x, int y) {
@@ -457,67 +587,76 @@ bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl) {
     const int mcount = (g.Q + nph - 1) / nph;
     const int mblocks = (mcount + 31) / 32;
     const int nchunks = g.pitchB / 8;
-    // bank conflicts of the fragment reads: the 32 lanes of a half-wave read
-    // chunks D*nph/8 apart; count 16-lane groups that miss one of 16 bank
-    // groups (64 banks) and 8-lane groups that miss one of 8 (32 banks),
-    // without and with the swizzle, and keep the better layout
-    const int sp = D * nph / 8;
-    auto conflicts = [&](int on) {
-        int bad = 0;
-        for (int base = 0; base < 64; ++base) {
-            int pos[32];
-            for (int m = 0; m < 32; ++m) {
-                const int ch = base + m * sp;
-                pos[m] = on ? (ch ^ ((ch >> 3) & 15)) : ch;
-            }
-            for (int ph = 0; ph < 32; ph += 16) {
-                int seen = 0;
-                for (int m = ph; m < ph + 16; ++m) seen |= 1 << (pos[m] & 15);
-                bad += seen != 0xffff;
-            }
-            for (int ph = 0; ph < 32; ph += 8) {
-                int seen = 0;
-                for (int m = ph; m < ph + 8; ++m) seen |= 1 << (pos[m] & 7);
-                bad += seen != 0xff;
-            }
-        }
-        return bad;
-    };
-    const int swz = conflicts(1) < conflicts(0) ? 1 : 0;
-    const int copy_chunks = swz ? (nchunks + 15) / 16 * 16 : nchunks;
+    // row layout: with nph > 1 the lanes of a fragment start an odd number
+    // of chunks apart (D * nph / 8 = D / gcd(D, 8)); with nph = 1 they start
+    // G = D / 8 chunks apart and a pad chunk after every PAD chunks (PAD the
+    // power-of-two part of G, at most 8) makes the stride G + G / PAD odd
+    const int G = nph == 1 ? D / 8 : 0;
+    int pad = 1;
+    if (nph == 1)
+        while (pad < 8 && G % (2 * pad) == 0) pad *= 2;
+    const int stride = pad == 1 ? D * nph / 8 : G + G / pad;   // chunks between lane starts
+    const int copy_chunks = pad == 1 ? nchunks : (nchunks + pad - 1) / pad * (pad + 1);
     if (copy_chunks > kMfMaxChunks * kThreads) return false;
-    // the furthest chunk any fragment read touches (the last pixel's window
-    // over the whole padded reduction), rounded to 256 bytes
-    const int wmax = std::max(g.Q - 1, nph - 1);   // furthest pixel whose window is read
-    const int last_chunk = (wmax * D) / 8 + 2 * steps + 1;
-    int buf_chunks = std::max(copy_chunks, last_chunk + 1);
+    const int nd = (copy_chunks + kThreads - 1) / kThreads;
+    // the furthest LDS chunk a fragment read touches: the last pixel's run
+    // over the whole padded reduction (a run starts at the pixel's stride
+    // position; g adds one chunk; each step two, plus the pads passed)
+    const int wmax = std::max(g.Q - 1, nph - 1);
+    const int run_end = 1 + 2 * (steps - 1) + (pad == 1 ? 0 : (2 * (steps - 1)) / pad);
+    const int last_chunk = (pad == 1 ? (wmax * D) / 8 : wmax * stride) + run_end;
+    // one copy instruction covers 256 positions, so a row shorter than that
+    // still takes 256
+    int buf_chunks = std::max(std::max(copy_chunks, last_chunk + 1), nd == 1 ? kThreads : 0);
     buf_chunks = (buf_chunks + 15) / 16 * 16;
     const int buf = buf_chunks * 8;
-    const int ostride = (g.Q + 3) / 4 * 4;
-    const size_t lds = (size_t)2 * buf * 2 + (size_t)g.K * ostride * 4 + 64 * 4;
-    const int crs = g.C * g.R * g.S;
-    if (lds > 65536) return false;
-    (void)crs;
+    // output tile: every pixel of every block has a column (pixels past the
+    // row end are written but never stored); an odd number of 16-byte units
+    // per row spreads the channel rows of a tile write over the banks
+    const int V = 16 / out_bytes;
+    int ostride = (nph * 32 * mblocks + V - 1) / V * V;
+    if (((ostride * out_bytes) / 16) % 2 == 0) ostride += V;
+    const size_t tile = (size_t)g.K * ostride * out_bytes + 64 * 4;
+    // workgroups per CU, then ring depth, within the 160 KB of LDS of a CU:
+    // two workgroups (two waves per SIMD, one multiplying while the other
+    // waits at a barrier or stores) beat one with a deeper ring
+    int nbuf = 0, wgs = 0;
+    for (int w = 2; w >= 1 && nbuf == 0; --w)
+        for (int nb = 6; nb >= 2; --nb)
+            if (((size_t)nb * buf * 2 + tile) * w <= 160 * 1024) {
+                nbuf = nb;
+                wgs = w;
+                break;
+            }
+    if (nbuf == 0) return false;
+    const int vec_store = (g.Q % V == 0 && ((int64_t)g.P * g.Q) % V == 0) ? 1 : 0;
+    const int64_t total = vec_store ? (int64_t)g.K * (g.Q / V) : (int64_t)g.K * g.Q;
+    const int ns = (int)((total + kThreads - 1) / kThreads);
+    // the wait counts must fit the 6-bit vector-memory counter: a shorter
+    // ring when the copies and stores of nbuf - 1 rows would not
+    while (nbuf > 2 && (nd + ns) * (nbuf - 1) > 63) --nbuf;
+    if ((nd + ns) * (nbuf - 1) > 63) return false;
+    const size_t lds = (size_t)nbuf * buf * 2 + tile;
     a.C = g.C; a.K = g.K; a.R = g.R; a.S = g.S; a.P = g.P; a.Q = g.Q;
     a.pitch = g.pitchB;
     a.D = D; a.T = T;
     a.nph = nph; a.mblocks = mblocks;
-    a.steps = steps;
+    a.G = G;
     a.nchunks = nchunks;
     a.copy_chunks = copy_chunks;
-    a.swz = swz;
     a.buf_elems = buf;
+    a.nbuf = nbuf;
+    a.nd = nd;
     a.ostride = ostride;
-    const int V = 16 / out_bytes;
-    a.vec_store = (g.Q % V == 0 && ((int64_t)g.P * g.Q) % V == 0) ? 1 : 0;
+    a.vec_store = vec_store;
+    a.ns = ns;
     a.fdP = make_fastdiv(g.P);
-    a.fdCp = make_fastdiv(g.C);
-    a.fdR = make_fastdiv(g.R);
-    a.fdRS = make_fastdiv(g.R * g.S);
     pl.nset = nset;
     pl.steps = steps;
+    pl.pad = pad;
     pl.mask = mask;
     pl.lds_bytes = lds;
+    pl.wgs_per_cu = wgs;
     return true;
 }
 
@@ -533,30 +672,47 @@ hipError_t launch_rows(const Geom& g, MfRowPlan pl, const void* xw, const void* 
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 1)
         cus = 256;
-    int64_t grid = (int64_t)cus * 2;   // two resident workgroups per CU
+    int64_t grid = (int64_t)cus * pl.wgs_per_cu;   // resident workgroups only
     if (grid > rows) grid = rows;
-#define CIW_MF_LAUNCH(NS, M, MK)                                                               \
-    hipLaunchKernelGGL((conv_mfma_rows_kernel<TIn, TOut, NS, M, MK>), dim3((uint32_t)grid),     \
-                       dim3(kThreads), pl.lds_bytes, st, (const uint16_t*)xw, (const uint16_t*)aperm, \
-                       (const TIn*)bias, (TOut*)y, a)
-    if (pl.nset == 1 && !pl.mask) {
-        if (pl.steps == 10) CIW_MF_LAUNCH(1, 10, false);
-        else if (pl.steps == 16) CIW_MF_LAUNCH(1, 16, false);
-        else if (pl.steps == 24) CIW_MF_LAUNCH(1, 24, false);
-        else if (pl.steps == 36) CIW_MF_LAUNCH(1, 36, false);
-        else CIW_MF_LAUNCH(1, 40, false);
-    } else if (pl.nset == 1) {
-        if (pl.steps == 10) CIW_MF_LAUNCH(1, 10, true);
-        else if (pl.steps == 16) CIW_MF_LAUNCH(1, 16, true);
-        else if (pl.steps == 24) CIW_MF_LAUNCH(1, 24, true);
-        else if (pl.steps == 36) CIW_MF_LAUNCH(1, 36, true);
-        else CIW_MF_LAUNCH(1, 40, true);
-    } else if (pl.nset == 2) {
-        if (pl.steps == 10) CIW_MF_LAUNCH(2, 10, true);
-        else CIW_MF_LAUNCH(2, 16, true);
+    // more than 64 KB of dynamic LDS per workgroup must be allowed explicitly
+#define CIW_MF_LAUNCH(NS, M, MK, PD)                                                           \
+    do {                                                                                       \
+        auto kfn = conv_mfma_rows_kernel<TIn, TOut, NS, M, MK, PD>;                            \
+        if (pl.lds_bytes > 65536 &&                                                            \
+            hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                            \
+                                hipFuncAttributeMaxDynamicSharedMemorySize,                    \
+                                (int)pl.lds_bytes) != hipSuccess)                              \
+            return hipErrorInvalidValue;                                                       \
+        hipLaunchKernelGGL(kfn, dim3((uint32_t)grid), dim3(kThreads), pl.lds_bytes, st,        \
+                           (const uint16_t*)xw, (const uint16_t*)aperm, (const TIn*)bias,      \
+                           (TOut*)y, a);                                                       \
+    } while (0)
+#define CIW_MF_STEPS(MK, PD)                                                                   \
+    do {                                                                                       \
+        if (pl.steps == 10) CIW_MF_LAUNCH(1, 10, MK, PD);                                      \
+        else if (pl.steps == 16) CIW_MF_LAUNCH(1, 16, MK, PD);                                 \
+        else if (pl.steps == 24) CIW_MF_LAUNCH(1, 24, MK, PD);                                 \
+        else if (pl.steps == 36) CIW_MF_LAUNCH(1, 36, MK, PD);                                 \
+        else CIW_MF_LAUNCH(1, 40, MK, PD);                                                     \
+    } while (0)
+#define CIW_MF_PAD(MK)                                                                         \
+    do {                                                                                       \
+        if (pl.pad == 1) CIW_MF_STEPS(MK, 1);                                                  \
+        else if (pl.pad == 2) CIW_MF_STEPS(MK, 2);                                             \
+        else if (pl.pad == 4) CIW_MF_STEPS(MK, 4);                                             \
+        else CIW_MF_STEPS(MK, 8);                                                              \
+    } while (0)
+    if (pl.nset == 1) {
+        if (pl.mask) CIW_MF_PAD(true);
+        else CIW_MF_PAD(false);
+    } else if (pl.nset == 2) {    // several phases: nph > 1, no pad chunks
+        if (pl.steps == 10) CIW_MF_LAUNCH(2, 10, true, 1);
+        else CIW_MF_LAUNCH(2, 16, true, 1);
     } else {
-        CIW_MF_LAUNCH(4, 10, true);
+        CIW_MF_LAUNCH(4, 10, true, 1);
     }
+#undef CIW_MF_PAD
+#undef CIW_MF_STEPS
 #undef CIW_MF_LAUNCH
     return hipGetLastError();
 }
@@ -599,11 +755,11 @@ hipError_t launch_mfma_prep(const Geom& g, ciw_dtype out, const void* w, void* a
     if (!mf_row_plan(g, elem_bytes(out), pl)) return hipSuccess;   // generic kernel: no prep
     PermArgs p;
     p.C = g.C; p.K = g.K; p.R = g.R; p.S = g.S;
-    p.D = pl.a.D; p.T = pl.a.T; p.nph = pl.a.nph; p.Tp = pl.steps * 16;
-    p.fdTp = make_fastdiv(p.Tp);
+    p.D = pl.a.D; p.T = pl.a.T; p.steps = pl.steps;
+    p.fdSteps = make_fastdiv(pl.steps);
     p.fdC = make_fastdiv(g.C);
     p.fdR = make_fastdiv(g.R);
-    p.total = (uint32_t)(p.nph * 64 * p.Tp);
+    p.total = (uint32_t)(pl.a.nph * 2 * pl.steps * 512);
     hipLaunchKernelGGL(mfma_filter_perm_kernel, dim3((p.total + kThreads - 1) / kThreads),
                        dim3(kThreads), 0, st, (const uint16_t*)w, (uint16_t*)aperm, p);
     return hipGetLastError();

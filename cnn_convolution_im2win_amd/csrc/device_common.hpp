@@ -43,6 +43,20 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
     return r;
 }
 
+// The 16-bit pattern of from_f32<T>(v), for the 16-bit element types.
+template <typename T>
+__device__ __forceinline__ uint16_t f32_bits(float v);
+
+template <>
+__device__ __forceinline__ uint16_t f32_bits<half_t>(float v) {
+    return __builtin_bit_cast(uint16_t, from_f32<half_t>(v));
+}
+
+template <>
+__device__ __forceinline__ uint16_t f32_bits<bf16_t>(float v) {
+    return from_f32<bf16_t>(v).bits;
+}
+
 template <typename T>
 __device__ __forceinline__ T zero_elem() {
     return from_f32<T>(0.0f);
