@@ -81,7 +81,8 @@ class Step:
         self.ws_bytes = ciw.conv2d_workspace_bytes(self.desc, self.in_code, L.N)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
         self.win_bytes = ciw.conv_im2win_window_bytes(self.desc, self.in_code, self.layout, L.N)
-        self.stream = torch.cuda.current_stream()
+        # one side stream for everything the step launches
+        self.stream = torch.cuda.Stream()
         self.sp = self.stream.cuda_stream
         self.fn = self.lib.conv2d_dw_fwd if self.depthwise else self.lib.conv2d_fwd
         self.dref = ctypes.byref(self.desc)
@@ -178,6 +179,11 @@ def stored_traffic(workload: str):
 
 
 def time_steps(step: Step, steps: int, warmup: int):
+    """K timed steps, each the two C-ABI calls on the step's stream,
+    bracketed by a device synchronisation on both sides; HIP events on that
+    stream time the two calls.  (Replaying the calls as HIP graphs was
+    measured slower here than launching them directly, so the step launches
+    them directly.)"""
     import torch
     for _ in range(warmup):
         step.transform()

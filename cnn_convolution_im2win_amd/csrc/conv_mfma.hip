@@ -11,6 +11,8 @@
 // width", §III-C).  Products are exact in fp32 and accumulate in fp32
 // (§III-F); the bias is added in fp32 and the result rounded once.
 #include <algorithm>
+#include <map>
+#include <mutex>
 
 #include "internal.hpp"
 #include "device_common.hpp"
@@ -660,6 +662,19 @@ bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl) {
     return true;
 }
 
+// Raise a kernel's dynamic-LDS limit on this device once: the attribute
+// persists, so later launches (graph captures included) skip the call.
+hipError_t allow_lds(const void* fn, int dev, size_t bytes) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, size_t> done;
+    std::lock_guard<std::mutex> lock(mu);
+    size_t& have = done[{dev, fn}];
+    if (have >= bytes) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) have = bytes;
+    return e;
+}
+
 template <typename TIn, typename TOut>
 hipError_t launch_rows(const Geom& g, MfRowPlan pl, const void* xw, const void* aperm,
                        const void* bias, void* y, int n_images, hipStream_t st) {
@@ -679,9 +694,7 @@ hipError_t launch_rows(const Geom& g, MfRowPlan pl, const void* xw, const void* 
     do {                                                                                       \
         auto kfn = conv_mfma_rows_kernel<TIn, TOut, NS, M, MK, PD>;                            \
         if (pl.lds_bytes > 65536 &&                                                            \
-            hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                            \
-                                hipFuncAttributeMaxDynamicSharedMemorySize,                    \
-                                (int)pl.lds_bytes) != hipSuccess)                              \
+            allow_lds(reinterpret_cast<const void*>(kfn), dev, pl.lds_bytes) != hipSuccess)    \
             return hipErrorInvalidValue;                                                       \
         hipLaunchKernelGGL(kfn, dim3((uint32_t)grid), dim3(kThreads), pl.lds_bytes, st,        \
                            (const uint16_t*)xw, (const uint16_t*)aperm, (const TIn*)bias,      \

@@ -1,0 +1,80 @@
+"""GPU: the hot path captured in a HIP graph replays to the eager result.
+
+One step (conv_im2win_transform, then conv2d_fwd / conv2d_dw_fwd on the ready
+window tensor) is captured on a side stream and replayed several times.
+Between replays the output and the whole workspace are overwritten by eager
+fills and the device is synchronised, so a replay can only match by redoing
+every write itself; every replay must equal the eager result bit for bit
+(all kernels sum in a fixed order).
+"""
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from tests.gpu_util import to_dev, to_host_bits, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import cnn_convolution_im2win_amd as ciw  # noqa: E402
+from cnn_convolution_im2win_amd import _lib  # noqa: E402
+
+CODE = {"f32": ciw.CIW_F32, "f16": ciw.CIW_F16, "bf16": ciw.CIW_BF16}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("name", workloads.LAYER_ORDER)
+def test_graph_replays_match_eager(name):
+    L = workloads.LAYERS[name]
+    L = L.replace(N=min(L.N, 4))
+    say(f"graph replay {name} N={L.N}")
+    lib = _lib.load()
+    x, w, b = (to_dev(a, L.dtype) for a in workloads.make_inputs(L))
+    desc = ciw.make_desc(L.x_shape, L.w_shape, L.stride, L.pad, L.dil, L.groups)
+    depthwise = L.groups > 1
+    layout = ciw.CIW_WIN_HWC if (L.dtype != "f32" and not depthwise) else ciw.CIW_WIN_CHW
+    P, Q = ciw.conv_im2win_output_dims(desc)
+    y = torch.empty((L.N, L.K, P, Q), dtype=torch_dtype(L.out_dtype), device="cuda")
+    ws_bytes = ciw.conv2d_workspace_bytes(desc, CODE[L.dtype], L.N)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    fn = lib.conv2d_dw_fwd if depthwise else lib.conv2d_fwd
+    s = torch.cuda.Stream()
+
+    def step():
+        st = lib.conv_im2win_transform(ctypes.byref(desc), CODE[L.dtype], layout, x.data_ptr(),
+                                       ws.data_ptr(), s.cuda_stream)
+        assert st == 0
+        st = fn(ctypes.byref(desc), CODE[L.dtype], CODE[L.out_dtype], None, w.data_ptr(),
+                None if b is None else b.data_ptr(), y.data_ptr(), ws.data_ptr(), ws_bytes,
+                ciw.CIW_FLAG_WINDOW_READY, s.cuda_stream)
+        assert st == 0
+
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    ref = to_host_bits(y).copy()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s, capture_error_mode="relaxed"):
+        step()
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        with torch.cuda.stream(s):
+            y.view(torch.uint8).fill_(0xA5)
+            ws.fill_((37 * rep + 11) & 0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = to_host_bits(y)
+        assert np.array_equal(got, ref), f"{name}: replay {rep} differs from the eager result"
