@@ -20,7 +20,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libconv_im2win.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "transform.hip", "conv_fp32.hip", "conv_mfma.hip", "conv_dw.hip"]
+SOURCES = ["api.cpp", "transform.hip", "conv_fp32.hip", "conv_mfma.hip", "conv_mfma_f16.hip",
+           "conv_mfma_bf16.hip", "conv_dw.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [

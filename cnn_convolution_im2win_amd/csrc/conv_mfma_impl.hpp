@@ -1,0 +1,857 @@
+// conv_mfma_impl.hpp -- fp16/bf16 windowed contraction on the gfx950 matrix
+// cores: kernels, row-kernel plan and launchers (templates).  Included by
+// conv_mfma.hip (entry points, filter prep) and by one file per input type,
+// which instantiate the kernels, so the two compile in parallel.
+//
+// The im2win paper ("Enabling Memory-efficient Im2win Convolution with
+// Multi-precision Support ...", §III-D) maps the output to a matrix product
+// with M = output channels and N = images x output rows x output columns,
+// reducing over the window.  With the HWC window layout the window of output
+// (n, h, w) is, for each filter column q, the R*C contiguous elements at
+// column w*stride_w + q*dil_w of row (n, h); with dil_w = 1 the whole window
+// (S*R*C elements) is one contiguous run.  The reduction index is
+// t = (q*R + r)*C + c and the filter operand is F[k][c][r][q] ("height before
+// width", §III-C).  Products are exact in fp32 and accumulate in fp32
+// (§III-F); the bias is added in fp32 and the result rounded once.
+#pragma once
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+
+#include "internal.hpp"
+#include "device_common.hpp"
+
+namespace ciw {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kMB = 64;       // output channels per workgroup
+constexpr int kNB = 64;       // pixels per workgroup
+constexpr int kKB = 32;       // reduction step (one 16x16x32 MFMA)
+constexpr int kLdsRow = 40;   // 32 + 8 halves: rows 80 B apart
+
+struct MfmaArgs {
+    int C, K, R, S, P, Q, sw, dw, pitch;
+    int T, RC, npix;
+    FastDiv fdRC, fdC, fdPQ, fdQ;
+};
+
+template <typename TIn>
+__device__ __forceinline__ f32x4 mfma16x16x32(const uint16_t* a, const uint16_t* b, f32x4 acc);
+
+template <>
+__device__ __forceinline__ f32x4 mfma16x16x32<half_t>(const uint16_t* a, const uint16_t* b,
+                                                      f32x4 acc) {
+    f16x8 va = *reinterpret_cast<const f16x8*>(a);
+    f16x8 vb = *reinterpret_cast<const f16x8*>(b);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(va, vb, acc, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x4 mfma16x16x32<bf16_t>(const uint16_t* a, const uint16_t* b,
+                                                      f32x4 acc) {
+    bf16x8 va = *reinterpret_cast<const bf16x8*>(a);
+    bf16x8 vb = *reinterpret_cast<const bf16x8*>(b);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, vb, acc, 0, 0, 0);
+}
+
+// Generic tile kernel: 64 output channels x 64 pixels per workgroup, four
+// waves each owning a 32x32 quadrant (2x2 MFMA tiles).  Operands go through
+// LDS one 32-wide reduction step at a time.
+template <typename TIn, typename TOut>
+__global__ __launch_bounds__(kThreads) void conv_mfma_generic_kernel(
+    const uint16_t* __restrict__ xw, const uint16_t* __restrict__ w,
+    const TIn* __restrict__ bias, TOut* __restrict__ y, MfmaArgs a) {
+    __shared__ __align__(16) uint16_t As[kMB * kLdsRow];
+    __shared__ __align__(16) uint16_t Bs[kNB * kLdsRow];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int k0 = blockIdx.y * kMB;
+    const int p0 = blockIdx.x * kNB;
+
+    // loader role: row (filter or pixel) and 8-element slot of the step
+    const int lrow = tid >> 2;
+    const int lslot = (tid & 3) * 8;
+    const int kload = k0 + lrow;
+    const int pload = p0 + lrow;
+    // per-thread window base of its pixel (index precomputation)
+    int64_t bbase = -1;
+    if (pload < a.npix) {
+        uint32_t n = fdiv(pload, a.fdPQ);
+        int pix = pload - n * (a.P * a.Q);
+        int h = fdiv(pix, a.fdQ);
+        int wo = pix - h * a.Q;
+        bbase = ((int64_t)n * a.P + h) * a.pitch + (int64_t)wo * a.sw * a.RC;
+    }
+
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int wm = wave >> 1, wn = wave & 1;
+    for (int t0 = 0; t0 < a.T; t0 += kKB) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int t = t0 + lslot + i;
+            uint16_t av = 0, bv = 0;
+            if (t < a.T) {
+                uint32_t q = fdiv(t, a.fdRC);
+                int rc = t - q * a.RC;
+                uint32_t r = fdiv(rc, a.fdC);
+                int c = rc - r * a.C;
+                if (kload < a.K) av = w[(((int64_t)kload * a.C + c) * a.R + r) * a.S + q];
+                if (bbase >= 0) bv = xw[bbase + (int64_t)q * a.dw * a.RC + rc];
+            }
+            As[lrow * kLdsRow + lslot + i] = av;
+            Bs[lrow * kLdsRow + lslot + i] = bv;
+        }
+        __syncthreads();
+        const int kq = (lane >> 4) * 8;
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                acc[mi][ni] = mfma16x16x32<TIn>(
+                    &As[(wm * 32 + mi * 16 + (lane & 15)) * kLdsRow + kq],
+                    &Bs[(wn * 32 + ni * 16 + (lane & 15)) * kLdsRow + kq], acc[mi][ni]);
+        __syncthreads();
+    }
+
+    // epilogue: lane holds D[4*(lane/16) + i][lane % 16] of each 16x16 tile
+    const int PQ = a.P * a.Q;
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+        int p = p0 + wn * 32 + ni * 16 + (lane & 15);
+        if (p >= a.npix) continue;
+        uint32_t n = fdiv(p, a.fdPQ);
+        int pix = p - n * PQ;
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                int k = k0 + wm * 32 + mi * 16 + (lane >> 4) * 4 + i;
+                if (k >= a.K) continue;
+                float v = acc[mi][ni][i];
+                if (bias) v += to_f32(bias[k]);
+                y[((int64_t)n * a.K + k) * PQ + pix] = from_f32<TOut>(v);
+            }
+    }
+}
+
+// ------------------------------------------------------------ row kernel
+// Persistent kernel for layers whose filter fits in registers (K <= 64,
+// padded reduction <= 640 per phase set).  The GEMM view is the paper's
+// (§III-D), output pixels x output channels reduced over the window.  One
+// workgroup owns whole window rows (n, h):
+//   - each of its four waves keeps the filter fragments of 32 output
+//     channels over the whole padded reduction in registers for the life of
+//     the kernel;
+//   - window rows stream through a ring of LDS buffers, copied from global
+//     memory straight into LDS several rows ahead of the row being
+//     multiplied (load/compute overlap, §III-D/§III-E);
+//   - the window of pixel w is the run of LDS chunks starting at w*D, D =
+//     stride_w*R*C, so consecutive pixels read overlapping runs and each
+//     window element crosses HBM once per output row ("elements loaded in
+//     a previous window remain in cache", §III-C);
+//   - the window fragment is the MFMA's first operand, so a lane ends up
+//     holding 16 pixels of one output channel, four of them adjacent; they
+//     go through an LDS tile so each output row leaves with whole-vector
+//     stores.
+// Alignment: a window fragment is a 16-byte LDS read, so its start must be
+// a multiple of 8 elements.  Pixels are grouped into `nph` phases (w mod
+// nph, nph = 8 / gcd(D, 8)) whose window starts share one misalignment
+// delta; each phase multiplies a copy of the filter shifted right by delta,
+// and reads start delta elements early.  Reduction entries outside the
+// window (the shift, the padding to a multiple of 16) are zero in the filter
+// and masked to zero in the window fragment, so values outside a window
+// never reach a stored output.
+// Bank conflicts: the 32 pixels of a fragment start G = D*nph/8 chunks
+// apart.  With nph > 1, G is odd and consecutive lanes fall in distinct
+// banks.  With nph = 1 the row is stored with one pad chunk after every PAD
+// chunks (PAD the largest power of two dividing G, at most 8), which makes
+// the lane stride G + G/PAD odd; every run starts on the pad grid, so the
+// offset of each reduction step is a compile-time constant.
+struct MfRowArgs {
+    int C, K, R, S, P, Q, pitch;   // pitch: window row pitch (elements)
+    int D, T;                      // window start stride, window length
+    int nph, mblocks;              // pixel phases, 32-pixel blocks per phase
+    int G;                         // chunks between window starts (nph == 1)
+    int nchunks;                   // 16-byte chunks of a window row
+    int copy_chunks;               // LDS chunk positions of a row (pads included)
+    int buf_elems;                 // elements per LDS row buffer
+    int nbuf;                      // row buffers in the LDS ring
+    int nd;                        // row-copy instructions per thread per row
+    int ostride;                   // LDS output tile row stride (elements of TOut)
+    int vec_store;                 // output rows are whole 16-byte vectors
+    int ns;                        // output store instructions per thread per row
+    int rows;                      // N * P
+    FastDiv fdP;
+};
+
+constexpr int kMfMaxChunks = 8;    // 16-byte chunks per thread per row copy
+constexpr int kPf = 4;             // window fragments read ahead of the multiplies
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename TIn>
+__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, f32x16 acc);
+
+template <>
+__device__ __forceinline__ f32x16 mfma32<half_t>(const uint4& a, const uint4& b, f32x16 acc) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x16 mfma32<bf16_t>(const uint4& a, const uint4& b, f32x16 acc) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+// The window chunk whose copy LDS position q holds: one pad position after
+// every PAD chunks, filled with the chunk before it.
+template <int PAD>
+__device__ __forceinline__ int pad_src(int q) {
+    if (PAD == 1) return q;
+    const int grp = q / (PAD + 1);
+    return grp * PAD + min(q - grp * (PAD + 1), PAD - 1);
+}
+
+// Byte offset of reduction step s within a run: 32 bytes a step plus one
+// pad chunk for every PAD chunks passed.
+template <int PAD>
+__device__ constexpr int step_off(int s) {
+    return PAD == 1 ? 32 * s : 32 * s + 16 * ((2 * s) / PAD);
+}
+
+// Mask of the 8 elements [t0, t0 + 8) that lie inside [lo, hi).
+__device__ __forceinline__ uint4 elem_mask(int t0, int lo, int hi) {
+    uint32_t m[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 2 * i;
+        m[i] = ((t >= lo && t < hi) ? 0xffffu : 0u) | ((t + 1 >= lo && t + 1 < hi) ? 0xffff0000u : 0u);
+    }
+    return make_uint4(m[0], m[1], m[2], m[3]);
+}
+
+// Two outputs rounded to a 16-bit type and packed into one word (the
+// hardware's packed round-to-nearest-even conversions).
+template <typename TOut>
+__device__ __forceinline__ uint32_t pack2(float a0, float a1);
+
+template <>
+__device__ __forceinline__ uint32_t pack2<half_t>(float a0, float a1) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a0, a1}, f16x2));
+}
+
+template <>
+__device__ __forceinline__ uint32_t pack2<bf16_t>(float a0, float a1) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a0, a1}, bf16x2));
+}
+
+// Two adjacent outputs as one LDS write.
+template <typename TOut>
+__device__ __forceinline__ void put2(TOut* p, float a0, float a1) {
+    *reinterpret_cast<uint32_t*>(p) = pack2<TOut>(a0, a1);
+}
+
+template <>
+__device__ __forceinline__ void put2<float>(float* p, float a0, float a1) {
+    *reinterpret_cast<float2*>(p) = make_float2(a0, a1);
+}
+
+// Four adjacent outputs as one LDS write (8 bytes of halves, 16 of floats).
+template <typename TOut>
+__device__ __forceinline__ void put4(TOut* p, float a0, float a1, float a2, float a3) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack2<TOut>(a0, a1), pack2<TOut>(a2, a3));
+}
+
+template <>
+__device__ __forceinline__ void put4<float>(float* p, float a0, float a1, float a2, float a3) {
+    *reinterpret_cast<float4*>(p) = make_float4(a0, a1, a2, a3);
+}
+
+// s_waitcnt with a run-time vector-memory count (the instruction takes an
+// immediate): wait until at most n of this wave's vector memory operations
+// are outstanding and all its LDS operations are done.
+__device__ __forceinline__ void wait_vm_lgkm(int n) {
+    asm volatile("" ::: "memory");
+    switch (n < 0 ? 0 : (n > 63 ? 63 : n)) {
+#define CIW_WAIT_CASE(k) \
+    case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | (7 << 4) | (0 << 8)); break;
+#define CIW_WAIT_CASE8(b) CIW_WAIT_CASE(b) CIW_WAIT_CASE(b + 1) CIW_WAIT_CASE(b + 2) CIW_WAIT_CASE(b + 3) \
+    CIW_WAIT_CASE(b + 4) CIW_WAIT_CASE(b + 5) CIW_WAIT_CASE(b + 6) CIW_WAIT_CASE(b + 7)
+        CIW_WAIT_CASE8(0) CIW_WAIT_CASE8(8) CIW_WAIT_CASE8(16) CIW_WAIT_CASE8(24)
+        CIW_WAIT_CASE8(32) CIW_WAIT_CASE8(40) CIW_WAIT_CASE8(48) CIW_WAIT_CASE8(56)
+#undef CIW_WAIT_CASE8
+#undef CIW_WAIT_CASE
+    }
+    asm volatile("" ::: "memory");
+}
+
+// Wait for this wave's LDS operations only.
+__device__ __forceinline__ void wait_vm_lgkm_lds_only() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier without the memory fence __syncthreads adds (the waits
+// above are placed by hand so row copies can stay in flight across it).
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wg_barrier_lds() {
+    wait_vm_lgkm_lds_only();
+    wg_barrier();
+}
+
+template <typename TIn, typename TOut, int NSET, int STEPS, bool MASK, int PAD, bool TAILLAST>
+__global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
+    const uint16_t* __restrict__ xw, const uint16_t* __restrict__ aperm,
+    const TIn* __restrict__ bias, TOut* __restrict__ y, MfRowArgs a) {
+    extern __shared__ __align__(16) uint16_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    const int kh = wave & 1;          // output channels [32 kh, 32 kh + 32)
+    const int pb0 = wave >> 1;        // block groups pb0, pb0 + 2, ... (see below)
+    const int g = lane >> 5;          // which 8 of a fragment's 16 reduction entries
+    const int ml = lane & 31;         // fragment row (pixel) / column (channel)
+    const int npb = a.nph * a.mblocks;
+
+    uint16_t* ring = lds;                                                 // nbuf x buf_elems
+    TOut* otile = reinterpret_cast<TOut*>(lds + a.nbuf * a.buf_elems);   // K x ostride
+    float* bias_l = reinterpret_cast<float*>(otile + a.K * a.ostride);   // 64 floats
+
+    // ---- filter fragments, laid out by the prep kernel in fragment order
+    // (phase-shifted, zero-padded): lane holds F[t = 16 s + 8 (lane / 32)
+    // + 0..7][k = 32 kh + lane % 32], the second MFMA operand
+    uint4 F[NSET][STEPS];
+#pragma unroll
+    for (int j = 0; j < NSET; ++j) {
+        const int pb = min(pb0 * NSET + j, npb - 1);   // set j serves phase pb % nph
+        const uint16_t* fp = aperm + ((size_t)((pb % a.nph) * 2 + kh) * STEPS * 64 + lane) * 8;
+#pragma unroll
+        for (int s2 = 0; s2 < STEPS; ++s2)
+            F[j][s2] = *reinterpret_cast<const uint4*>(fp + 512 * s2);
+    }
+    if (tid < 64) bias_l[tid] = (bias && tid < a.K) ? to_f32(bias[tid]) : 0.f;
+    // complete these loads now: the wait counts below cover only row copies
+    // and output stores
+#pragma unroll
+    for (int j = 0; j < NSET; ++j)
+#pragma unroll
+        for (int s2 = 0; s2 < STEPS; ++s2) asm volatile("" ::"v"(F[j][s2].x));
+    wait_vm_lgkm(0);
+
+    // ---- window rows: global -> LDS directly (no registers), into a ring of
+    // nbuf row buffers, nbuf - 1 rows ahead of the row being multiplied.
+    // Every wave issues exactly a.nd copy instructions per row, so the
+    // number of this wave's memory operations after any row's copy is known.
+    // Copy instruction j fills LDS positions [256 j, 256 j + 256); the last
+    // one is moved back to end at the row's last position (positions it
+    // shares with the one before receive the same chunk twice).  A lane's
+    // source offsets do not depend on the row and are computed once.
+    uint32_t src_off[kMfMaxChunks];
+    int pos_base[kMfMaxChunks];
+#pragma unroll
+    for (int j = 0; j < kMfMaxChunks; ++j) {
+        pos_base[j] = (j == a.nd - 1 && a.nd > 1) ? a.copy_chunks - kThreads : j * kThreads;
+        const int q = min(pos_base[j] + tid, a.copy_chunks - 1);
+        src_off[j] = 16u * (uint32_t)min(pad_src<PAD>(q), a.nchunks - 1);
+    }
+    // The copies are issued as inline asm: the compiler then neither counts
+    // them nor makes the LDS reads that follow wait for every copy in flight
+    // (it would drain the ring before each row); the hand-placed waits below
+    // order them instead.  M0 holds the wave's LDS destination (lane i writes
+    // 16 bytes at M0 + 16 i); the source is the row base (scalar) plus a
+    // 32-bit byte offset per lane.
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)ring;
+    auto copy_row = [&](int row, int buf) {
+        const uint16_t* src = xw + (size_t)row * a.pitch;
+        const uint32_t dst0 = ring_lds + 2u * (uint32_t)(buf * a.buf_elems) + 1024u * (uint32_t)wave;
+#pragma unroll
+        for (int j = 0; j < kMfMaxChunks; ++j) {
+            if (j < a.nd) {
+                const uint32_t dst = __builtin_amdgcn_readfirstlane(dst0 + 16u * (uint32_t)pos_base[j]);
+                asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+                             :: "v"(src_off[j]), "s"(dst), "s"(src) : "memory");
+            }
+        }
+    };
+
+    // each workgroup takes a contiguous run of rows: neighbouring output
+    // rows share cache lines, and one workgroup writing them back to back
+    // completes those lines while they are still in L2
+    const int rows_per = (a.rows + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int first = blockIdx.x * rows_per;
+    if (first >= a.rows) return;
+    const int my_rows = min(rows_per, a.rows - first);   // rows first .. first + my_rows - 1
+    for (int i = 0; i < a.nbuf - 1 && i < my_rows; ++i) copy_row(first + i, i);
+    wg_barrier_lds();                // bias_l visible
+    const float bias_k = bias_l[kh * 32 + ml];
+    // Small filter sets leave registers for two kernel-lifetime helpers: the
+    // bias splat, which seeds the accumulators (the first multiply adds onto
+    // it, no separate add), and each set's edge masks, which depend only on
+    // its phase and so are built once here instead of every row.
+    constexpr bool kLean = NSET * STEPS <= 20;
+    f32x16 bias_vec;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bias_vec[i] = kLean ? bias_k : 0.f;
+    uint4 mkf[NSET], mkt[NSET];
+    int sfj[NSET];
+#pragma unroll
+    for (int j = 0; j < NSET; ++j) {
+        const int dj = (((pb0 * NSET + j) % a.nph) * a.D) & 7;
+        sfj[j] = (dj + a.T) / 16;
+        mkf[j] = make_uint4(~0u, ~0u, ~0u, ~0u);
+        mkt[j] = mkf[j];
+        if (MASK && kLean) {
+            mkf[j] = elem_mask(8 * g, dj, dj + a.T);
+            mkt[j] = elem_mask(16 * (TAILLAST ? STEPS - 1 : sfj[j]) + 8 * g, dj, dj + a.T);
+        }
+    }
+
+    // output stores: thread's first (k, column vector) and its step per 256
+    // vectors, fixed for the kernel
+    constexpr int V = 16 / sizeof(TOut);
+    const int E = a.vec_store ? V : 1;          // elements per store
+    const int nq = a.Q / E;                     // stores per output row
+    const int sk0 = tid / nq, sv0 = tid - sk0 * nq;
+    const int dk = kThreads / nq, dv = kThreads - dk * nq;
+
+    const int PQ = a.P * a.Q;
+    for (int it = 0; it < my_rows; ++it) {
+        const int row = first + it;
+        const int buf = it % a.nbuf;
+        if (it + a.nbuf - 1 < my_rows) copy_row(first + it + a.nbuf - 1, (it + a.nbuf - 1) % a.nbuf);
+        // wait for this row's copy: allow the copies of the rows after it
+        // and the output stores issued since it to stay in flight
+        const int later_rows = min(a.nbuf - 1, my_rows - 1 - it);
+        wait_vm_lgkm(a.nd * later_rows + a.ns * min(it, a.nbuf - 1));
+        wg_barrier();                // every wave's part of the row has landed
+
+        const uint16_t* lb = ring + buf * a.buf_elems;
+        // Pixel blocks pb = phase + nph * (32-pixel block): the wave takes
+        // groups gi = pb0, pb0 + 2, ... of NSET consecutive blocks, block
+        // gi * NSET + j with filter set j.  With NSET > 1 (nph = 2 NSET) a
+        // group is NSET adjacent phases of one 32-pixel block, so blocks
+        // j and j + 1 hold neighbouring pixels and their outputs go to the
+        // tile in pairs.
+        constexpr int kNph = NSET > 1 ? 2 * NSET : 1;   // nph when NSET > 1
+        for (int base = 0; (pb0 + 2 * base) * NSET < npb; ++base) {
+            f32x16 accp;   // block j - 1 of a pair, until block j is done
+#pragma unroll
+            for (int j = 0; j < NSET; ++j) {
+            const int pb = (pb0 + 2 * base) * NSET + j;
+            if (NSET == 1 && pb >= npb) break;
+            const int ph = pb % a.nph;
+            const int mb = pb / a.nph;
+            const int delta = (ph * a.D) & 7;
+            const int wpix = a.nph * (32 * mb + ml) + ph;
+            // pixels past the row end (never stored) read the last pixel of
+            // their phase instead, so reads stay inside the row buffer
+            const int wlast = a.Q - 1 >= ph ? a.Q - 1 - (a.Q - 1 - ph) % a.nph : ph;
+            const int wread = min(wpix, wlast);
+            // LDS chunk position of the lane's step-0 read: the window start
+            // minus delta (a multiple of 8 elements), plus 8 elements for g
+            const int run = PAD == 1 ? (wread * a.D - delta) / 8 + g
+                                     : wread * (a.G + a.G / PAD) + g;
+            const char* rp = reinterpret_cast<const char*>(lb + 8 * run);
+            f32x16 acc = bias_vec;
+            // window fragments kPf steps ahead of the multiply that uses them
+            uint4 bq[kPf];
+#pragma unroll
+            for (int s2 = 0; s2 < kPf && s2 < STEPS; ++s2)
+                bq[s2] = *reinterpret_cast<const uint4*>(rp + step_off<PAD>(s2));
+            // Edge masks.  Step 0 holds the window start (entries below
+            // delta are masked); step s_full holds its end (entries from
+            // delta + T on are masked); later steps lie wholly past the end
+            // and are zeroed; the steps between need no mask.  With TAILLAST
+            // every phase ends in the last step, so only steps 0 and
+            // STEPS - 1 are masked.  Without kLean the masks are rebuilt
+            // every row from opaque copies of delta and s_full rather than
+            // kept live across the row loop.
+            uint4 mk_first = mkf[j], mk_tail = mkt[j];
+            int sf = sfj[j];
+            if (MASK && !kLean) {
+                int dl = delta;
+                sf = (delta + a.T) / 16;
+                asm volatile("" : "+v"(dl));
+                asm volatile("" : "+s"(sf));
+                mk_first = elem_mask(8 * g, dl, dl + a.T);
+                mk_tail = elem_mask(16 * (TAILLAST ? STEPS - 1 : sf) + 8 * g, dl, dl + a.T);
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < STEPS; ++s2) {
+                uint4 b = bq[s2 % kPf];
+                if (s2 + kPf < STEPS)
+                    bq[s2 % kPf] = *reinterpret_cast<const uint4*>(rp + step_off<PAD>(s2 + kPf));
+                if (MASK) {
+                    if (s2 == 0) {
+                        b.x &= mk_first.x; b.y &= mk_first.y; b.z &= mk_first.z; b.w &= mk_first.w;
+                    }
+                    if (TAILLAST) {
+                        if (s2 == STEPS - 1) {
+                            b.x &= mk_tail.x; b.y &= mk_tail.y; b.z &= mk_tail.z; b.w &= mk_tail.w;
+                        }
+                    } else {
+                        // branch-free: keep all before s_full, the tail mask at it
+                        const uint32_t keep = s2 < sf ? ~0u : 0u;
+                        const uint32_t at = s2 == sf ? ~0u : 0u;
+                        b.x &= keep | (at & mk_tail.x); b.y &= keep | (at & mk_tail.y);
+                        b.z &= keep | (at & mk_tail.z); b.w &= keep | (at & mk_tail.w);
+                    }
+                }
+                acc = mfma32<TIn>(b, F[j][s2], acc);
+            }
+            // keep the reads kPf multiplies ahead: the first reads, then one
+            // multiply and one read per step
+            __builtin_amdgcn_sched_group_barrier(0x100, kPf < STEPS ? kPf : STEPS, 0);
+#pragma unroll
+            for (int s2 = 0; s2 < STEPS; ++s2) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (s2 + kPf < STEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            // lane holds D[m][n] for channel n = lane % 32 and block pixel
+            // m = 8 (i / 4) + 4 (lane / 32) + i % 4; pixels past the row end
+            // land in tile columns that are never stored
+            // (with kLean the bias is already in the sum; no "+ 0", which
+            // the compiler must keep for the sign of a zero sum)
+#define CIW_OUT(v) (kLean ? (v) : (v) + bias_k)
+            const int k = kh * 32 + ml;
+            if (NSET == 1) {
+                if (k < a.K) {
+                    TOut* orow = otile + k * a.ostride + a.nph * 32 * mb + ph;
+                    if (a.nph == 1) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            put4<TOut>(orow + 8 * q + 4 * g, CIW_OUT(acc[4 * q]), CIW_OUT(acc[4 * q + 1]),
+                                       CIW_OUT(acc[4 * q + 2]), CIW_OUT(acc[4 * q + 3]));
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            orow[a.nph * (8 * (i >> 2) + 4 * g + (i & 3))] = from_f32<TOut>(CIW_OUT(acc[i]));
+                    }
+                }
+            } else if ((j & 1) == 0) {
+                accp = acc;
+            } else if (k < a.K) {
+                // blocks j - 1 and j: phases ph - 1 and ph, neighbouring pixels
+                TOut* orow = otile + k * a.ostride + kNph * (32 * mb + 4 * g) + ph - 1;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    put2<TOut>(orow + kNph * (8 * (i >> 2) + (i & 3)), CIW_OUT(accp[i]), CIW_OUT(acc[i]));
+            }
+#undef CIW_OUT
+            }
+        }
+        wait_vm_lgkm_lds_only();
+        wg_barrier();                // tile complete; this row's buffer is free
+
+        // ---- output row (n, h): K rows of Q contiguous elements.  Exactly
+        // a.ns stores per thread (surplus threads repeat the last one).
+        const uint32_t n = fdiv(row, a.fdP);
+        const int h = row - n * a.P;
+        TOut* yrow = y + (size_t)n * a.K * PQ + (size_t)h * a.Q;
+        int k = sk0, v = sv0;
+        for (int j = 0; j < a.ns; ++j) {
+            const int kk = min(k, a.K - 1);
+            const int off = kk < k ? (a.Q - E) : v * E;
+            if (a.vec_store)
+                *reinterpret_cast<uint4*>(yrow + (size_t)kk * PQ + off) =
+                    *reinterpret_cast<const uint4*>(otile + kk * a.ostride + off);
+            else
+                yrow[(size_t)kk * PQ + off] = otile[kk * a.ostride + off];
+            k += dk;
+            v += dv;
+            if (v >= nq) {
+                v -= nq;
+                ++k;
+            }
+        }
+        // the tile is rewritten by the next row only after its row-ready
+        // barrier, which every thread reaches after finishing these reads
+    }
+}
+
+// Filter layout for the row kernel, in the order the A fragments are
+// loaded: aperm[ph][kh][s][lane][e] holds filter entry (k, t') with
+// k = 32 kh + lane % 32 and t' = 16 s + 8 (lane / 32) + e, so one wave's
+// load of a whole step is 1 KB of consecutive bytes.  Entry (k, t') is
+// F[k][c][r][q] at window-order index t = t' - delta(ph) = (q*R + r)*C + c
+// when 0 <= t < T and k < K, else 0 (phase shift and zero padding).
+struct PermArgs {
+    int C, K, R, S, D, T, steps;
+    FastDiv fdSteps, fdC, fdR;
+    uint32_t total;                // nph * 2 * steps * 512
+};
+
+__global__ __launch_bounds__(kThreads) void mfma_filter_perm_kernel(
+    const uint16_t* __restrict__ w, uint16_t* __restrict__ aperm, PermArgs p) {
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= p.total) return;
+    const int e = i & 7;
+    const int lane = (i >> 3) & 63;
+    const uint32_t rest = i >> 9;                 // (ph * 2 + kh) * steps + s
+    const uint32_t phk = fdiv(rest, p.fdSteps);
+    const int s = rest - phk * p.steps;
+    const int kh = phk & 1;
+    const int ph = phk >> 1;
+    const int k = kh * 32 + (lane & 31);
+    const int t = 16 * s + 8 * (lane >> 5) + e - ((ph * p.D) & 7);
+    uint16_t v = 0;
+    if (k < p.K && t >= 0 && t < p.T) {
+        const uint32_t qr = fdiv(t, p.fdC);
+        const int c = t - qr * p.C;
+        const uint32_t q = fdiv(qr, p.fdR);
+        const int r = qr - q * p.R;
+        v = w[(((size_t)k * p.C + c) * p.R + r) * p.S + q];
+    }
+    aperm[i] = v;
+}
+
+struct MfRowPlan {
+    MfRowArgs a;
+    int nset, steps, pad;
+    bool mask, tail_last;
+    size_t lds_bytes;
+    int wgs_per_cu;
+};
+
+int gcd_int(int x, int y) {
+    while (y) {
+        int t = x % y;
+        x = y;
+        y = t;
+    }
+    return x;
+}
+
+// Row-kernel plan; false when the layer does not fit it.
+bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl) {
+    if (g.K > 64 || g.dw != 1) return false;
+    MfRowArgs& a = pl.a;
+    const int D = g.sw * g.R * g.C;
+    const int T = g.S * g.R * g.C;
+    const int nph = 8 / gcd_int(D, 8);
+    int maxdelta = 0;
+    for (int ph = 0; ph < nph; ++ph) maxdelta = std::max(maxdelta, (ph * D) & 7);
+    const int need = (T + maxdelta + 15) / 16;
+    const int nset = nph == 1 ? 1 : nph / 2;
+    // compiled step counts (a few more steps than needed only cost MFMAs
+    // on zero filter entries)
+    int steps = 0;
+    for (int c : {10, 16, 24, 36, 40})
+        if (c >= need) {
+            steps = c;
+            break;
+        }
+    if (steps == 0 || nset * steps > 40) return false;
+    // masking is needed unless every step lies wholly inside the window;
+    // tail_last: every phase's window ends in the last step
+    const bool mask = maxdelta > 0 || T != 16 * steps;
+    bool tail_last = true;
+    for (int ph = 0; ph < nph; ++ph) tail_last = tail_last && ((ph * D) & 7) + T >= 16 * (steps - 1);
+    const int mcount = (g.Q + nph - 1) / nph;
+    const int mblocks = (mcount + 31) / 32;
+    const int nchunks = g.pitchB / 8;
+    // row layout: with nph > 1 the lanes of a fragment start an odd number
+    // of chunks apart (D * nph / 8 = D / gcd(D, 8)); with nph = 1 they start
+    // G = D / 8 chunks apart and a pad chunk after every PAD chunks (PAD the
+    // power-of-two part of G, at most 8) makes the stride G + G / PAD odd
+    const int G = nph == 1 ? D / 8 : 0;
+    int pad = 1;
+    if (nph == 1)
+        while (pad < 8 && G % (2 * pad) == 0) pad *= 2;
+    const int stride = pad == 1 ? D * nph / 8 : G + G / pad;   // chunks between lane starts
+    const int copy_chunks = pad == 1 ? nchunks : (nchunks + pad - 1) / pad * (pad + 1);
+    if (copy_chunks > kMfMaxChunks * kThreads) return false;
+    const int nd = (copy_chunks + kThreads - 1) / kThreads;
+    // the furthest LDS chunk a fragment read touches: the last pixel's run
+    // over the whole padded reduction (a run starts at the pixel's stride
+    // position; g adds one chunk; each step two, plus the pads passed)
+    const int wmax = std::max(g.Q - 1, nph - 1);
+    const int run_end = 1 + 2 * (steps - 1) + (pad == 1 ? 0 : (2 * (steps - 1)) / pad);
+    const int last_chunk = (pad == 1 ? (wmax * D) / 8 : wmax * stride) + run_end;
+    // one copy instruction covers 256 positions, so a row shorter than that
+    // still takes 256
+    int buf_chunks = std::max(std::max(copy_chunks, last_chunk + 1), nd == 1 ? kThreads : 0);
+    buf_chunks = (buf_chunks + 15) / 16 * 16;
+    const int buf = buf_chunks * 8;
+    // output tile: every pixel of every block has a column (pixels past the
+    // row end are written but never stored); an odd number of 16-byte units
+    // per row spreads the channel rows of a tile write over the banks
+    const int V = 16 / out_bytes;
+    int ostride = (nph * 32 * mblocks + V - 1) / V * V;
+    if (((ostride * out_bytes) / 16) % 2 == 0) ostride += V;
+    const size_t tile = (size_t)g.K * ostride * out_bytes + 64 * 4;
+    // workgroups per CU, then ring depth, within the 160 KB of LDS of a CU:
+    // two workgroups (two waves per SIMD, one multiplying while the other
+    // waits at a barrier or stores) beat one with a deeper ring
+    int nbuf = 0, wgs = 0;
+    for (int w = 2; w >= 1 && nbuf == 0; --w)
+        for (int nb = 6; nb >= 2; --nb)
+            if (((size_t)nb * buf * 2 + tile) * w <= 160 * 1024) {
+                nbuf = nb;
+                wgs = w;
+                break;
+            }
+    if (nbuf == 0) return false;
+    const int vec_store = (g.Q % V == 0 && ((int64_t)g.P * g.Q) % V == 0) ? 1 : 0;
+    const int64_t total = vec_store ? (int64_t)g.K * (g.Q / V) : (int64_t)g.K * g.Q;
+    const int ns = (int)((total + kThreads - 1) / kThreads);
+    // the wait counts must fit the 6-bit vector-memory counter: a shorter
+    // ring when the copies and stores of nbuf - 1 rows would not
+    while (nbuf > 2 && (nd + ns) * (nbuf - 1) > 63) --nbuf;
+    if ((nd + ns) * (nbuf - 1) > 63) return false;
+    const size_t lds = (size_t)nbuf * buf * 2 + tile;
+    a.C = g.C; a.K = g.K; a.R = g.R; a.S = g.S; a.P = g.P; a.Q = g.Q;
+    a.pitch = g.pitchB;
+    a.D = D; a.T = T;
+    a.nph = nph; a.mblocks = mblocks;
+    a.G = G;
+    a.nchunks = nchunks;
+    a.copy_chunks = copy_chunks;
+    a.buf_elems = buf;
+    a.nbuf = nbuf;
+    a.nd = nd;
+    a.ostride = ostride;
+    a.vec_store = vec_store;
+    a.ns = ns;
+    a.fdP = make_fastdiv(g.P);
+    pl.nset = nset;
+    pl.steps = steps;
+    pl.pad = pad;
+    pl.mask = mask;
+    pl.tail_last = tail_last;
+    pl.lds_bytes = lds;
+    pl.wgs_per_cu = wgs;
+    return true;
+}
+
+// Raise a kernel's dynamic-LDS limit on this device once: the attribute
+// persists, so later launches (graph captures included) skip the call.
+hipError_t allow_lds(const void* fn, int dev, size_t bytes) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, size_t> done;
+    std::lock_guard<std::mutex> lock(mu);
+    size_t& have = done[{dev, fn}];
+    if (have >= bytes) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) have = bytes;
+    return e;
+}
+
+// One compiled kernel: the tail-in-last-step form exists only for masked
+// plans (without masks it would be the same kernel).
+template <typename TIn, typename TOut, int NS, int M, bool MK, int PD>
+hipError_t launch_rows_one(const MfRowPlan& pl, int dev, int64_t grid, const void* xw,
+                           const void* aperm, const void* bias, void* y, const MfRowArgs& a,
+                           hipStream_t st) {
+    void (*kfn)(const uint16_t*, const uint16_t*, const TIn*, TOut*, MfRowArgs) =
+        conv_mfma_rows_kernel<TIn, TOut, NS, M, MK, PD, false>;
+    if constexpr (MK) {
+        if (pl.tail_last) kfn = conv_mfma_rows_kernel<TIn, TOut, NS, M, MK, PD, true>;
+    }
+    // more than 64 KB of dynamic LDS per workgroup must be allowed explicitly
+    if (pl.lds_bytes > 65536 && allow_lds(reinterpret_cast<const void*>(kfn), dev, pl.lds_bytes) != hipSuccess)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kfn, dim3((uint32_t)grid), dim3(kThreads), pl.lds_bytes, st,
+                       (const uint16_t*)xw, (const uint16_t*)aperm, (const TIn*)bias, (TOut*)y, a);
+    return hipSuccess;
+}
+
+template <typename TIn, typename TOut>
+hipError_t launch_rows(const Geom& g, MfRowPlan pl, const void* xw, const void* aperm,
+                       const void* bias, void* y, int n_images, hipStream_t st) {
+    MfRowArgs a = pl.a;
+    const int64_t rows = (int64_t)n_images * g.P;
+    if (rows >= (1ll << 31)) return hipErrorInvalidValue;
+    a.rows = (int)rows;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    int64_t grid = (int64_t)cus * pl.wgs_per_cu;   // resident workgroups only
+    if (grid > rows) grid = rows;
+#define CIW_MF_LAUNCH(NS, M, MK, PD)                                                           \
+    do {                                                                                       \
+        const hipError_t e_ = launch_rows_one<TIn, TOut, NS, M, MK, PD>(pl, dev, grid, xw, aperm, \
+                                                                        bias, y, a, st);       \
+        if (e_ != hipSuccess) return e_;                                                       \
+    } while (0)
+#define CIW_MF_STEPS(MK, PD)                                                                   \
+    do {                                                                                       \
+        if (pl.steps == 10) CIW_MF_LAUNCH(1, 10, MK, PD);                                      \
+        else if (pl.steps == 16) CIW_MF_LAUNCH(1, 16, MK, PD);                                 \
+        else if (pl.steps == 24) CIW_MF_LAUNCH(1, 24, MK, PD);                                 \
+        else if (pl.steps == 36) CIW_MF_LAUNCH(1, 36, MK, PD);                                 \
+        else CIW_MF_LAUNCH(1, 40, MK, PD);                                                     \
+    } while (0)
+#define CIW_MF_PAD(MK)                                                                         \
+    do {                                                                                       \
+        if (pl.pad == 1) CIW_MF_STEPS(MK, 1);                                                  \
+        else if (pl.pad == 2) CIW_MF_STEPS(MK, 2);                                             \
+        else if (pl.pad == 4) CIW_MF_STEPS(MK, 4);                                             \
+        else CIW_MF_STEPS(MK, 8);                                                              \
+    } while (0)
+    if (pl.nset == 1) {
+        if (pl.mask) CIW_MF_PAD(true);
+        else CIW_MF_PAD(false);
+    } else if (pl.nset == 2) {    // several phases: nph > 1, no pad chunks
+        if (pl.steps == 10) CIW_MF_LAUNCH(2, 10, true, 1);
+        else CIW_MF_LAUNCH(2, 16, true, 1);
+    } else {
+        CIW_MF_LAUNCH(4, 10, true, 1);
+    }
+#undef CIW_MF_PAD
+#undef CIW_MF_STEPS
+#undef CIW_MF_LAUNCH
+    return hipGetLastError();
+}
+
+template <typename TIn, typename TOut>
+hipError_t launch_t(const Geom& g, const void* xw, const void* w, const void* aperm,
+                    const void* bias, void* y, int n_images, bool generic, hipStream_t st) {
+    if (n_images == 0) return hipSuccess;
+    MfRowPlan pl;
+    if (!generic && aperm && mf_row_plan(g, (int)sizeof(TOut), pl))
+        return launch_rows<TIn, TOut>(g, pl, xw, aperm, bias, y, n_images, st);
+    MfmaArgs a;
+    a.C = g.C; a.K = g.K; a.R = g.R; a.S = g.S; a.P = g.P; a.Q = g.Q;
+    a.sw = g.sw; a.dw = g.dw; a.pitch = g.pitchB;
+    a.RC = g.R * g.C;
+    a.T = g.S * a.RC;
+    a.npix = n_images * g.P * g.Q;
+    a.fdRC = make_fastdiv(a.RC);
+    a.fdC = make_fastdiv(g.C);
+    a.fdPQ = make_fastdiv(g.P * g.Q);
+    a.fdQ = make_fastdiv(g.Q);
+    dim3 grid((a.npix + kNB - 1) / kNB, (g.K + kMB - 1) / kMB);
+    hipLaunchKernelGGL((conv_mfma_generic_kernel<TIn, TOut>), grid, dim3(kThreads), 0, st,
+                       (const uint16_t*)xw, (const uint16_t*)w, (const TIn*)bias, (TOut*)y, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace ciw

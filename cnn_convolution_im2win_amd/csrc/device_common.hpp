@@ -29,17 +29,12 @@ __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <>
 __device__ __forceinline__ half_t from_f32<half_t>(float v) { return (half_t)v; }
 
-// fp32 -> bf16, round to nearest even on the bit pattern; NaN stays NaN.
+// fp32 -> bf16, round to nearest even (the hardware conversion, two values
+// per instruction); NaN stays NaN.
 template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
-    uint32_t u = __float_as_uint(v);
     bf16_t r;
-    if ((u & 0x7fffffffu) > 0x7f800000u) {
-        r.bits = (uint16_t)((u >> 16) | 0x40u);
-    } else {
-        u += 0x7fffu + ((u >> 16) & 1u);
-        r.bits = (uint16_t)(u >> 16);
-    }
+    r.bits = __builtin_bit_cast(uint16_t, (__bf16)v);
     return r;
 }
 
