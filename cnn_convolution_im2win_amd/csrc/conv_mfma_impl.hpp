@@ -338,8 +338,8 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
     const int npb = a.nph * a.mblocks;
 
     uint16_t* ring = lds;                                                 // nbuf x buf_elems
-    TOut* otile = reinterpret_cast<TOut*>(lds + a.nbuf * a.buf_elems);   // K x ostride
-    float* bias_l = reinterpret_cast<float*>(otile + a.K * a.ostride);   // 64 floats
+    TOut* otile0 = reinterpret_cast<TOut*>(lds + a.nbuf * a.buf_elems);  // 2 x K x ostride
+    float* bias_l = reinterpret_cast<float*>(otile0 + 2 * a.K * a.ostride);   // 64 floats
 
     // ---- filter fragments, laid out by the prep kernel in fragment order
     // (phase-shifted, zero-padded): lane holds F[t = 16 s + 8 (lane / 32)
@@ -438,16 +438,75 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
     const int sk0 = tid / nq, sv0 = tid - sk0 * nq;
     const int dk = kThreads / nq, dv = kThreads - dk * nq;
 
+    // ---- output row (n, h) from a tile: K rows of Q contiguous elements.
+    // Exactly a.ns stores per thread (surplus threads repeat the last one);
+    // each tile read is issued one store ahead of its use.
     const int PQ = a.P * a.Q;
+    auto store_row = [&](int row, const TOut* tl) {
+        const uint32_t n = fdiv(row, a.fdP);
+        const int h = row - n * a.P;
+        TOut* yrow = y + (size_t)n * a.K * PQ + (size_t)h * a.Q;
+        int k = sk0, v = sv0;
+        // element offsets of store j in the tile (src) and in the output row
+        // block (dst); advance to store j + 1
+        int src, dst_k, dst_off;
+        auto take = [&]() {
+            const int kk = min(k, a.K - 1);
+            dst_off = kk < k ? (a.Q - E) : v * E;
+            dst_k = kk;
+            src = kk * a.ostride + dst_off;
+            k += dk;
+            v += dv;
+            if (v >= nq) {
+                v -= nq;
+                ++k;
+            }
+        };
+        take();
+        if (a.vec_store) {
+            uint4 cur = *reinterpret_cast<const uint4*>(tl + src);
+            for (int j = 0; j < a.ns; ++j) {
+                TOut* dp = yrow + (size_t)dst_k * PQ + dst_off;
+                uint4 nxt = cur;
+                if (j + 1 < a.ns) {
+                    take();
+                    nxt = *reinterpret_cast<const uint4*>(tl + src);
+                }
+                *reinterpret_cast<uint4*>(dp) = cur;
+                cur = nxt;
+            }
+        } else {
+            TOut cur = tl[src];
+            for (int j = 0; j < a.ns; ++j) {
+                TOut* dp = yrow + (size_t)dst_k * PQ + dst_off;
+                TOut nxt = cur;
+                if (j + 1 < a.ns) {
+                    take();
+                    nxt = tl[src];
+                }
+                *dp = cur;
+                cur = nxt;
+            }
+        }
+    };
+
+    // Iteration it: wait for row it's copy, barrier, copy row it + nbuf - 1
+    // into the buffer row it - 1 used (every wave is past it now), store
+    // row it - 1 from its tile, then multiply row it into the other tile.
+    // The stores thus overlap the next row's multiplies, and the barrier
+    // that makes row it visible also makes tile it - 1 complete.
     for (int it = 0; it < my_rows; ++it) {
         const int row = first + it;
         const int buf = it % a.nbuf;
-        if (it + a.nbuf - 1 < my_rows) copy_row(first + it + a.nbuf - 1, (it + a.nbuf - 1) % a.nbuf);
         // wait for this row's copy: allow the copies of the rows after it
         // and the output stores issued since it to stay in flight
-        const int later_rows = min(a.nbuf - 1, my_rows - 1 - it);
-        wait_vm_lgkm(a.nd * later_rows + a.ns * min(it, a.nbuf - 1));
-        wg_barrier();                // every wave's part of the row has landed
+        const int later_rows = min(a.nbuf - 2, my_rows - 1 - it);
+        const int later_stores = max(0, it - max(it - a.nbuf + 1, 1));
+        wait_vm_lgkm(a.nd * later_rows + a.ns * later_stores);
+        wg_barrier();                // row it landed; tile it - 1 complete and read by nobody
+        if (it + a.nbuf - 1 < my_rows) copy_row(first + it + a.nbuf - 1, (it + a.nbuf - 1) % a.nbuf);
+        if (it > 0) store_row(row - 1, otile0 + ((it - 1) & 1) * a.K * a.ostride);
+        TOut* otile = otile0 + (it & 1) * a.K * a.ostride;
 
         const uint16_t* lb = ring + buf * a.buf_elems;
         // Pixel blocks pb = phase + nph * (32-pixel block): the wave takes
@@ -564,33 +623,11 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
 #undef CIW_OUT
             }
         }
-        wait_vm_lgkm_lds_only();
-        wg_barrier();                // tile complete; this row's buffer is free
-
-        // ---- output row (n, h): K rows of Q contiguous elements.  Exactly
-        // a.ns stores per thread (surplus threads repeat the last one).
-        const uint32_t n = fdiv(row, a.fdP);
-        const int h = row - n * a.P;
-        TOut* yrow = y + (size_t)n * a.K * PQ + (size_t)h * a.Q;
-        int k = sk0, v = sv0;
-        for (int j = 0; j < a.ns; ++j) {
-            const int kk = min(k, a.K - 1);
-            const int off = kk < k ? (a.Q - E) : v * E;
-            if (a.vec_store)
-                *reinterpret_cast<uint4*>(yrow + (size_t)kk * PQ + off) =
-                    *reinterpret_cast<const uint4*>(otile + kk * a.ostride + off);
-            else
-                yrow[(size_t)kk * PQ + off] = otile[kk * a.ostride + off];
-            k += dk;
-            v += dv;
-            if (v >= nq) {
-                v -= nq;
-                ++k;
-            }
-        }
-        // the tile is rewritten by the next row only after its row-ready
-        // barrier, which every thread reaches after finishing these reads
     }
+    // the last row's tile
+    wait_vm_lgkm_lds_only();
+    wg_barrier();
+    store_row(first + my_rows - 1, otile0 + ((my_rows - 1) & 1) * a.K * a.ostride);
 }
 
 // Filter layout for the row kernel, in the order the A fragments are
@@ -703,7 +740,8 @@ bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl) {
     const int V = 16 / out_bytes;
     int ostride = (nph * 32 * mblocks + V - 1) / V * V;
     if (((ostride * out_bytes) / 16) % 2 == 0) ostride += V;
-    const size_t tile = (size_t)g.K * ostride * out_bytes + 64 * 4;
+    // two tiles: row it - 1 is stored from one while row it fills the other
+    const size_t tile = 2 * (size_t)g.K * ostride * out_bytes + 64 * 4;
     // workgroups per CU, then ring depth, within the 160 KB of LDS of a CU:
     // two workgroups (two waves per SIMD, one multiplying while the other
     // waits at a barrier or stores) beat one with a deeper ring
