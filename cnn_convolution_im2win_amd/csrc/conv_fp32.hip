@@ -102,7 +102,11 @@ __global__ __launch_bounds__(kThreads) void conv_fp32_generic_kernel(
 }
 
 // --------------------------------------------------------------- fast kernel
-constexpr int kRW = 4;          // output rows per wave (fast kernel)
+// Output rows per wave (fast kernel).  Two balance the row groups of
+// small images (13 rows split 2,2,...,1 rather than 4,3,3,3) and leave
+// registers for more resident waves; measured faster than 3 or 4 on the
+// 13x13 and 32x32 layers even though each filter tap then serves 2 rows.
+constexpr int kRW = 2;
 
 struct KlArgs {
     int C, K, P, Q, pitch;
