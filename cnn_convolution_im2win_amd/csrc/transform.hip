@@ -356,22 +356,41 @@ __global__ __launch_bounds__(kThreads) void im2win_hwc_rows_kernel(const T* __re
         __syncthreads();
         const int wv = a.W / V;
         const int vitems = a.C * a.R * wv;
-        for (int it = tid; it < vitems; it += kThreads) {
-            const uint32_t q = fdiv(it, a.fdWv);
-            const int jv = it - q * wv;
-            const uint32_t c = fdiv(q, a.fdR);
-            const int r = q - c * a.R;
-            const int ih = h * a.sh - a.ph + r * a.dh;
-            if (ih < 0 || ih >= a.H) continue;
+        // up to kBatch items per thread: all their loads are in flight before
+        // the first is scattered into LDS
+        constexpr int kBatch = 4;
+        for (int base = tid; base < vitems; base += kBatch * kThreads) {
             union {
                 uint4 u;
                 T e[V];
-            } pk;
-            pk.u = reinterpret_cast<const uint4*>(x + (((size_t)n * a.C + c) * a.H + ih) * a.W)[jv];
-            T* tp = tile + (jv * V + a.pw) * a.xs + r * a.C + c;
+            } pk[kBatch];
+            int dst[kBatch], col0[kBatch];
 #pragma unroll
-            for (int i = 0; i < V; ++i) {
-                if (jv * V + i + a.pw < a.Wwin) tp[i * a.xs] = pk.e[i];
+            for (int u = 0; u < kBatch; ++u) {
+                const int it = base + u * kThreads;
+                dst[u] = -1;
+                col0[u] = 0;
+                pk[u].u = make_uint4(0u, 0u, 0u, 0u);
+                if (it < vitems) {
+                    const uint32_t q = fdiv(it, a.fdWv);
+                    const int jv = it - q * wv;
+                    const uint32_t c = fdiv(q, a.fdR);
+                    const int r = q - c * a.R;
+                    const int ih = h * a.sh - a.ph + r * a.dh;
+                    if (ih >= 0 && ih < a.H) {
+                        pk[u].u = reinterpret_cast<const uint4*>(
+                            x + (((size_t)n * a.C + c) * a.H + ih) * a.W)[jv];
+                        col0[u] = jv * V + a.pw;
+                        dst[u] = col0[u] * a.xs + r * a.C + c;
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (dst[u] < 0) continue;
+#pragma unroll
+                for (int i = 0; i < V; ++i)
+                    if (col0[u] + i < a.Wwin) tile[dst[u] + i * a.xs] = pk[u].e[i];
             }
         }
         __syncthreads();
