@@ -17,6 +17,9 @@ Parts (the C ones live in ``conv_oracle.c``, plain C, fp64):
   O4 ``im2col_conv`` -- numpy: the im2col matrix (one row per sliding window)
      times the filter matrix, per image ("CS149 L9 ... Rewriting as matrix
      multiply: explicit GEMM").
+  O5 ``relu_pool`` -- the fused epilogue of the CS149 page's conv ->
+     scale/bias -> max-pool chain ("Fusion: keep intermediates out of
+     memory"): ReLU, then the max over non-overlapping 2x2 regions.
 The diagonalwise identity for depthwise layers ("Diagonalwise
 Refactorization ...", abstract) is exercised in the tests through O1.
 """
@@ -43,7 +46,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-                               "-Wall", "-o", tmp, _SRC])
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -78,6 +81,8 @@ def open_library(path: str):
     lib.oracle_im2win.restype = None
     lib.oracle_window_conv.argtypes = [P, ctypes.c_int, P, P, P, P]
     lib.oracle_window_conv.restype = None
+    lib.oracle_relu_pool.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P]
+    lib.oracle_relu_pool.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -231,3 +236,21 @@ def im2col_conv(x, w, b=None, stride=1, pad=0, dil=1, groups=1) -> np.ndarray:
     if b is not None:
         y += b[None, :, None, None]
     return y
+
+
+def pooled_dims(P, Q, pool=True):
+    """Extent of O5's output: P/2 x Q/2 (floor) with pooling, else P x Q."""
+    return (P // 2, Q // 2) if pool else (P, Q)
+
+
+def relu_pool(y, relu=True, pool=True) -> np.ndarray:
+    """O5 on an fp64 copy of the conv output y[N][K][P][Q]."""
+    y = _f64(y)
+    N, K, P, Q = y.shape
+    P2, Q2 = pooled_dims(P, Q, pool)
+    out = np.zeros((N, K, P2, Q2), dtype=np.float64)
+    if out.size:
+        shape = np.array([N, K, P, Q], dtype=np.int64)
+        _load().oracle_relu_pool(shape.ctypes.data, int(bool(relu)), int(bool(pool)),
+                                 y.ctypes.data, out.ctypes.data)
+    return out

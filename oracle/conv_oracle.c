@@ -20,6 +20,7 @@
 #include <stdint.h>
 #include <stddef.h>
 #include <string.h>
+#include <math.h>
 
 enum { DN, DC, DH, DW, DK, DR, DS, DSH, DSW, DPH, DPW, DDH, DDW, DG, DLEN };
 
@@ -197,6 +198,36 @@ void oracle_window_conv(const int64_t* d, int layout, const double* xw,
                 y[(nk * P + h) * Q + wo] = b ? acc + b[k] : acc;
             }
     }
+}
+
+/* O5: the fused epilogue of the conv -> scale/bias -> max-pool chain
+ * ([CS149] "Fusion: keep intermediates out of memory", slides 56-57),
+ * applied to a biased convolution output y[N][K][P][Q] (O1's result):
+ *   - relu != 0: each value becomes max(v, 0) (the ReLU of [CS149] slide 14);
+ *   - pool != 0: out[n][k][j][i] is the largest of the 2x2 region
+ *     y[n][k][2j .. 2j+1][2i .. 2i+1] ("max over each 2x2 region", slide 23):
+ *     non-overlapping regions, so out is [N][K][P/2][Q/2] (floor: an odd
+ *     last row or column belongs to no region and is dropped).
+ * Every maximum is IEEE-754 maxNum (C's fmax): a NaN loses to a number.
+ * shape = { N, K, P, Q }. */
+static double act(double v, int relu) { return relu ? fmax(v, 0.0) : v; }
+
+void oracle_relu_pool(const int64_t* shape, int relu, int pool, const double* y, double* out) {
+    const int64_t N = shape[0], K = shape[1], P = shape[2], Q = shape[3];
+    if (!pool) {
+        for (int64_t i = 0; i < N * K * P * Q; ++i) out[i] = act(y[i], relu);
+        return;
+    }
+    const int64_t P2 = P / 2, Q2 = Q / 2;
+    for (int64_t nk = 0; nk < N * K; ++nk)
+        for (int64_t j = 0; j < P2; ++j)
+            for (int64_t i = 0; i < Q2; ++i) {
+                double m = act(y[(nk * P + 2 * j) * Q + 2 * i], relu);
+                for (int64_t dy = 0; dy < 2; ++dy)
+                    for (int64_t dx = 0; dx < 2; ++dx)
+                        m = fmax(m, act(y[(nk * P + 2 * j + dy) * Q + 2 * i + dx], relu));
+                out[(nk * P2 + j) * Q2 + i] = m;
+            }
 }
 
 int oracle_num_threads(void) {

@@ -44,6 +44,11 @@ MUTANTS = [
     ("win_width_short", "return (Q - 1) * d[DSW] + d[DDW] * (d[DS] - 1) + 1;",
      "return (Q - 1) * d[DSW] + d[DDW] * (d[DS] - 1);"),
     ("pitch_not_rounded", "return (row_elems + v - 1) / v * v;", "return row_elems;"),
+    ("relu_dropped", "return relu ? fmax(v, 0.0) : v;", "return v;"),
+    ("pool_min_not_max", "m = fmax(m, act(", "m = fmin(m, act("),
+    ("pool_stride_one", "y[(nk * P + 2 * j + dy) * Q + 2 * i + dx]", "y[(nk * P + j + dy) * Q + i + dx]"),
+    ("pool_column_dropped", "y[(nk * P + 2 * j + dy) * Q + 2 * i + dx]", "y[(nk * P + 2 * j + dy) * Q + 2 * i]"),
+    ("pool_row_dropped", "y[(nk * P + 2 * j + dy) * Q + 2 * i + dx]", "y[(nk * P + 2 * j) * Q + 2 * i + dx]"),
 ]
 
 PIN_TESTS = [getattr(pins, n) for n in dir(pins) if n.startswith("test_")]
@@ -81,7 +86,7 @@ def test_mutant_is_caught(name, old, new, tmp_path):
     c_path.write_text(mutated)
     so_path = tmp_path / "libmutant.so"
     subprocess.check_call(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-                           "-o", str(so_path), str(c_path)])
+                           "-o", str(so_path), str(c_path), "-lm"])
     saved = oracle._lib
     oracle._lib = oracle.open_library(str(so_path))
     try:

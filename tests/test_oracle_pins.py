@@ -4,7 +4,9 @@ Every check here ties the oracle to something other than itself: closed
 forms worked out by hand, scipy's 2-D cross-correlation, a numpy im2col
 product, textbook reductions (1x1 conv = matrix product, full-size filter =
 fully connected layer), invariants (delta filter, linearity, zero-padding tap
-counts) and the diagonalwise identity for depthwise layers.
+counts) and the diagonalwise identity for depthwise layers.  The fused
+epilogue (ReLU, 2x2 max-pool) is pinned by closed forms on ramps, torch's
+CPU max_pool2d, the ReLU/max commutation and IEEE maxNum on NaN.
 """
 import numpy as np
 import pytest
@@ -358,6 +360,74 @@ def test_window_conv_depthwise_equals_direct():
         y3 = oracle.window_conv(xw, x.shape, w, b, L.stride, L.pad, L.dil, L.groups)
         y1 = oracle.conv2d(x, w, b, L.stride, L.pad, L.dil, L.groups)
         np.testing.assert_allclose(y3, y1, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------- fused epilogue (O5)
+def ramp_map(P, Q, sign=1.0):
+    # y[h][w] = sign * (h Q + w) for one image and channel
+    return sign * np.arange(P * Q, dtype=np.float64).reshape(1, 1, P, Q)
+
+
+def test_pool_increasing_ramp_takes_bottom_right():
+    # odd extents: the last row and column belong to no 2x2 region
+    out = oracle.relu_pool(ramp_map(5, 7), relu=False, pool=True)
+    assert out.shape == (1, 1, 2, 3)
+    expect = [[(2 * j + 1) * 7 + 2 * i + 1 for i in range(3)] for j in range(2)]
+    assert np.array_equal(out[0, 0], expect)
+
+
+def test_pool_decreasing_ramp_takes_top_left():
+    out = oracle.relu_pool(ramp_map(4, 6, -1.0), relu=False, pool=True)
+    expect = [[-(2 * j * 6 + 2 * i) for i in range(3)] for j in range(2)]
+    assert np.array_equal(out[0, 0], expect)
+
+
+def test_relu_closed_form():
+    y = np.array([-2.0, -0.5, 0.0, 0.5, 3.0]).reshape(1, 1, 1, 5)
+    assert np.array_equal(oracle.relu_pool(y, relu=True, pool=False)[0, 0, 0],
+                          [0.0, 0.0, 0.0, 0.5, 3.0])
+    assert np.array_equal(oracle.relu_pool(y, relu=False, pool=False), y)
+    # a region of negatives pools to its largest value, or to 0 after ReLU
+    neg = ramp_map(2, 2, -1.0) - 1.0
+    assert oracle.relu_pool(neg, relu=False, pool=True)[0, 0, 0, 0] == -1.0
+    assert oracle.relu_pool(neg, relu=True, pool=True)[0, 0, 0, 0] == 0.0
+
+
+def test_pool_against_torch_max_pool2d():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(31)
+    for P, Q in [(2, 2), (7, 6), (6, 9), (13, 13), (3, 2)]:
+        y = rng.standard_normal((2, 3, P, Q))
+        t = torch.from_numpy(y)
+        ref_pool = torch.nn.functional.max_pool2d(t, 2).numpy()
+        ref_both = torch.nn.functional.max_pool2d(torch.relu(t), 2).numpy()
+        assert np.array_equal(oracle.relu_pool(y, relu=False, pool=True), ref_pool)
+        assert np.array_equal(oracle.relu_pool(y, relu=True, pool=True), ref_both)
+
+
+def test_relu_and_pool_commute():
+    # ReLU is monotone, so it commutes with the max: the order the kernels
+    # apply them in cannot change the result
+    y = np.random.default_rng(32).standard_normal((2, 2, 6, 8))
+    relu_then_pool = oracle.relu_pool(y, relu=True, pool=True)
+    pool_then_relu = oracle.relu_pool(oracle.relu_pool(y, relu=False, pool=True),
+                                      relu=True, pool=False)
+    assert np.array_equal(relu_then_pool, pool_then_relu)
+
+
+def test_pool_maxima_are_maxnum():
+    y = np.array([[np.nan, 1.0], [-2.0, 0.5]]).reshape(1, 1, 2, 2)
+    assert oracle.relu_pool(y, relu=False, pool=True)[0, 0, 0, 0] == 1.0
+    assert np.isnan(oracle.relu_pool(np.full((1, 1, 2, 2), np.nan), False, True)).all()
+    assert oracle.relu_pool(np.array([np.nan]).reshape(1, 1, 1, 1), True, False)[0, 0, 0, 0] == 0.0
+
+
+def test_conv_bias_relu_pool_chain():
+    # delta filter and bias -8.5 on the ramp: y = X - 8.5; the bias comes
+    # before the ReLU, so only the bottom rows survive
+    y = oracle.conv2d(ramp16(), np.ones((1, 1, 1, 1)), np.array([-8.5]))
+    out = oracle.relu_pool(y, relu=True, pool=True)
+    assert np.array_equal(out[0, 0], [[0.0, 0.0], [14.0 - 8.5, 16.0 - 8.5]])
 
 
 # ---------------------------------------------------------------- input recipe
