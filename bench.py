@@ -11,9 +11,14 @@ the dominant kernel's roofline position (timed with HIP events on its launch
 stream), and the CPU oracle's throughput on the host cores.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers]
+                  [--epilogue none|relu|relu_pool]
 
 --workload picks one of the five synthetic layers (default: the 1x512x13x13
 -> 1024, 3x3 layer); --layers adds a per-layer summary of all five.
+--epilogue fuses ReLU, or ReLU and the 2x2 max-pool, into the contraction
+(CIW_FLAG_RELU / CIW_FLAG_MAXPOOL2); each layer then also reports, as
+context, the same result computed unfused: the plain convolution followed by
+torch's ReLU and max-pool over the full output.
 """
 from __future__ import annotations
 
@@ -39,6 +44,7 @@ PEAK_TFLOPS = {"mfma_f16": 2516.6, "mfma_bf16": 2516.6, "valu_f32": 157.3}
 PAGE_BASELINE = {"mid_3x3_fp32": 2 * 1024 * 512 * 9 * 169 / 913.301e-3 / 1e12}
 
 DEFAULT_WORKLOAD = "mid_3x3_fp32"
+EPILOGUES = ("none", "relu", "relu_pool")
 
 
 def describe(L: workloads.Layer) -> str:
@@ -51,14 +57,17 @@ class Step:
     """Pre-marshalled C-ABI calls for one layer (argument marshalling happens
     once, outside the timed region)."""
 
-    def __init__(self, L: workloads.Layer):
+    def __init__(self, L: workloads.Layer, epilogue: str = "none"):
         import numpy as np  # noqa: F401
         import torch
         import cnn_convolution_im2win_amd as ciw
         from cnn_convolution_im2win_amd import _lib
 
         self.L = L
+        self.epilogue = epilogue
         self.ciw = ciw
+        self.epi_flags = {"none": 0, "relu": ciw.CIW_FLAG_RELU,
+                          "relu_pool": ciw.CIW_FLAG_RELU | ciw.CIW_FLAG_MAXPOOL2}[epilogue]
         self.lib = _lib.load()
         code = {"f32": ciw.CIW_F32, "f16": ciw.CIW_F16, "bf16": ciw.CIW_BF16}
         self.in_code, self.out_code = code[L.dtype], code[L.out_dtype]
@@ -76,8 +85,9 @@ class Step:
         self.depthwise = L.groups > 1
         self.layout = ciw.CIW_WIN_HWC if (L.dtype != "f32" and not self.depthwise) else ciw.CIW_WIN_CHW
         self.P, self.Q = ciw.conv_im2win_output_dims(self.desc)
+        Po, Qo = ciw.conv2d_output_dims(self.desc, self.epi_flags)
         tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-        self.y = torch.empty((L.N, L.K, self.P, self.Q), dtype=tdt[L.out_dtype], device="cuda")
+        self.y = torch.empty((L.N, L.K, Po, Qo), dtype=tdt[L.out_dtype], device="cuda")
         self.ws_bytes = ciw.conv2d_workspace_bytes(self.desc, self.in_code, L.N)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
         self.win_bytes = ciw.conv_im2win_window_bytes(self.desc, self.in_code, self.layout, L.N)
@@ -88,7 +98,8 @@ class Step:
         self.dref = ctypes.byref(self.desc)
         self.args_fwd = (self.dref, self.in_code, self.out_code, None, self.w.data_ptr(),
                          None if self.b is None else self.b.data_ptr(), self.y.data_ptr(),
-                         self.ws.data_ptr(), self.ws_bytes, ciw.CIW_FLAG_WINDOW_READY, self.sp)
+                         self.ws.data_ptr(), self.ws_bytes,
+                         ciw.CIW_FLAG_WINDOW_READY | self.epi_flags, self.sp)
         self.args_tr = (self.dref, self.in_code, self.layout, self.x.data_ptr(),
                         self.ws.data_ptr(), self.sp)
 
@@ -120,7 +131,8 @@ class Step:
         return self.y.numel() * self.y.element_size()
 
     def contraction_bytes(self):
-        # window tensor read once, filters and bias once, output written once
+        # window tensor read once, filters and bias once, output (pooled, if
+        # the pool is fused) written once
         return self.win_bytes + self.bytes_w() + self.bytes_b() + self.bytes_y()
 
     def transform_bytes(self):
@@ -160,6 +172,10 @@ def kernel_source_hash() -> str:
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(f.read())
     return h.hexdigest()
+
+
+def traffic_key(L: workloads.Layer, epilogue: str) -> str:
+    return L.name if epilogue == "none" else f"{L.name}+{epilogue}"
 
 
 def stored_traffic(workload: str):
@@ -234,9 +250,39 @@ def cpu_baseline(L: workloads.Layer, seconds: float) -> dict:
                       f"fp64 seven-loop direct convolution"}
 
 
-def measure_layer(L: workloads.Layer, steps: int, warmup: int) -> dict:
-    import statistics
+def time_unfused(L: workloads.Layer, epilogue: str, steps: int, warmup: int) -> float:
+    """Context for a fused epilogue: mean ms of the plain contraction followed
+    by torch's ReLU (and 2x2 max-pool) over the full output, on one stream."""
+    import torch
+    import torch.nn.functional as F
     step = Step(L)
+
+    def run():
+        step.contract()
+        with torch.cuda.stream(step.stream):
+            y = torch.relu(step.y)
+            if epilogue == "relu_pool":
+                y = F.max_pool2d(y, 2)
+        return y
+
+    for _ in range(warmup):
+        step.transform()
+        run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        step.transform()
+        e[0].record(step.stream)
+        run()
+        e[1].record(step.stream)
+    torch.cuda.synchronize()
+    return sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+
+
+def measure_layer(L: workloads.Layer, steps: int, warmup: int, epilogue: str = "none",
+                  unfused: bool = True) -> dict:
+    import statistics
+    step = Step(L, epilogue)
     ms, tr, co = time_steps(step, steps, warmup)
     tr_ms, co_ms = statistics.mean(tr), statistics.mean(co)
     res = {
@@ -250,9 +296,14 @@ def measure_layer(L: workloads.Layer, steps: int, warmup: int) -> dict:
         "contract_gbs": round(step.contraction_bytes() / (co_ms * 1e-3) / 1e9, 1),
         "roofline": step.contraction_roofline(co_ms),
     }
-    res["roofline"]["traffic"] = stored_traffic(L.name)
+    res["roofline"]["traffic"] = stored_traffic(traffic_key(L, epilogue))
     if not step.depthwise and L.dtype != "f32":
         res["mfma_frac"] = round(res["contract_tflops"] / PEAK_TFLOPS["mfma_" + L.dtype], 4)
+    if epilogue != "none":
+        res["epilogue"] = epilogue
+        res["output_bytes"] = step.bytes_y()
+        if unfused:
+            res["unfused_contract_ms"] = round(time_unfused(L, epilogue, steps, warmup), 5)
     return res, step
 
 
@@ -263,6 +314,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=workloads.LAYER_ORDER)
     ap.add_argument("--layers", action="store_true", help="also summarise all five layers")
+    ap.add_argument("--epilogue", default="none", choices=EPILOGUES,
+                    help="fuse ReLU / ReLU + 2x2 max-pool into the contraction")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="with --epilogue, skip the unfused comparison (e.g. under a profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -283,9 +338,9 @@ def main():
     torch.cuda.set_device(0)
 
     L = workloads.LAYERS[args.workload]
-    print(f"# measuring {describe(L)}: {args.warmup} warmup + {args.steps} steps", file=sys.stderr,
-          flush=True)
-    res, step = measure_layer(L, args.steps, args.warmup)
+    print(f"# measuring {describe(L)} (epilogue {args.epilogue}): {args.warmup} warmup + "
+          f"{args.steps} steps", file=sys.stderr, flush=True)
+    res, step = measure_layer(L, args.steps, args.warmup, args.epilogue, not args.no_unfused)
     print(f"# {json.dumps(res)}", file=sys.stderr, flush=True)
 
     if args.copy_calibration:
@@ -303,7 +358,8 @@ def main():
                 layers[name] = res
                 continue
             print(f"# measuring {name}", file=sys.stderr, flush=True)
-            r, _ = measure_layer(workloads.LAYERS[name], max(10, args.steps // 5), 5)
+            r, _ = measure_layer(workloads.LAYERS[name], max(10, args.steps // 5), 5,
+                                 args.epilogue, not args.no_unfused)
             layers[name] = r
             print(f"# {name}: {json.dumps(r)}", file=sys.stderr, flush=True)
 
@@ -329,6 +385,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(L), "global_batch": L.N,
                    "step": "conv_im2win_transform + conv2d_fwd(window ready)",
+                   "epilogue": "bias" + {"none": "", "relu": " + relu",
+                                         "relu_pool": " + relu + 2x2 max-pool"}[args.epilogue],
                    "transform_ms": res["transform_ms"], "contract_ms": res["contract_ms"]},
         "roofline": res["roofline"],
         "cpu_baseline": cpu,

@@ -7,6 +7,7 @@ every step of the computation runs in the library's HIP kernels.  PyTorch
 supplies device memory and streams.
 
     y = conv2d(x, w, b, stride=1, padding=1)          # F.conv2d-style helper
+    y = conv2d(x, w, b, 1, 1, flags=CIW_FLAG_RELU | CIW_FLAG_MAXPOOL2)   # fused epilogue
     y = conv2d_fwd(x, w, b, y, workspace, ...)        # the C entry point
     xw = conv_im2win_transform(x, R, S, ...)          # the repack alone
 """
@@ -16,18 +17,20 @@ import ctypes
 from typing import Optional, Sequence, Tuple, Union
 
 from . import _lib
-from ._lib import (CIW_BF16, CIW_F16, CIW_F32, CIW_FLAG_GENERIC, CIW_FLAG_NO_SPLIT,
-                   CIW_FLAG_WINDOW_READY, CIW_WIN_CHW, CIW_WIN_HWC, ConvDesc, Im2winError,
-                   LIB_PATH, status_string)
+from ._lib import (CIW_BF16, CIW_F16, CIW_F32, CIW_FLAG_GENERIC, CIW_FLAG_MAXPOOL2,
+                   CIW_FLAG_NO_SPLIT, CIW_FLAG_RELU, CIW_FLAG_WINDOW_READY, CIW_WIN_CHW,
+                   CIW_WIN_HWC, ConvDesc, Im2winError, LIB_PATH, status_string)
 
 IntPair = Union[int, Sequence[int]]
 
 __all__ = [
     "conv2d", "conv2d_fwd", "conv2d_dw_fwd", "conv_im2win_transform",
-    "conv_im2win_output_dims", "conv_im2win_window_geometry", "conv_im2win_window_bytes",
+    "conv_im2win_output_dims", "conv2d_output_dims", "conv_im2win_window_geometry",
+    "conv_im2win_window_bytes",
     "conv2d_workspace_bytes", "make_desc", "Im2winError", "status_string", "LIB_PATH",
     "CIW_F32", "CIW_F16", "CIW_BF16", "CIW_WIN_CHW", "CIW_WIN_HWC",
-    "CIW_FLAG_WINDOW_READY", "CIW_FLAG_NO_SPLIT", "CIW_FLAG_GENERIC",
+    "CIW_FLAG_WINDOW_READY", "CIW_FLAG_NO_SPLIT", "CIW_FLAG_GENERIC", "CIW_FLAG_RELU",
+    "CIW_FLAG_MAXPOOL2",
 ]
 
 
@@ -80,6 +83,15 @@ def conv_im2win_output_dims(desc: ConvDesc) -> Tuple[int, int]:
     return P.value, Q.value
 
 
+def conv2d_output_dims(desc: ConvDesc, flags: int = 0) -> Tuple[int, int]:
+    """Extent of the output conv2d_fwd writes with these flags (P/2 x Q/2
+    with CIW_FLAG_MAXPOOL2)."""
+    P, Q = ctypes.c_int64(), ctypes.c_int64()
+    _lib.check(_lib.load().conv2d_output_dims(ctypes.byref(desc), int(flags), ctypes.byref(P),
+                                              ctypes.byref(Q)), "conv2d_output_dims")
+    return P.value, Q.value
+
+
 def conv_im2win_window_geometry(desc: ConvDesc, dtype: int, layout: int) -> Tuple[int, int, int]:
     rows, elems, pitch = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
     _lib.check(_lib.load().conv_im2win_window_geometry(
@@ -126,7 +138,7 @@ def conv_im2win_transform(x, R: int, S: int, stride: IntPair = 1, padding: IntPa
     return out
 
 
-def _check_shapes(desc: ConvDesc, x, w, bias, y) -> None:
+def _check_shapes(desc: ConvDesc, x, w, bias, y, flags: int = 0) -> None:
     """Host-side shape and dtype checks: the C ABI takes every extent from the
     descriptor, so a tensor that disagrees with it must never reach a kernel."""
     import torch
@@ -139,7 +151,7 @@ def _check_shapes(desc: ConvDesc, x, w, bias, y) -> None:
         raise ValueError("x and weight must share a dtype")
     if bias is not None and (bias.dim() != 1 or bias.numel() != desc.K or bias.dtype != w.dtype):
         raise ValueError("bias must be a [K] tensor of the weight's dtype")
-    P, Q = conv_im2win_output_dims(desc)
+    P, Q = conv2d_output_dims(desc, flags)
     if tuple(y.shape) != (desc.N, desc.K, P, Q):
         raise ValueError(f"y shape {tuple(y.shape)} != {(desc.N, desc.K, P, Q)}")
     if y.dtype not in (w.dtype, torch.float32):
@@ -151,7 +163,7 @@ def _conv_call(fn_name, x, w, bias, y, workspace, stride, padding, dilation, gro
     shape = x.shape if x is not None else x_shape
     desc = make_desc(shape, w.shape, stride, padding, dilation, groups)
     _need_device(x, w, bias, y, workspace)
-    _check_shapes(desc, x, w, bias, y)
+    _check_shapes(desc, x, w, bias, y, flags)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = getattr(_lib.load(), fn_name)(
         ctypes.byref(desc), _dtype_code(w.dtype), _dtype_code(y.dtype), _ptr(x), _ptr(w),
@@ -186,7 +198,7 @@ def conv2d(x, weight, bias=None, stride: IntPair = 1, padding: IntPair = 0,
     if x.dim() != 4 or weight.dim() != 4:
         raise ValueError("x and weight must be 4-D")
     desc = make_desc(x.shape, weight.shape, stride, padding, dilation, groups)
-    P, Q = conv_im2win_output_dims(desc)
+    P, Q = conv2d_output_dims(desc, flags)
     out_dtype = x.dtype if out_dtype is None else out_dtype
     y = torch.empty((x.shape[0], weight.shape[0], P, Q), dtype=out_dtype, device=x.device)
     depthwise = groups > 1

@@ -23,10 +23,13 @@ CIW_WIN_CHW, CIW_WIN_HWC = 0, 1
 CIW_FLAG_WINDOW_READY = 0x1
 CIW_FLAG_NO_SPLIT = 0x2
 CIW_FLAG_GENERIC = 0x4
+CIW_FLAG_RELU = 0x8
+CIW_FLAG_MAXPOOL2 = 0x10
 
 # the exported entry points, in header order
 ENTRY_POINTS = (
     "conv_im2win_output_dims",
+    "conv2d_output_dims",
     "conv_im2win_window_geometry",
     "conv_im2win_window_bytes",
     "conv_im2win_transform",
@@ -76,6 +79,7 @@ def load():
     psz = ctypes.POINTER(ctypes.c_size_t)
     sig = {
         "conv_im2win_output_dims": [D, pi64, pi64],
+        "conv2d_output_dims": [D, u32, pi64, pi64],
         "conv_im2win_window_geometry": [D, i32, i32, pi64, pi64, pi64],
         "conv_im2win_window_bytes": [D, i32, i32, i64, psz],
         "conv_im2win_transform": [D, i32, i32, P, P, P],

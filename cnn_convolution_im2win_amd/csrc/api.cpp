@@ -106,8 +106,13 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
     if (!dtype_ok(out)) return CIW_ERR_INVALID_ARG;
     // allowed (in -> out) pairs
     if (in == CIW_F32 ? out != CIW_F32 : (out != in && out != CIW_F32)) return CIW_ERR_INVALID_ARG;
-    if (flags & ~(CIW_FLAG_WINDOW_READY | CIW_FLAG_NO_SPLIT | CIW_FLAG_GENERIC))
+    if (flags & ~(CIW_FLAG_WINDOW_READY | CIW_FLAG_NO_SPLIT | CIW_FLAG_GENERIC | CIW_FLAG_RELU |
+                  CIW_FLAG_MAXPOOL2))
         return CIW_ERR_INVALID_ARG;
+    Epi epi;
+    epi.relu = (flags & CIW_FLAG_RELU) != 0;
+    epi.pool = (flags & CIW_FLAG_MAXPOOL2) != 0;
+    if (epi.pool && (g.P < 2 || g.Q < 2)) return CIW_ERR_INVALID_ARG;   // no 2x2 region
     if (depthwise) {
         if (!(g.G == g.C && g.K == g.C)) return g.G == 1 ? CIW_ERR_INVALID_ARG : CIW_ERR_UNSUPPORTED;
     } else if (g.G != 1) {
@@ -153,7 +158,7 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
         if (e != hipSuccess) return from_hip(e);
     }
     const int64_t x_img = (int64_t)g.C * g.H * g.W * g.elem;
-    const int64_t y_img = (int64_t)g.K * g.P * g.Q * elem_bytes(out);
+    const int64_t y_img = (int64_t)g.K * out_rows(g, epi) * out_cols(g, epi) * elem_bytes(out);
     unsigned char* wsb = (unsigned char*)ws;
     for (int64_t n0 = 0; n0 < g.N; n0 += nc) {
         const int n = (int)((g.N - n0) < nc ? (g.N - n0) : nc);
@@ -170,11 +175,11 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
             int splits = no_split ? 1 : fp32_splits(g, (int)nc);
             float* partials = (float*)(wsb + round_up(window_bytes_per_image(g, lay) * nc, 256));
             e = launch_conv_fp32(g, (const float*)wsb, (const float*)w, (const float*)bias,
-                                 (float*)yc, n, partials, splits, generic, st);
+                                 (float*)yc, n, partials, splits, generic, epi, st);
         } else if (p == PATH_MFMA) {
-            e = launch_conv_mfma(g, in, out, wsb, w, aperm, bias, yc, n, generic, st);
+            e = launch_conv_mfma(g, in, out, wsb, w, aperm, bias, yc, n, generic, epi, st);
         } else {
-            e = launch_conv_dw(g, in, out, wsb, w, bias, yc, n, generic, st);
+            e = launch_conv_dw(g, in, out, wsb, w, bias, yc, n, generic, epi, st);
         }
         if (e != hipSuccess) return from_hip(e);
     }
@@ -191,6 +196,18 @@ ciw_status conv_im2win_output_dims(const ciw_conv_desc* desc, int64_t* P, int64_
     if (s != CIW_OK) return s;
     if (P) *P = g.P;
     if (Q) *Q = g.Q;
+    return CIW_OK;
+}
+
+ciw_status conv2d_output_dims(const ciw_conv_desc* desc, uint32_t flags, int64_t* P, int64_t* Q) {
+    Geom g;
+    ciw_status s = resolve(desc, CIW_F32, &g);
+    if (s != CIW_OK) return s;
+    Epi epi;
+    epi.pool = (flags & CIW_FLAG_MAXPOOL2) != 0;
+    if (epi.pool && (g.P < 2 || g.Q < 2)) return CIW_ERR_INVALID_ARG;
+    if (P) *P = out_rows(g, epi);
+    if (Q) *Q = out_cols(g, epi);
     return CIW_OK;
 }
 

@@ -17,6 +17,11 @@
 // outputs in memory order, so the stores are contiguous too.
 //
 // Generic kernel: any shape; one thread per output.
+//
+// Fused epilogue: bias, optional ReLU, optional 2x2 max-pool; with the pool
+// a thread computes the four outputs of its region and stores their max.
+#include <algorithm>
+
 #include "internal.hpp"
 #include "device_common.hpp"
 
@@ -27,9 +32,16 @@ constexpr int kThreads = 256;
 
 struct DwArgs {
     int C, R, S, P, Q, sw, dw, pitch;
-    FastDiv fdQ, fdP, fdC;
-    int64_t total;
+    int relu, pool, Po, Qo;         // epilogue; output extent (P/2 x Q/2 with pool)
+    FastDiv fdQo, fdPo, fdC;
+    int64_t total;                  // outputs
 };
+
+// Bias, then the optional ReLU (maxNum against 0).
+__device__ __forceinline__ float act(float v, float b, int relu) {
+    v += b;
+    return relu ? fmaxf(v, 0.f) : v;
+}
 
 template <typename TIn, typename TOut>
 __global__ __launch_bounds__(kThreads) void conv_dw_generic_kernel(
@@ -38,31 +50,43 @@ __global__ __launch_bounds__(kThreads) void conv_dw_generic_kernel(
     int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (idx >= a.total) return;
     uint32_t t = (uint32_t)idx;
-    uint32_t t1 = fdiv(t, a.fdQ);
-    int wo = t - t1 * a.Q;
-    uint32_t t2 = fdiv(t1, a.fdP);
-    int h = t1 - t2 * a.P;
-    uint32_t n = fdiv(t2, a.fdC);
-    int c = t2 - n * a.C;
-    const TIn* row = xw + (((size_t)n * a.C + c) * a.P + h) * a.pitch + (size_t)wo * a.sw * a.R;
+    uint32_t t1 = fdiv(t, a.fdQo);
+    const int wo2 = t - t1 * a.Qo;
+    uint32_t nc = fdiv(t1, a.fdPo);
+    const int h2 = t1 - nc * a.Po;
+    const int c = nc - fdiv(nc, a.fdC) * a.C;
     const TIn* f = w + (size_t)c * a.R * a.S;
-    float acc = 0.f;
-    for (int q = 0; q < a.S; ++q)
-        for (int r = 0; r < a.R; ++r)
-            acc = fmaf(to_f32(row[q * a.dw * a.R + r]), to_f32(f[r * a.S + q]), acc);
-    if (bias) acc += to_f32(bias[c]);
-    y[idx] = from_f32<TOut>(acc);
+    const float b = bias ? to_f32(bias[c]) : 0.f;
+    // one output, or the four of its 2x2 region with the pool
+    const int side = a.pool ? 2 : 1;
+    float m = 0.f;
+    for (int dy = 0; dy < side; ++dy)
+        for (int dx = 0; dx < side; ++dx) {
+            const int h = h2 * side + dy, wo = wo2 * side + dx;
+            const TIn* row = xw + ((size_t)nc * a.P + h) * a.pitch + (size_t)wo * a.sw * a.R;
+            float acc = 0.f;
+            for (int q = 0; q < a.S; ++q)
+                for (int r = 0; r < a.R; ++r)
+                    acc = fmaf(to_f32(row[q * a.dw * a.R + r]), to_f32(f[r * a.S + q]), acc);
+            const float v = act(acc, b, a.relu);
+            m = (dy | dx) ? fmaxf(m, v) : v;
+        }
+    y[idx] = from_f32<TOut>(m);
 }
 
 // ----------------------------------------------------------- block kernel
+// Work unit: one output row (n, c, h) -- one pooled row (n, c, j), which
+// reads window rows 2j and 2j + 1, with the pool.
 struct DwBlockArgs {
     int C, P, Q, pitch, sw, dw;
-    int rows_per_block;      // window rows (= output rows) per workgroup
-    uint32_t rows;           // total rows of the chunk: n_images * C * P
-    FastDiv fdQ, fdP, fdC;
+    int units_per_block;     // output rows per workgroup
+    uint32_t units;          // output rows of the chunk: n_images * C * Po
+    int relu, pool, Po, Qo;
+    FastDiv fdQo, fdPo, fdC;
 };
 
 constexpr int kDwLdsBytes = 16384;
+constexpr int kDwMaxCh = 64;                            // channels one block may span
 
 template <typename TIn, typename TOut, int R, int S>
 __global__ __launch_bounds__(kThreads) void conv_dw_block_kernel(
@@ -70,24 +94,31 @@ __global__ __launch_bounds__(kThreads) void conv_dw_block_kernel(
     TOut* __restrict__ y, DwBlockArgs a) {
     constexpr int V = 16 / sizeof(TIn);
     constexpr int T = R * S;
-    constexpr int kMaxCh = 64;                          // channels one block may span
     __shared__ __align__(16) TIn tile[kDwLdsBytes / sizeof(TIn)];
-    __shared__ float filt[kMaxCh * T + kMaxCh];
+    __shared__ float filt[kDwMaxCh * T + kDwMaxCh];
 
-    const uint32_t r0 = blockIdx.x * (uint32_t)a.rows_per_block;
-    const int nrows = min((uint32_t)a.rows_per_block, a.rows - r0);
+    const uint32_t u0 = blockIdx.x * (uint32_t)a.units_per_block;
+    const int nu = min((uint32_t)a.units_per_block, a.units - u0);
+    // first window row of unit u: its own row, or row 2j of its plane
+    auto first_row = [&](uint32_t u) -> uint32_t {
+        if (!a.pool) return u;
+        const uint32_t nc = fdiv(u, a.fdPo);
+        return nc * a.P + 2 * (u - nc * a.Po);
+    };
+    const uint32_t r_lo = first_row(u0);
+    const int nrows = first_row(u0 + nu - 1) + (a.pool ? 2 : 1) - r_lo;   // <= LDS rows (host-checked)
 
     // 1. the block's window rows are one contiguous run: copy it with
     //    16-byte loads, consecutive threads on consecutive 16 bytes
     const int nvec = nrows * a.pitch / V;
-    const uint4* src = reinterpret_cast<const uint4*>(xw + (size_t)r0 * a.pitch);
+    const uint4* src = reinterpret_cast<const uint4*>(xw + (size_t)r_lo * a.pitch);
     uint4* dstv = reinterpret_cast<uint4*>(tile);
     for (int i = threadIdx.x; i < nvec; i += kThreads) dstv[i] = src[i];
 
     // 2. filters and biases of the channels the block spans
-    const uint32_t nc_first = fdiv(r0, a.fdP);
-    const uint32_t nc_last = fdiv(r0 + nrows - 1, a.fdP);
-    const int nch = nc_last - nc_first + 1;             // <= kMaxCh (host-checked)
+    const uint32_t nc_first = fdiv(u0, a.fdPo);
+    const uint32_t nc_last = fdiv(u0 + nu - 1, a.fdPo);
+    const int nch = nc_last - nc_first + 1;             // <= kDwMaxCh (host-checked)
     for (int i = threadIdx.x; i < nch * T; i += kThreads) {
         const uint32_t ncx = nc_first + i / T;
         const int c = ncx - fdiv(ncx, a.fdC) * a.C;
@@ -96,48 +127,78 @@ __global__ __launch_bounds__(kThreads) void conv_dw_block_kernel(
     for (int i = threadIdx.x; i < nch; i += kThreads) {
         const uint32_t ncx = nc_first + i;
         const int c = ncx - fdiv(ncx, a.fdC) * a.C;
-        filt[kMaxCh * T + i] = bias ? to_f32(bias[c]) : 0.f;
+        filt[kDwMaxCh * T + i] = bias ? to_f32(bias[c]) : 0.f;
     }
     __syncthreads();
 
     // 3. outputs of the block, contiguous in y: consecutive threads take
     //    consecutive outputs (adjacent columns read window elements R*SW
     //    apart, an odd stride for odd R and SW: no bank conflicts)
-    const int nout = nrows * a.Q;
-    TOut* yb = y + (size_t)r0 * a.Q;
+    const int nout = nu * a.Qo;
+    TOut* yb = y + (size_t)u0 * a.Qo;
     for (int o = threadIdx.x; o < nout; o += kThreads) {
-        const uint32_t rl = fdiv(o, a.fdQ);
-        const int wo = o - rl * a.Q;
-        const int cl = fdiv(r0 + rl, a.fdP) - nc_first;
-        const TIn* row = tile + rl * a.pitch + wo * a.sw * R;
+        const uint32_t ul = fdiv(o, a.fdQo);
+        const int wo2 = o - ul * a.Qo;
+        const uint32_t u = u0 + ul;
+        const int cl = fdiv(u, a.fdPo) - nc_first;
+        const int tr = first_row(u) - r_lo;
         const float* f = filt + cl * T;
-        float acc = 0.f;
+        const float b = filt[kDwMaxCh * T + cl];
+        auto dot = [&](int trow, int wo) {
+            const TIn* row = tile + trow * a.pitch + wo * a.sw * R;
+            float acc = 0.f;
 #pragma unroll
-        for (int q = 0; q < S; ++q)
+            for (int q = 0; q < S; ++q)
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc = fmaf(to_f32(row[q * a.dw * R + r]), f[r * S + q], acc);
-        yb[o] = from_f32<TOut>(acc + filt[kMaxCh * T + cl]);
+                for (int r = 0; r < R; ++r) acc = fmaf(to_f32(row[q * a.dw * R + r]), f[r * S + q], acc);
+            return act(acc, b, a.relu);
+        };
+        float v;
+        if (a.pool) {
+            v = fmaxf(fmaxf(dot(tr, 2 * wo2), dot(tr, 2 * wo2 + 1)),
+                      fmaxf(dot(tr + 1, 2 * wo2), dot(tr + 1, 2 * wo2 + 1)));
+        } else {
+            v = dot(tr, wo2);
+        }
+        yb[o] = from_f32<TOut>(v);
     }
 }
 
+// Output rows per workgroup such that the window rows they read fit the
+// LDS tile and span at most kDwMaxCh channels; 0 if not even one fits.
+int dw_units_per_block(const Geom& g, const Epi& epi, int64_t row_bytes) {
+    const int64_t rpb = kDwLdsBytes / row_bytes;        // window rows the tile holds
+    if (!epi.pool) {
+        const int64_t cap = (int64_t)(kDwMaxCh - 2) * g.P;   // spans <= cap/P + 2 channels
+        return (int)std::min(rpb, cap);
+    }
+    // pooled rows u .. u + n - 1 read 2n window rows, plus the skipped last
+    // row of every plane they cross when P is odd (at most (n + Po - 2) / Po)
+    const int Po = g.P / 2;
+    for (int64_t n = std::min<int64_t>(rpb / 2, (int64_t)(kDwMaxCh - 2) * Po); n >= 1; --n) {
+        const int64_t crossings = (n + Po - 2) / Po;
+        if (2 * n + (g.P & 1) * crossings <= rpb) return (int)n;
+    }
+    return 0;
+}
+
 template <typename TIn, typename TOut, int R, int S>
-hipError_t launch_block(const Geom& g, const void* xw, const void* w, const void* bias, void* y,
-                        int n_images, hipStream_t st) {
+hipError_t launch_block(const Geom& g, const Epi& epi, int upb, const void* xw, const void* w,
+                        const void* bias, void* y, int n_images, hipStream_t st) {
     DwBlockArgs a;
     a.C = g.C; a.P = g.P; a.Q = g.Q; a.pitch = g.pitchA; a.sw = g.sw; a.dw = g.dw;
-    const int64_t rows = (int64_t)n_images * g.C * g.P;
-    if (rows >= (1ll << 31)) return hipErrorInvalidValue;
-    a.rows = (uint32_t)rows;
-    const int64_t row_bytes = (int64_t)g.pitchA * sizeof(TIn);
-    int rpb = (int)(kDwLdsBytes / row_bytes);
-    // a block spans at most rpb/P + 2 channels; keep that within 64
-    const int max_rows_for_ch = (64 - 2) * g.P;
-    if (rpb > max_rows_for_ch) rpb = max_rows_for_ch;
-    a.rows_per_block = rpb;
-    a.fdQ = make_fastdiv(g.Q);
-    a.fdP = make_fastdiv(g.P);
+    a.relu = epi.relu;
+    a.pool = epi.pool;
+    a.Po = out_rows(g, epi);
+    a.Qo = out_cols(g, epi);
+    const int64_t units = (int64_t)n_images * g.C * a.Po;
+    if (units >= (1ll << 31)) return hipErrorInvalidValue;
+    a.units = (uint32_t)units;
+    a.units_per_block = upb;
+    a.fdQo = make_fastdiv(a.Qo);
+    a.fdPo = make_fastdiv(a.Po);
     a.fdC = make_fastdiv(g.C);
-    const int64_t blocks = (rows + rpb - 1) / rpb;
+    const int64_t blocks = (units + upb - 1) / upb;
     hipLaunchKernelGGL((conv_dw_block_kernel<TIn, TOut, R, S>), dim3((uint32_t)blocks),
                        dim3(kThreads), 0, st, (const TIn*)xw, (const TIn*)w, (const TIn*)bias,
                        (TOut*)y, a);
@@ -145,15 +206,19 @@ hipError_t launch_block(const Geom& g, const void* xw, const void* w, const void
 }
 
 template <typename TIn, typename TOut>
-hipError_t launch_generic(const Geom& g, const void* xw, const void* w, const void* bias, void* y,
-                          int n_images, hipStream_t st) {
+hipError_t launch_generic(const Geom& g, const Epi& epi, const void* xw, const void* w,
+                          const void* bias, void* y, int n_images, hipStream_t st) {
     DwArgs a;
     a.C = g.C; a.R = g.R; a.S = g.S; a.P = g.P; a.Q = g.Q;
     a.sw = g.sw; a.dw = g.dw; a.pitch = g.pitchA;
-    a.fdQ = make_fastdiv(g.Q);
-    a.fdP = make_fastdiv(g.P);
+    a.relu = epi.relu;
+    a.pool = epi.pool;
+    a.Po = out_rows(g, epi);
+    a.Qo = out_cols(g, epi);
+    a.fdQo = make_fastdiv(a.Qo);
+    a.fdPo = make_fastdiv(a.Po);
     a.fdC = make_fastdiv(g.C);
-    a.total = (int64_t)n_images * g.C * g.P * g.Q;
+    a.total = (int64_t)n_images * g.C * a.Po * a.Qo;
     if (a.total >= (1ll << 31)) return hipErrorInvalidValue;
     uint32_t blocks = (uint32_t)((a.total + kThreads - 1) / kThreads);
     hipLaunchKernelGGL((conv_dw_generic_kernel<TIn, TOut>), dim3(blocks), dim3(kThreads), 0, st,
@@ -165,30 +230,31 @@ hipError_t launch_generic(const Geom& g, const void* xw, const void* w, const vo
 // go to the generic kernel.
 template <typename TIn, typename TOut>
 hipError_t launch_t(const Geom& g, const void* xw, const void* w, const void* bias, void* y,
-                    int n_images, bool generic, hipStream_t st) {
+                    int n_images, bool generic, const Epi& epi, hipStream_t st) {
     if (n_images == 0) return hipSuccess;
-    const bool fits = (int64_t)g.pitchA * (int64_t)sizeof(TIn) <= kDwLdsBytes;
-    if (!generic && fits) {
-        if (g.R == 3 && g.S == 3) return launch_block<TIn, TOut, 3, 3>(g, xw, w, bias, y, n_images, st);
-        if (g.R == 5 && g.S == 5) return launch_block<TIn, TOut, 5, 5>(g, xw, w, bias, y, n_images, st);
-        if (g.R == 7 && g.S == 7) return launch_block<TIn, TOut, 7, 7>(g, xw, w, bias, y, n_images, st);
-        if (g.R == 1 && g.S == 1) return launch_block<TIn, TOut, 1, 1>(g, xw, w, bias, y, n_images, st);
+    const int upb = dw_units_per_block(g, epi, (int64_t)g.pitchA * (int64_t)sizeof(TIn));
+    if (!generic && upb > 0) {
+#define CIW_DW(RR, SS)                                                                         \
+        if (g.R == RR && g.S == SS)                                                            \
+            return launch_block<TIn, TOut, RR, SS>(g, epi, upb, xw, w, bias, y, n_images, st);
+        CIW_DW(3, 3) CIW_DW(5, 5) CIW_DW(7, 7) CIW_DW(1, 1)
+#undef CIW_DW
     }
-    return launch_generic<TIn, TOut>(g, xw, w, bias, y, n_images, st);
+    return launch_generic<TIn, TOut>(g, epi, xw, w, bias, y, n_images, st);
 }
 
 }  // namespace
 
 hipError_t launch_conv_dw(const Geom& g, ciw_dtype in, ciw_dtype out, const void* xw,
                           const void* w, const void* bias, void* y, int n_images,
-                          bool generic, hipStream_t st) {
-    if (in == CIW_F32) return launch_t<float, float>(g, xw, w, bias, y, n_images, generic, st);
+                          bool generic, const Epi& epi, hipStream_t st) {
+    if (in == CIW_F32) return launch_t<float, float>(g, xw, w, bias, y, n_images, generic, epi, st);
     if (in == CIW_F16)
         return out == CIW_F32
-                   ? launch_t<half_t, float>(g, xw, w, bias, y, n_images, generic, st)
-                   : launch_t<half_t, half_t>(g, xw, w, bias, y, n_images, generic, st);
-    return out == CIW_F32 ? launch_t<bf16_t, float>(g, xw, w, bias, y, n_images, generic, st)
-                          : launch_t<bf16_t, bf16_t>(g, xw, w, bias, y, n_images, generic, st);
+                   ? launch_t<half_t, float>(g, xw, w, bias, y, n_images, generic, epi, st)
+                   : launch_t<half_t, half_t>(g, xw, w, bias, y, n_images, generic, epi, st);
+    return out == CIW_F32 ? launch_t<bf16_t, float>(g, xw, w, bias, y, n_images, generic, epi, st)
+                          : launch_t<bf16_t, bf16_t>(g, xw, w, bias, y, n_images, generic, epi, st);
 }
 
 }  // namespace ciw

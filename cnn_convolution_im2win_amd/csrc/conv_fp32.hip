@@ -27,6 +27,13 @@
 //
 // Generic kernel: any filter size, stride and dilation; one thread computes
 // kTK output channels of one pixel.
+//
+// Fused epilogue (bias, optional ReLU, optional 2x2 max-pool).  The max is
+// not linear, so it is taken where the whole channel sum is known: in the
+// fast kernel's registers (a row group is the two rows of a pooled row, a
+// column tile an even run of columns), in the generic kernel's thread
+// (which computes the four outputs of its region), or in the split
+// reduction, which reads the four pixels' partial sums.
 #include <algorithm>
 #include <cmath>
 
@@ -44,9 +51,16 @@ constexpr int kWaves = 4;       // waves per workgroup (fast kernel)
 struct Fp32Args {
     int C, K, R, S, P, Q, sw, dw, pitch;
     int n_images, splits, c_per_split, kgroups;
-    FastDiv fdPQ, fdKg, fdQ, fdSplit;
+    int relu, pool, Po, Qo;          // epilogue; output extent
+    FastDiv fdPQo, fdKg, fdQo, fdSplit;
     int64_t total;   // threads doing work
 };
+
+// Bias, then the optional ReLU (maxNum against 0).
+__device__ __forceinline__ float act(float v, float b, int relu) {
+    v += b;
+    return relu ? fmaxf(v, 0.f) : v;
+}
 
 __global__ __launch_bounds__(kThreads) void conv_fp32_generic_kernel(
     const float* __restrict__ xw, const float* __restrict__ w, const float* __restrict__ bias,
@@ -54,50 +68,60 @@ __global__ __launch_bounds__(kThreads) void conv_fp32_generic_kernel(
     int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (idx >= a.total) return;
     const int PQ = a.P * a.Q;
+    const int PQo = a.Po * a.Qo;
     uint32_t t = (uint32_t)idx;
-    uint32_t t1 = fdiv(t, a.fdPQ);
-    int pix = t - t1 * PQ;
+    uint32_t t1 = fdiv(t, a.fdPQo);
+    const int opix = t - t1 * PQo;               // output pixel
     uint32_t t2 = fdiv(t1, a.fdKg);
     int kg = t1 - t2 * a.kgroups;
     uint32_t n = fdiv(t2, a.fdSplit);
     int sidx = t2 - n * a.splits;
-    int h = fdiv(pix, a.fdQ);
-    int wo = pix - h * a.Q;
+    const int h2 = fdiv(opix, a.fdQo);
+    const int w2 = opix - h2 * a.Qo;
 
     const int k0 = kg * kTK;
     const int c_begin = sidx * a.c_per_split;
     const int c_end = min(a.C, c_begin + a.c_per_split);
     const int RS = a.R * a.S;
-    float acc[kTK];
+    // one pixel, or the four of the output's 2x2 region with the pool
+    const int side = a.pool ? 2 : 1;
+    float m[kTK];
+    for (int sub = 0; sub < side * side; ++sub) {
+        const int h = h2 * side + (sub >> 1);
+        const int wo = w2 * side + (sub & 1);
+        float acc[kTK];
 #pragma unroll
-    for (int i = 0; i < kTK; ++i) acc[i] = 0.f;
-
-    for (int c = c_begin; c < c_end; ++c) {
-        const float* row = xw + (((size_t)n * a.C + c) * a.P + h) * a.pitch +
-                           (size_t)wo * a.sw * a.R;
-        for (int q = 0; q < a.S; ++q) {
-            const float* col = row + q * a.dw * a.R;
-            for (int r = 0; r < a.R; ++r) {
-                float v = col[r];
+        for (int i = 0; i < kTK; ++i) acc[i] = 0.f;
+        for (int c = c_begin; c < c_end; ++c) {
+            const float* row = xw + (((size_t)n * a.C + c) * a.P + h) * a.pitch +
+                               (size_t)wo * a.sw * a.R;
+            for (int q = 0; q < a.S; ++q) {
+                const float* col = row + q * a.dw * a.R;
+                for (int r = 0; r < a.R; ++r) {
+                    float v = col[r];
 #pragma unroll
-                for (int i = 0; i < kTK; ++i) {
-                    int k = min(k0 + i, a.K - 1);
-                    acc[i] = fmaf(v, w[((size_t)k * a.C + c) * RS + r * a.S + q], acc[i]);
+                    for (int i = 0; i < kTK; ++i) {
+                        int k = min(k0 + i, a.K - 1);
+                        acc[i] = fmaf(v, w[((size_t)k * a.C + c) * RS + r * a.S + q], acc[i]);
+                    }
                 }
             }
         }
-    }
 #pragma unroll
-    for (int i = 0; i < kTK; ++i) {
-        int k = k0 + i;
-        if (k >= a.K) break;
-        if (a.splits == 1) {
-            float v = acc[i];
-            if (bias) v += bias[k];
-            out[(((size_t)n * a.K + k) * PQ) + pix] = v;
-        } else {
-            out[((((size_t)sidx * a.n_images + n) * PQ) + pix) * a.K + k] = acc[i];
+        for (int i = 0; i < kTK; ++i) {
+            const int k = min(k0 + i, a.K - 1);
+            if (a.splits == 1) {
+                const float v = act(acc[i], bias ? bias[k] : 0.f, a.relu);
+                m[i] = sub ? fmaxf(m[i], v) : v;
+            } else if (k0 + i < a.K) {
+                out[((((size_t)sidx * a.n_images + n) * PQ) + h * a.Q + wo) * a.K + k] = acc[i];
+            }
         }
+    }
+    if (a.splits == 1) {
+#pragma unroll
+        for (int i = 0; i < kTK; ++i)
+            if (k0 + i < a.K) out[(((size_t)n * a.K + k0 + i) * PQo) + opix] = m[i];
     }
 }
 
@@ -107,9 +131,12 @@ __global__ __launch_bounds__(kThreads) void conv_fp32_generic_kernel(
 // registers for more resident waves; measured faster than 3 or 4 on the
 // 13x13 and 32x32 layers even though each filter tap then serves 2 rows.
 constexpr int kRW = 2;
+static_assert(kRW >= 2, "a pooled row group holds the two rows of its region");
 
 struct KlArgs {
     int C, K, P, Q, pitch;
+    int Qc;                        // columns computed: Q, or 2 (Q / 2) with the pool
+    int Po, Qo;                    // output extent
     int col_tiles, kblocks, splits, c_per_split, row_groups;
     FastDiv fdN, fdKb, fdTiles, fdRg;
     int n_images;
@@ -129,7 +156,7 @@ struct KlShape {
 // waves share out (wave w takes every fourth channel).  A lane loads its
 // R*S filter taps of a channel once and applies them to all its rows, so
 // the filter stream is read once per row group rather than once per row.
-template <int R, int S, int SW, int TN>
+template <int R, int S, int SW, int TN, bool RELU, bool POOL>
 __global__ __launch_bounds__(kThreads) void conv_fp32_klanes_kernel(
     const float* __restrict__ xw, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ out, KlArgs a) {
@@ -161,14 +188,16 @@ __global__ __launch_bounds__(kThreads) void conv_fp32_klanes_kernel(
     const int k = kb * 64 + lane;
     const int kk = min(k, a.K - 1);
 
-    // rows [h0, h0 + nrows): the P rows split evenly over the row groups
-    const int h0 = rg * a.P / a.row_groups;
-    const int nrows = (rg + 1) * a.P / a.row_groups - h0;   // 1 .. kRW
+    // rows [h0, h0 + nrows): the P rows split evenly over the row groups;
+    // with the pool, row group j is rows 2j and 2j + 1
+    const int h0 = POOL ? 2 * rg : rg * a.P / a.row_groups;
+    const int nrows = POOL ? 2 : (rg + 1) * a.P / a.row_groups - h0;   // 1 .. kRW
 
-    // the last tile is shifted left so it ends at column Q (its leading
-    // columns repeat the previous tile's and are not stored)
+    // the last tile is shifted left so it ends at column Qc (its leading
+    // columns repeat the previous tile's and are not stored); with the pool
+    // TN and Qc are even, so tiles start on even columns
     const int w_store = tile * TN;
-    const int w0 = min(w_store, a.Q - TN);
+    const int w0 = min(w_store, a.Qc - TN);
 
     const int c_begin = sidx * a.c_per_split;
     const int c_end = min(a.C, c_begin + a.c_per_split);
@@ -227,11 +256,13 @@ __global__ __launch_bounds__(kThreads) void conv_fp32_klanes_kernel(
             const int h = h0 + rr;
             if (k < a.K) {
                 if (a.splits == 1) {
-                    const float b = bias ? bias[k] : 0.f;
-                    float* yp = out + ((size_t)n * a.K + k) * PQ + h * a.Q + w0;
+                    if (!POOL) {
+                        const float b = bias ? bias[k] : 0.f;
+                        float* yp = out + ((size_t)n * a.K + k) * PQ + h * a.Q + w0;
 #pragma unroll
-                    for (int t = 0; t < TN; ++t)
-                        if (w0 + t >= w_store) yp[t] = acc[rr][t] + b;
+                        for (int t = 0; t < TN; ++t)
+                            if (w0 + t >= w_store) yp[t] = act(acc[rr][t], b, RELU);
+                    }
                 } else {
                     // partial sums [slice][n][h][w][k]: output channels
                     // innermost, so the 64 lanes store one contiguous run
@@ -244,12 +275,23 @@ __global__ __launch_bounds__(kThreads) void conv_fp32_klanes_kernel(
         }
         __syncthreads();
     }
+    // pooled row rg: wave 0 holds both rows' full sums; columns 2t, 2t + 1
+    // of the tile form output column (w0 / 2) + t
+    if (POOL && a.splits == 1 && wave == 0 && k < a.K) {
+        const float b = bias ? bias[k] : 0.f;
+        float* yp = out + ((size_t)n * a.K + k) * a.Po * a.Qo + rg * a.Qo + w0 / 2;
+#pragma unroll
+        for (int t = 0; t < TN / 2; ++t)
+            if (w0 + 2 * t >= w_store)
+                yp[t] = fmaxf(fmaxf(act(acc[0][2 * t], b, RELU), act(acc[0][2 * t + 1], b, RELU)),
+                              fmaxf(act(acc[1][2 * t], b, RELU), act(acc[1][2 * t + 1], b, RELU)));
+    }
 }
 
 // y[n][k][pix] = bias[k] + sum over slices s (in order) of part[s][n][pix][k].
 __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, float* __restrict__ y,
-    uint32_t per_split, int splits, int PQ, int K, FastDiv fdK, FastDiv fdPQ) {
+    uint32_t per_split, int splits, int PQ, int K, int relu, FastDiv fdK, FastDiv fdPQ) {
     const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
     if (i >= per_split) return;
     float v = 0.f;
@@ -269,19 +311,51 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
     const int k = i - t * K;
     const uint32_t n = fdiv(t, fdPQ);
     const int pix = t - n * PQ;
-    if (bias) v += bias[k];
-    y[((size_t)n * K + k) * PQ + pix] = v;
+    y[((size_t)n * K + k) * PQ + pix] = act(v, bias ? bias[k] : 0.f, relu);
+}
+
+// Pooled form: output (n, k, j, i) adds the slices of each of the four
+// pixels (2j + dy, 2i + dx) in slice order, then bias, ReLU and the max.
+__global__ __launch_bounds__(kThreads) void split_reduce_pool_kernel(
+    const float* __restrict__ part, const float* __restrict__ bias, float* __restrict__ y,
+    uint32_t per_split, uint32_t total, int splits, int P, int Q, int Po, int Qo, int K,
+    int relu, FastDiv fdK, FastDiv fdQo, FastDiv fdPo) {
+    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= total) return;
+    const uint32_t t = fdiv(i, fdK);
+    const int k = i - t * K;
+    const uint32_t t2 = fdiv(t, fdQo);
+    const int i2 = t - t2 * Qo;
+    const uint32_t n = fdiv(t2, fdPo);
+    const int j = t2 - n * Po;
+    const float b = bias ? bias[k] : 0.f;
+    float m = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+        const int pix = (2 * j + (sub >> 1)) * Q + 2 * i2 + (sub & 1);
+        const float* pp = part + ((size_t)n * P * Q + pix) * K + k;
+        float v = 0.f;
+        for (int s = 0; s < splits; ++s) v += pp[(size_t)s * per_split];
+        v = act(v, b, relu);
+        m = sub ? fmaxf(m, v) : v;
+    }
+    y[((size_t)n * K + k) * Po * Qo + j * Qo + i2] = m;
 }
 
 // ------------------------------------------------------------------ planning
 typedef void (*KlKernel)(const float*, const float*, const float*, float*, KlArgs);
 
+// One variant per shape, compiled for each epilogue (index relu + 2 pool).
 struct KlVariant {
     int R, S, SW, TN;
-    KlKernel fn;
+    KlKernel fn[4];
 };
 
-#define CIW_KL(R, S, SW, TN) {R, S, SW, TN, conv_fp32_klanes_kernel<R, S, SW, TN>}
+#define CIW_KL(R, S, SW, TN)                                                                   \
+    {R, S, SW, TN, {conv_fp32_klanes_kernel<R, S, SW, TN, false, false>,                     \
+                    conv_fp32_klanes_kernel<R, S, SW, TN, true, false>,                      \
+                    conv_fp32_klanes_kernel<R, S, SW, TN, false, true>,                      \
+                    conv_fp32_klanes_kernel<R, S, SW, TN, true, true>}}
 // Column-tile widths per filter shape: the scalar window segment
 // ((TN-1)*SW + S)*R stays at or below 60 registers.
 const KlVariant kKlVariants[] = {
@@ -304,13 +378,15 @@ struct Fp32Plan {
 };
 
 // The fast kernel's variant for this shape: the tile width that wastes the
-// fewest recomputed columns (ties: the widest).
-const KlVariant* pick_variant(const Geom& g) {
+// fewest recomputed columns (ties: the widest).  Pooled layers need an even
+// width, so that tiles cover whole 2x2 regions.
+const KlVariant* pick_variant(const Geom& g, bool even) {
     if (g.dw != 1) return nullptr;
     const KlVariant* best = nullptr;
     int64_t best_cols = 0;
     for (const KlVariant& v : kKlVariants) {
         if (v.R != g.R || v.S != g.S || v.SW != g.sw || v.TN > g.Q) continue;
+        if (even && (v.TN & 1)) continue;
         int64_t cols = (int64_t)((g.Q + v.TN - 1) / v.TN) * v.TN;
         if (!best || cols < best_cols || (cols == best_cols && v.TN > best->TN)) {
             best = &v;
@@ -363,18 +439,30 @@ int fast_splits(const Geom& g, const KlVariant& v, int n_images, int col_tiles, 
     return best;
 }
 
-Fp32Plan plan(const Geom& g, int n_images, bool generic) {
+// The fast kernel works on the pixels that reach an output: all of them, or
+// with the pool the 2 (P / 2) x 2 (Q / 2) that the regions cover.
+Geom computed_region(const Geom& g, const Epi& epi) {
+    Geom c = g;
+    if (epi.pool) {
+        c.P = 2 * (g.P / 2);
+        c.Q = 2 * (g.Q / 2);
+    }
+    return c;
+}
+
+Fp32Plan plan(const Geom& g, int n_images, bool generic, const Epi& epi) {
     Fp32Plan p{};
-    p.kl = generic ? nullptr : pick_variant(g);
+    const Geom gc = computed_region(g, epi);
+    p.kl = generic ? nullptr : pick_variant(gc, epi.pool);
     if (!p.kl) {
         p.splits = generic_splits(g, n_images);
         p.c_per_split = (g.C + p.splits - 1) / p.splits;
         return p;
     }
-    p.col_tiles = (g.Q + p.kl->TN - 1) / p.kl->TN;
+    p.col_tiles = (gc.Q + p.kl->TN - 1) / p.kl->TN;
     p.kblocks = (g.K + 63) / 64;
-    p.row_groups = (g.P + kRW - 1) / kRW;
-    const int s = fast_splits(g, *p.kl, n_images, p.col_tiles, p.kblocks, p.row_groups);
+    p.row_groups = epi.pool ? gc.P / 2 : (g.P + kRW - 1) / kRW;
+    const int s = fast_splits(gc, *p.kl, n_images, p.col_tiles, p.kblocks, p.row_groups);
     p.c_per_split = (g.C + s - 1) / s;
     p.splits = (g.C + p.c_per_split - 1) / p.c_per_split;
     return p;
@@ -385,16 +473,19 @@ Fp32Plan plan(const Geom& g, int n_images, bool generic) {
 int fp32_splits(const Geom& g, int n_images) {
     // partial-sum slices the workspace must hold: the larger of the two
     // kernels' plans, so either may run in a workspace sized by this
-    int a = plan(g, n_images, false).splits;
-    int b = plan(g, n_images, true).splits;
+    // (without the epilogue: a pooled plan that wants more slices than fit
+    // is cut down to this count at launch)
+    int a = plan(g, n_images, false, Epi{}).splits;
+    int b = plan(g, n_images, true, Epi{}).splits;
     return a > b ? a : b;
 }
 
 hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, const float* bias,
                             float* y, int n_images, float* partials, int max_splits,
-                            bool generic, hipStream_t st) {
+                            bool generic, const Epi& epi, hipStream_t st) {
     if (n_images == 0) return hipSuccess;
-    Fp32Plan p = plan(g, n_images, generic);
+    Fp32Plan p = plan(g, n_images, generic, epi);
+    const int Po = out_rows(g, epi), Qo = out_cols(g, epi);
     if (max_splits <= 1) {   // single pass requested
         p.splits = 1;
         p.c_per_split = g.C;
@@ -407,6 +498,9 @@ hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, cons
     if (p.kl) {
         KlArgs a;
         a.C = g.C; a.K = g.K; a.P = g.P; a.Q = g.Q; a.pitch = g.pitchA;
+        a.Qc = epi.pool ? 2 * Qo : g.Q;
+        a.Po = Po;
+        a.Qo = Qo;
         a.col_tiles = p.col_tiles;
         a.kblocks = p.kblocks;
         a.splits = p.splits;
@@ -421,7 +515,7 @@ hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, cons
         if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
         a.xcd_per = (uint32_t)(blocks / 8);
         a.xcd_rem = (uint32_t)(blocks % 8);
-        hipLaunchKernelGGL(p.kl->fn, dim3((uint32_t)blocks), dim3(kThreads), 0, st, xw, w, bias,
+        hipLaunchKernelGGL(p.kl->fn[(epi.relu ? 1 : 0) + (epi.pool ? 2 : 0)], dim3((uint32_t)blocks), dim3(kThreads), 0, st, xw, w, bias,
                            dst, a);
     } else {
         Fp32Args a;
@@ -431,11 +525,15 @@ hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, cons
         a.splits = p.splits;
         a.c_per_split = p.c_per_split;
         a.kgroups = (g.K + kTK - 1) / kTK;
-        a.fdPQ = make_fastdiv(g.P * g.Q);
+        a.relu = epi.relu;
+        a.pool = epi.pool;
+        a.Po = Po;
+        a.Qo = Qo;
+        a.fdPQo = make_fastdiv(Po * Qo);
         a.fdKg = make_fastdiv(a.kgroups);
-        a.fdQ = make_fastdiv(g.Q);
+        a.fdQo = make_fastdiv(Qo);
         a.fdSplit = make_fastdiv(p.splits);
-        a.total = (int64_t)n_images * p.splits * a.kgroups * g.P * g.Q;
+        a.total = (int64_t)n_images * p.splits * a.kgroups * Po * Qo;
         if (a.total >= (1ll << 31)) return hipErrorInvalidValue;
         uint32_t blocks = (uint32_t)((a.total + kThreads - 1) / kThreads);
         hipLaunchKernelGGL(conv_fp32_generic_kernel, dim3(blocks), dim3(kThreads), 0, st, xw, w,
@@ -444,9 +542,17 @@ hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, cons
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t per_split = (int64_t)n_images * g.K * g.P * g.Q;
-    hipLaunchKernelGGL(split_reduce_kernel, dim3((uint32_t)((per_split + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, st, partials, bias, y, (uint32_t)per_split, p.splits,
-                       g.P * g.Q, g.K, make_fastdiv(g.K), make_fastdiv(g.P * g.Q));
+    if (epi.pool) {
+        const int64_t total = (int64_t)n_images * g.K * Po * Qo;
+        hipLaunchKernelGGL(split_reduce_pool_kernel, dim3((uint32_t)((total + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, st, partials, bias, y, (uint32_t)per_split,
+                           (uint32_t)total, p.splits, g.P, g.Q, Po, Qo, g.K, (int)epi.relu,
+                           make_fastdiv(g.K), make_fastdiv(Qo), make_fastdiv(Po));
+    } else {
+        hipLaunchKernelGGL(split_reduce_kernel, dim3((uint32_t)((per_split + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, st, partials, bias, y, (uint32_t)per_split, p.splits,
+                           g.P * g.Q, g.K, (int)epi.relu, make_fastdiv(g.K), make_fastdiv(g.P * g.Q));
+    }
     return hipGetLastError();
 }
 

@@ -7,10 +7,10 @@ namespace ciw {
 
 hipError_t launch_conv_mfma_f16(const Geom& g, ciw_dtype out, const void* xw, const void* w,
                                 const void* aperm, const void* bias, void* y, int n_images,
-                                bool generic, hipStream_t st);
+                                bool generic, const Epi& epi, hipStream_t st);
 hipError_t launch_conv_mfma_bf16(const Geom& g, ciw_dtype out, const void* xw, const void* w,
                                  const void* aperm, const void* bias, void* y, int n_images,
-                                 bool generic, hipStream_t st);
+                                 bool generic, const Epi& epi, hipStream_t st);
 
 size_t mfma_prep_bytes(const Geom& g) {
     MfRowPlan pl;
@@ -37,10 +37,10 @@ hipError_t launch_mfma_prep(const Geom& g, ciw_dtype out, const void* w, void* a
 
 hipError_t launch_conv_mfma(const Geom& g, ciw_dtype in, ciw_dtype out, const void* xw,
                             const void* w, const void* aperm, const void* bias, void* y,
-                            int n_images, bool generic, hipStream_t st) {
+                            int n_images, bool generic, const Epi& epi, hipStream_t st) {
     return in == CIW_F16
-               ? launch_conv_mfma_f16(g, out, xw, w, aperm, bias, y, n_images, generic, st)
-               : launch_conv_mfma_bf16(g, out, xw, w, aperm, bias, y, n_images, generic, st);
+               ? launch_conv_mfma_f16(g, out, xw, w, aperm, bias, y, n_images, generic, epi, st)
+               : launch_conv_mfma_bf16(g, out, xw, w, aperm, bias, y, n_images, generic, epi, st);
 }
 
 }  // namespace ciw

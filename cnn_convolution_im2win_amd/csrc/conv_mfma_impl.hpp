@@ -37,9 +37,16 @@ constexpr int kLdsRow = 40;   // 32 + 8 halves: rows 80 B apart
 
 struct MfmaArgs {
     int C, K, R, S, P, Q, sw, dw, pitch;
-    int T, RC, npix;
-    FastDiv fdRC, fdC, fdPQ, fdQ;
+    int T, RC, npix;                // npix: GEMM columns (4 per output with the pool)
+    int relu, pool, Po, Qo;         // epilogue; output extent
+    FastDiv fdRC, fdC, fdPQo, fdQo;
 };
+
+// Bias, then the optional ReLU (maxNum against 0).
+__device__ __forceinline__ float act(float v, float b, int relu) {
+    v += b;
+    return relu ? fmaxf(v, 0.f) : v;
+}
 
 template <typename TIn>
 __device__ __forceinline__ f32x4 mfma16x16x32(const uint16_t* a, const uint16_t* b, f32x4 acc);
@@ -62,7 +69,9 @@ __device__ __forceinline__ f32x4 mfma16x16x32<bf16_t>(const uint16_t* a, const u
 
 // Generic tile kernel: 64 output channels x 64 pixels per workgroup, four
 // waves each owning a 32x32 quadrant (2x2 MFMA tiles).  Operands go through
-// LDS one 32-wide reduction step at a time.
+// LDS one 32-wide reduction step at a time.  With the 2x2 max-pool, GEMM
+// column 4 o + d is pixel d of output o's region, so a region lies in four
+// neighbouring lanes and two lane exchanges give its max.
 template <typename TIn, typename TOut>
 __global__ __launch_bounds__(kThreads) void conv_mfma_generic_kernel(
     const uint16_t* __restrict__ xw, const uint16_t* __restrict__ w,
@@ -84,10 +93,14 @@ __global__ __launch_bounds__(kThreads) void conv_mfma_generic_kernel(
     // per-thread window base of its pixel (index precomputation)
     int64_t bbase = -1;
     if (pload < a.npix) {
-        uint32_t n = fdiv(pload, a.fdPQ);
-        int pix = pload - n * (a.P * a.Q);
-        int h = fdiv(pix, a.fdQ);
-        int wo = pix - h * a.Q;
+        const int side = a.pool ? 2 : 1;
+        const uint32_t o = a.pool ? (uint32_t)pload >> 2 : (uint32_t)pload;   // output index
+        uint32_t n = fdiv(o, a.fdPQo);
+        int opix = o - n * (a.Po * a.Qo);
+        int h2 = fdiv(opix, a.fdQo);
+        int w2 = opix - h2 * a.Qo;
+        int h = h2 * side + (a.pool ? (pload >> 1) & 1 : 0);
+        int wo = w2 * side + (a.pool ? pload & 1 : 0);
         bbase = ((int64_t)n * a.P + h) * a.pitch + (int64_t)wo * a.sw * a.RC;
     }
 
@@ -127,22 +140,27 @@ __global__ __launch_bounds__(kThreads) void conv_mfma_generic_kernel(
     }
 
     // epilogue: lane holds D[4*(lane/16) + i][lane % 16] of each 16x16 tile
-    const int PQ = a.P * a.Q;
+    const int PQo = a.Po * a.Qo;
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
-        int p = p0 + wn * 32 + ni * 16 + (lane & 15);
-        if (p >= a.npix) continue;
-        uint32_t n = fdiv(p, a.fdPQ);
-        int pix = p - n * PQ;
+        const int p = p0 + wn * 32 + ni * 16 + (lane & 15);
+        const uint32_t o = a.pool ? (uint32_t)p >> 2 : (uint32_t)p;
+        // every lane takes part in the exchanges; a region's four columns
+        // are all in range or all out (npix is a multiple of 4)
+        const bool store = p < a.npix && (!a.pool || (lane & 3) == 0);
+        uint32_t n = fdiv(o, a.fdPQo);
+        int opix = o - n * PQo;
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                int k = k0 + wm * 32 + mi * 16 + (lane >> 4) * 4 + i;
-                if (k >= a.K) continue;
-                float v = acc[mi][ni][i];
-                if (bias) v += to_f32(bias[k]);
-                y[((int64_t)n * a.K + k) * PQ + pix] = from_f32<TOut>(v);
+                const int k = k0 + wm * 32 + mi * 16 + (lane >> 4) * 4 + i;
+                float v = act(acc[mi][ni][i], (bias && k < a.K) ? to_f32(bias[k]) : 0.f, a.relu);
+                if (a.pool) {
+                    v = fmaxf(v, __shfl_xor(v, 1));
+                    v = fmaxf(v, __shfl_xor(v, 2));
+                }
+                if (store && k < a.K) y[((int64_t)n * a.K + k) * PQo + opix] = from_f32<TOut>(v);
             }
     }
 }
@@ -192,9 +210,11 @@ struct MfRowArgs {
     int nd;                        // row-copy instructions per thread per row
     int ostride;                   // LDS output tile row stride (elements of TOut)
     int vec_store;                 // output rows are whole 16-byte vectors
-    int ns;                        // output store instructions per thread per row
-    int rows;                      // N * P
-    FastDiv fdP;
+    int ns;                        // output store instructions per thread per output row
+    int rows;                      // row units: N * P, or N * 2 (P / 2) with the pool
+    int relu, pool;                // epilogue
+    int Po, Qo;                    // output extent (P / 2 x Q / 2 with the pool)
+    FastDiv fdPo;
 };
 
 constexpr int kMfMaxChunks = 8;    // 16-byte chunks per thread per row copy
@@ -285,6 +305,65 @@ __device__ __forceinline__ void put4<float>(float* p, float a0, float a1, float 
     *reinterpret_cast<float4*>(p) = make_float4(a0, a1, a2, a3);
 }
 
+// The two 16-bit outputs of a packed word, as floats (exact).
+template <typename TOut>
+__device__ __forceinline__ float2 unpack2(uint32_t u);
+
+template <>
+__device__ __forceinline__ float2 unpack2<half_t>(uint32_t u) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 h = __builtin_bit_cast(f16x2, u);
+    return make_float2((float)h[0], (float)h[1]);
+}
+
+template <>
+__device__ __forceinline__ float2 unpack2<bf16_t>(uint32_t u) {
+    return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+}
+
+// Two / four adjacent tile outputs read back as floats.
+template <typename TOut>
+__device__ __forceinline__ float2 get2(const TOut* p) {
+    return unpack2<TOut>(*reinterpret_cast<const uint32_t*>(p));
+}
+
+template <>
+__device__ __forceinline__ float2 get2<float>(const float* p) {
+    return *reinterpret_cast<const float2*>(p);
+}
+
+template <typename TOut>
+__device__ __forceinline__ float4 get4(const TOut* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    const float2 a = unpack2<TOut>(u.x), b = unpack2<TOut>(u.y);
+    return make_float4(a.x, a.y, b.x, b.y);
+}
+
+template <>
+__device__ __forceinline__ float4 get4<float>(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+}
+
+// 2x2 pooling, horizontal half: 2V adjacent outputs (the 16-byte vectors lo,
+// hi) to the V maxima of their pairs.  Values come from the output type, so
+// converting a maximum back is exact.
+template <typename TOut>
+__device__ __forceinline__ uint4 pool_pairs(uint4 lo, uint4 hi) {
+    auto word = [](uint32_t u0, uint32_t u1) {
+        const float2 a = unpack2<TOut>(u0), b = unpack2<TOut>(u1);
+        return pack2<TOut>(fmaxf(a.x, a.y), fmaxf(b.x, b.y));
+    };
+    return make_uint4(word(lo.x, lo.y), word(lo.z, lo.w), word(hi.x, hi.y), word(hi.z, hi.w));
+}
+
+template <>
+__device__ __forceinline__ uint4 pool_pairs<float>(uint4 lo, uint4 hi) {
+    auto m = [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+    };
+    return make_uint4(m(lo.x, lo.y), m(lo.z, lo.w), m(hi.x, hi.y), m(hi.z, hi.w));
+}
+
 // s_waitcnt with a run-time vector-memory count (the instruction takes an
 // immediate): wait until at most n of this wave's vector memory operations
 // are outstanding and all its LDS operations are done.
@@ -323,7 +402,8 @@ __device__ __forceinline__ void wg_barrier_lds() {
     wg_barrier();
 }
 
-template <typename TIn, typename TOut, int NSET, int STEPS, bool MASK, int PAD, bool TAILLAST>
+template <typename TIn, typename TOut, int NSET, int STEPS, bool MASK, int PAD, bool TAILLAST,
+          bool POOL>
 __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
     const uint16_t* __restrict__ xw, const uint16_t* __restrict__ aperm,
     const TIn* __restrict__ bias, TOut* __restrict__ y, MfRowArgs a) {
@@ -385,8 +465,17 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
     // 16 bytes at M0 + 16 i); the source is the row base (scalar) plus a
     // 32-bit byte offset per lane.
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)ring;
-    auto copy_row = [&](int row, int buf) {
-        const uint16_t* src = xw + (size_t)row * a.pitch;
+    // Row units: window rows in order, or with the pool the two rows 2j,
+    // 2j + 1 of each pooled output row (n, j) = u / 2 (an odd last row of
+    // an image reaches no output and is skipped).
+    auto window_row = [&](int u) -> int {
+        if (!POOL) return u;
+        const uint32_t pr = (uint32_t)u >> 1;
+        const uint32_t n = fdiv(pr, a.fdPo);
+        return (int)(n * a.P + 2 * (pr - n * a.Po)) + (u & 1);
+    };
+    auto copy_row = [&](int u, int buf) {
+        const uint16_t* src = xw + (size_t)window_row(u) * a.pitch;
         const uint32_t dst0 = ring_lds + 2u * (uint32_t)(buf * a.buf_elems) + 1024u * (uint32_t)wave;
 #pragma unroll
         for (int j = 0; j < kMfMaxChunks; ++j) {
@@ -400,11 +489,14 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
 
     // each workgroup takes a contiguous run of rows: neighbouring output
     // rows share cache lines, and one workgroup writing them back to back
-    // completes those lines while they are still in L2
-    const int rows_per = (a.rows + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int first = blockIdx.x * rows_per;
+    // completes those lines while they are still in L2.  With the pool the
+    // run is whole pairs, so both rows of a region meet in one workgroup.
+    const int unit = POOL ? 2 : 1;                       // row units per output row
+    const int groups = a.rows / unit;
+    const int per = (groups + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int first = blockIdx.x * per * unit;
     if (first >= a.rows) return;
-    const int my_rows = min(rows_per, a.rows - first);   // rows first .. first + my_rows - 1
+    const int my_rows = min(per * unit, a.rows - first);  // units first .. first + my_rows - 1
     for (int i = 0; i < a.nbuf - 1 && i < my_rows; ++i) copy_row(first + i, i);
     wg_barrier_lds();                // bias_l visible
     const float bias_k = bias_l[kh * 32 + ml];
@@ -434,27 +526,30 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
     // vectors, fixed for the kernel
     constexpr int V = 16 / sizeof(TOut);
     const int E = a.vec_store ? V : 1;          // elements per store
-    const int nq = a.Q / E;                     // stores per output row
+    const int nq = a.Qo / E;                    // stores per output row
     const int sk0 = tid / nq, sv0 = tid - sk0 * nq;
     const int dk = kThreads / nq, dv = kThreads - dk * nq;
+    const int sc = POOL ? 2 : 1;                // tile columns per output column
 
-    // ---- output row (n, h) from a tile: K rows of Q contiguous elements.
+    // ---- output row (n, h) from a tile: K rows of Qo contiguous elements.
+    // With the pool the tile already holds the max of the region's two rows
+    // and each output is the max of two neighbouring tile columns.
     // Exactly a.ns stores per thread (surplus threads repeat the last one);
     // each tile read is issued one store ahead of its use.
-    const int PQ = a.P * a.Q;
-    auto store_row = [&](int row, const TOut* tl) {
-        const uint32_t n = fdiv(row, a.fdP);
-        const int h = row - n * a.P;
-        TOut* yrow = y + (size_t)n * a.K * PQ + (size_t)h * a.Q;
+    const int PQo = a.Po * a.Qo;
+    auto store_row = [&](int orow_idx, const TOut* tl) {
+        const uint32_t n = fdiv(orow_idx, a.fdPo);
+        const int h = orow_idx - n * a.Po;
+        TOut* yrow = y + (size_t)n * a.K * PQo + (size_t)h * a.Qo;
         int k = sk0, v = sv0;
         // element offsets of store j in the tile (src) and in the output row
         // block (dst); advance to store j + 1
         int src, dst_k, dst_off;
         auto take = [&]() {
             const int kk = min(k, a.K - 1);
-            dst_off = kk < k ? (a.Q - E) : v * E;
+            dst_off = kk < k ? (a.Qo - E) : v * E;
             dst_k = kk;
-            src = kk * a.ostride + dst_off;
+            src = kk * a.ostride + sc * dst_off;
             k += dk;
             v += dv;
             if (v >= nq) {
@@ -462,27 +557,34 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
                 ++k;
             }
         };
+        auto vec_at = [&](int i) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(tl + i);
+            return POOL ? pool_pairs<TOut>(lo, *reinterpret_cast<const uint4*>(tl + i + V)) : lo;
+        };
+        auto elem_at = [&](int i) {
+            return POOL ? from_f32<TOut>(fmaxf(to_f32(tl[i]), to_f32(tl[i + 1]))) : tl[i];
+        };
         take();
         if (a.vec_store) {
-            uint4 cur = *reinterpret_cast<const uint4*>(tl + src);
+            uint4 cur = vec_at(src);
             for (int j = 0; j < a.ns; ++j) {
-                TOut* dp = yrow + (size_t)dst_k * PQ + dst_off;
+                TOut* dp = yrow + (size_t)dst_k * PQo + dst_off;
                 uint4 nxt = cur;
                 if (j + 1 < a.ns) {
                     take();
-                    nxt = *reinterpret_cast<const uint4*>(tl + src);
+                    nxt = vec_at(src);
                 }
                 *reinterpret_cast<uint4*>(dp) = cur;
                 cur = nxt;
             }
         } else {
-            TOut cur = tl[src];
+            TOut cur = elem_at(src);
             for (int j = 0; j < a.ns; ++j) {
-                TOut* dp = yrow + (size_t)dst_k * PQ + dst_off;
+                TOut* dp = yrow + (size_t)dst_k * PQo + dst_off;
                 TOut nxt = cur;
                 if (j + 1 < a.ns) {
                     take();
-                    nxt = tl[src];
+                    nxt = elem_at(src);
                 }
                 *dp = cur;
                 cur = nxt;
@@ -494,19 +596,38 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
     // into the buffer row it - 1 used (every wave is past it now), store
     // row it - 1 from its tile, then multiply row it into the other tile.
     // The stores thus overlap the next row's multiplies, and the barrier
-    // that makes row it visible also makes tile it - 1 complete.
+    // that makes row it visible also makes tile it - 1 complete.  With the
+    // pool a tile serves a pair of rows: the first writes it, the second
+    // takes the max with it in place (each lane rewrites exactly the
+    // entries it wrote), and the pair is stored while the next pair's first
+    // row multiplies into the other tile.
+    const int tile_elems = a.K * a.ostride;
+    // ReLU without a branch: maxNum against 0, or against a quiet NaN, which
+    // returns the other operand unchanged (a NaN sum stays NaN)
+    const float relu_lo = a.relu ? 0.f : __builtin_nanf("");
     for (int it = 0; it < my_rows; ++it) {
-        const int row = first + it;
         const int buf = it % a.nbuf;
         // wait for this row's copy: allow the copies of the rows after it
-        // and the output stores issued since it to stay in flight
+        // and the output stores issued since it (in iterations lo .. it - 1;
+        // a store follows every row, or every second row with the pool) to
+        // stay in flight
         const int later_rows = min(a.nbuf - 2, my_rows - 1 - it);
-        const int later_stores = max(0, it - max(it - a.nbuf + 1, 1));
+        const int lo = max(it - a.nbuf + 1, 1);
+        int later_stores = max(0, it - lo);
+        if (POOL) {
+            const int lo2 = max(lo, 2);
+            later_stores = it - 1 >= lo2 ? (it - 1) / 2 - (lo2 - 1) / 2 : 0;
+        }
         wait_vm_lgkm(a.nd * later_rows + a.ns * later_stores);
-        wg_barrier();                // row it landed; tile it - 1 complete and read by nobody
+        wg_barrier();                // row it landed; the tile to store is complete and free
         if (it + a.nbuf - 1 < my_rows) copy_row(first + it + a.nbuf - 1, (it + a.nbuf - 1) % a.nbuf);
-        if (it > 0) store_row(row - 1, otile0 + ((it - 1) & 1) * a.K * a.ostride);
-        TOut* otile = otile0 + (it & 1) * a.K * a.ostride;
+        if (!POOL) {
+            if (it > 0) store_row(first + it - 1, otile0 + ((it - 1) & 1) * tile_elems);
+        } else if (it >= 2 && (it & 1) == 0) {
+            store_row((first + it) / 2 - 1, otile0 + (((it >> 1) - 1) & 1) * tile_elems);
+        }
+        TOut* otile = otile0 + (POOL ? (it >> 1) & 1 : it & 1) * tile_elems;
+        const bool merge = POOL && (it & 1);   // second row of a pair
 
         const uint16_t* lb = ring + buf * a.buf_elems;
         // Pixel blocks pb = phase + nph * (32-pixel block): the wave takes
@@ -592,23 +713,37 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
             }
             // lane holds D[m][n] for channel n = lane % 32 and block pixel
             // m = 8 (i / 4) + 4 (lane / 32) + i % 4; pixels past the row end
-            // land in tile columns that are never stored
-            // (with kLean the bias is already in the sum; no "+ 0", which
-            // the compiler must keep for the sign of a zero sum)
-#define CIW_OUT(v) (kLean ? (v) : (v) + bias_k)
+            // land in tile columns that are never stored.  The bias (unless
+            // it seeded the sum: adding "+ 0" would not be free, the
+            // compiler must keep it for the sign of a zero sum), then ReLU.
+            if (!kLean) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[i] += bias_k;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = fmaxf(acc[i], relu_lo);
             const int k = kh * 32 + ml;
             if (NSET == 1) {
                 if (k < a.K) {
                     TOut* orow = otile + k * a.ostride + a.nph * 32 * mb + ph;
                     if (a.nph == 1) {
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            put4<TOut>(orow + 8 * q + 4 * g, CIW_OUT(acc[4 * q]), CIW_OUT(acc[4 * q + 1]),
-                                       CIW_OUT(acc[4 * q + 2]), CIW_OUT(acc[4 * q + 3]));
+                        for (int q = 0; q < 4; ++q) {
+                            TOut* tp = orow + 8 * q + 4 * g;
+                            float v0 = acc[4 * q], v1 = acc[4 * q + 1], v2 = acc[4 * q + 2], v3 = acc[4 * q + 3];
+                            if (merge) {
+                                const float4 o = get4<TOut>(tp);
+                                v0 = fmaxf(v0, o.x); v1 = fmaxf(v1, o.y); v2 = fmaxf(v2, o.z); v3 = fmaxf(v3, o.w);
+                            }
+                            put4<TOut>(tp, v0, v1, v2, v3);
+                        }
                     } else {
 #pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            orow[a.nph * (8 * (i >> 2) + 4 * g + (i & 3))] = from_f32<TOut>(CIW_OUT(acc[i]));
+                        for (int i = 0; i < 16; ++i) {
+                            TOut* tp = orow + a.nph * (8 * (i >> 2) + 4 * g + (i & 3));
+                            const float v = merge ? fmaxf(acc[i], to_f32(*tp)) : acc[i];
+                            *tp = from_f32<TOut>(v);
+                        }
                     }
                 }
             } else if ((j & 1) == 0) {
@@ -617,17 +752,27 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
                 // blocks j - 1 and j: phases ph - 1 and ph, neighbouring pixels
                 TOut* orow = otile + k * a.ostride + kNph * (32 * mb + 4 * g) + ph - 1;
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    put2<TOut>(orow + kNph * (8 * (i >> 2) + (i & 3)), CIW_OUT(accp[i]), CIW_OUT(acc[i]));
+                for (int i = 0; i < 16; ++i) {
+                    TOut* tp = orow + kNph * (8 * (i >> 2) + (i & 3));
+                    float v0 = accp[i], v1 = acc[i];
+                    if (merge) {
+                        const float2 o = get2<TOut>(tp);
+                        v0 = fmaxf(v0, o.x);
+                        v1 = fmaxf(v1, o.y);
+                    }
+                    put2<TOut>(tp, v0, v1);
+                }
             }
-#undef CIW_OUT
             }
         }
     }
-    // the last row's tile
+    // the last row's (pair's) tile
     wait_vm_lgkm_lds_only();
     wg_barrier();
-    store_row(first + my_rows - 1, otile0 + ((my_rows - 1) & 1) * a.K * a.ostride);
+    if (POOL)
+        store_row((first + my_rows) / 2 - 1, otile0 + (((my_rows >> 1) - 1) & 1) * tile_elems);
+    else
+        store_row(first + my_rows - 1, otile0 + ((my_rows - 1) & 1) * tile_elems);
 }
 
 // Filter layout for the row kernel, in the order the A fragments are
@@ -683,8 +828,11 @@ int gcd_int(int x, int y) {
     return x;
 }
 
-// Row-kernel plan; false when the layer does not fit it.
-bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl) {
+// Row-kernel plan; false when the layer does not fit it.  Whether a layer
+// fits without the epilogue decides whether the filter is re-laid out, so
+// an epilogue may only turn a fitting plan down (to the generic kernel),
+// never accept one the plain plan rejects.
+bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl, const Epi& epi = Epi{}) {
     if (g.K > 64 || g.dw != 1) return false;
     MfRowArgs& a = pl.a;
     const int D = g.sw * g.R * g.C;
@@ -754,13 +902,26 @@ bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl) {
                 break;
             }
     if (nbuf == 0) return false;
-    const int vec_store = (g.Q % V == 0 && ((int64_t)g.P * g.Q) % V == 0) ? 1 : 0;
-    const int64_t total = vec_store ? (int64_t)g.K * (g.Q / V) : (int64_t)g.K * g.Q;
-    const int ns = (int)((total + kThreads - 1) / kThreads);
+    // stores per thread of an output row of Qo columns (16-byte vectors when
+    // every output row starts on a vector)
+    auto stores = [&](int Po, int Qo, int& vec) {
+        vec = (Qo % V == 0 && ((int64_t)Po * Qo) % V == 0) ? 1 : 0;
+        const int64_t total = vec ? (int64_t)g.K * (Qo / V) : (int64_t)g.K * Qo;
+        return (int)((total + kThreads - 1) / kThreads);
+    };
     // the wait counts must fit the 6-bit vector-memory counter: a shorter
     // ring when the copies and stores of nbuf - 1 rows would not
+    const int nbuf_lds = nbuf;
+    int vec_store = 0;
+    int ns = stores(g.P, g.Q, vec_store);
     while (nbuf > 2 && (nd + ns) * (nbuf - 1) > 63) --nbuf;
     if ((nd + ns) * (nbuf - 1) > 63) return false;
+    if (epi.pool) {   // fewer, narrower output rows
+        ns = stores(g.P / 2, g.Q / 2, vec_store);
+        nbuf = nbuf_lds;
+        while (nbuf > 2 && (nd + ns) * (nbuf - 1) > 63) --nbuf;
+        if ((nd + ns) * (nbuf - 1) > 63) return false;
+    }
     const size_t lds = (size_t)nbuf * buf * 2 + tile;
     a.C = g.C; a.K = g.K; a.R = g.R; a.S = g.S; a.P = g.P; a.Q = g.Q;
     a.pitch = g.pitchB;
@@ -775,7 +936,11 @@ bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl) {
     a.ostride = ostride;
     a.vec_store = vec_store;
     a.ns = ns;
-    a.fdP = make_fastdiv(g.P);
+    a.relu = epi.relu;
+    a.pool = epi.pool;
+    a.Po = out_rows(g, epi);
+    a.Qo = out_cols(g, epi);
+    a.fdPo = make_fastdiv(a.Po);
     pl.nset = nset;
     pl.steps = steps;
     pl.pad = pad;
@@ -801,14 +966,14 @@ hipError_t allow_lds(const void* fn, int dev, size_t bytes) {
 
 // One compiled kernel: the tail-in-last-step form exists only for masked
 // plans (without masks it would be the same kernel).
-template <typename TIn, typename TOut, int NS, int M, bool MK, int PD>
+template <typename TIn, typename TOut, int NS, int M, bool MK, int PD, bool POOL>
 hipError_t launch_rows_one(const MfRowPlan& pl, int dev, int64_t grid, const void* xw,
                            const void* aperm, const void* bias, void* y, const MfRowArgs& a,
                            hipStream_t st) {
     void (*kfn)(const uint16_t*, const uint16_t*, const TIn*, TOut*, MfRowArgs) =
-        conv_mfma_rows_kernel<TIn, TOut, NS, M, MK, PD, false>;
+        conv_mfma_rows_kernel<TIn, TOut, NS, M, MK, PD, false, POOL>;
     if constexpr (MK) {
-        if (pl.tail_last) kfn = conv_mfma_rows_kernel<TIn, TOut, NS, M, MK, PD, true>;
+        if (pl.tail_last) kfn = conv_mfma_rows_kernel<TIn, TOut, NS, M, MK, PD, true, POOL>;
     }
     // more than 64 KB of dynamic LDS per workgroup must be allowed explicitly
     if (pl.lds_bytes > 65536 && allow_lds(reinterpret_cast<const void*>(kfn), dev, pl.lds_bytes) != hipSuccess)
@@ -818,11 +983,12 @@ hipError_t launch_rows_one(const MfRowPlan& pl, int dev, int64_t grid, const voi
     return hipSuccess;
 }
 
-template <typename TIn, typename TOut>
+template <typename TIn, typename TOut, bool POOL>
 hipError_t launch_rows(const Geom& g, MfRowPlan pl, const void* xw, const void* aperm,
                        const void* bias, void* y, int n_images, hipStream_t st) {
     MfRowArgs a = pl.a;
-    const int64_t rows = (int64_t)n_images * g.P;
+    // row units: every window row, or both rows of every pooled output row
+    const int64_t rows = (int64_t)n_images * (a.pool ? 2 * a.Po : g.P);
     if (rows >= (1ll << 31)) return hipErrorInvalidValue;
     a.rows = (int)rows;
     int dev = 0, cus = 256;
@@ -831,11 +997,13 @@ hipError_t launch_rows(const Geom& g, MfRowPlan pl, const void* xw, const void* 
         cus < 1)
         cus = 256;
     int64_t grid = (int64_t)cus * pl.wgs_per_cu;   // resident workgroups only
-    if (grid > rows) grid = rows;
+    const int64_t groups = a.pool ? rows / 2 : rows;   // runs are whole pairs with the pool
+    if (grid > groups) grid = groups;
 #define CIW_MF_LAUNCH(NS, M, MK, PD)                                                           \
     do {                                                                                       \
-        const hipError_t e_ = launch_rows_one<TIn, TOut, NS, M, MK, PD>(pl, dev, grid, xw, aperm, \
-                                                                        bias, y, a, st);       \
+        const hipError_t e_ = launch_rows_one<TIn, TOut, NS, M, MK, PD, POOL>(pl, dev, grid, xw,   \
+                                                                              aperm, bias, y,  \
+                                                                              a, st);          \
         if (e_ != hipSuccess) return e_;                                                       \
     } while (0)
 #define CIW_MF_STEPS(MK, PD)                                                                   \
@@ -870,21 +1038,29 @@ hipError_t launch_rows(const Geom& g, MfRowPlan pl, const void* xw, const void* 
 
 template <typename TIn, typename TOut>
 hipError_t launch_t(const Geom& g, const void* xw, const void* w, const void* aperm,
-                    const void* bias, void* y, int n_images, bool generic, hipStream_t st) {
+                    const void* bias, void* y, int n_images, bool generic, const Epi& epi,
+                    hipStream_t st) {
     if (n_images == 0) return hipSuccess;
     MfRowPlan pl;
-    if (!generic && aperm && mf_row_plan(g, (int)sizeof(TOut), pl))
-        return launch_rows<TIn, TOut>(g, pl, xw, aperm, bias, y, n_images, st);
+    if (!generic && aperm && mf_row_plan(g, (int)sizeof(TOut), pl, epi))
+        return epi.pool ? launch_rows<TIn, TOut, true>(g, pl, xw, aperm, bias, y, n_images, st)
+                        : launch_rows<TIn, TOut, false>(g, pl, xw, aperm, bias, y, n_images, st);
     MfmaArgs a;
     a.C = g.C; a.K = g.K; a.R = g.R; a.S = g.S; a.P = g.P; a.Q = g.Q;
     a.sw = g.sw; a.dw = g.dw; a.pitch = g.pitchB;
     a.RC = g.R * g.C;
     a.T = g.S * a.RC;
-    a.npix = n_images * g.P * g.Q;
+    a.relu = epi.relu;
+    a.pool = epi.pool;
+    a.Po = out_rows(g, epi);
+    a.Qo = out_cols(g, epi);
+    const int64_t npix = (int64_t)n_images * a.Po * a.Qo * (epi.pool ? 4 : 1);
+    if (npix >= (1ll << 31)) return hipErrorInvalidValue;
+    a.npix = (int)npix;
     a.fdRC = make_fastdiv(a.RC);
     a.fdC = make_fastdiv(g.C);
-    a.fdPQ = make_fastdiv(g.P * g.Q);
-    a.fdQ = make_fastdiv(g.Q);
+    a.fdPQo = make_fastdiv(a.Po * a.Qo);
+    a.fdQo = make_fastdiv(a.Qo);
     dim3 grid((a.npix + kNB - 1) / kNB, (g.K + kMB - 1) / kMB);
     hipLaunchKernelGGL((conv_mfma_generic_kernel<TIn, TOut>), grid, dim3(kThreads), 0, st,
                        (const uint16_t*)xw, (const uint16_t*)w, (const TIn*)bias, (TOut*)y, a);

@@ -50,11 +50,24 @@ struct Geom {
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
+// Epilogue fused into the contraction kernels (CIW_FLAG_RELU,
+// CIW_FLAG_MAXPOOL2): after the bias, ReLU = max(v, 0), then the max over
+// each non-overlapping 2x2 region; the output is then P/2 x Q/2 (floor).
+// Maxima are IEEE maxNum (fmaxf).
+struct Epi {
+    bool relu = false;
+    bool pool = false;
+};
+
+inline int out_rows(const Geom& g, const Epi& e) { return e.pool ? g.P / 2 : g.P; }
+inline int out_cols(const Geom& g, const Epi& e) { return e.pool ? g.Q / 2 : g.Q; }
+
 inline int elem_bytes(ciw_dtype t) { return t == CIW_F32 ? 4 : 2; }
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the error of the launch.  Pointers are already
-// offset to the chunk; n_images is the chunk's image count.
+// offset to the chunk; n_images is the chunk's image count.  y has
+// out_rows x out_cols outputs per (image, channel).
 
 hipError_t launch_transform(const Geom& g, ciw_dtype dt, ciw_win_layout lay, const void* x,
                             void* xw, int n_images, hipStream_t st);
@@ -65,7 +78,7 @@ hipError_t launch_transform(const Geom& g, ciw_dtype dt, ciw_win_layout lay, con
 int fp32_splits(const Geom& g, int n_images);
 hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, const float* bias,
                             float* y, int n_images, float* partials, int splits, bool generic,
-                            hipStream_t st);
+                            const Epi& epi, hipStream_t st);
 
 // fp16/bf16 dense contraction over an HWC window tensor on the matrix cores.
 // The row kernel multiplies a re-laid-out copy of the filter (`aperm`,
@@ -76,11 +89,11 @@ hipError_t launch_mfma_prep(const Geom& g, ciw_dtype out, const void* w, void* a
                             hipStream_t st);
 hipError_t launch_conv_mfma(const Geom& g, ciw_dtype in, ciw_dtype out, const void* xw,
                             const void* w, const void* aperm, const void* bias, void* y,
-                            int n_images, bool generic, hipStream_t st);
+                            int n_images, bool generic, const Epi& epi, hipStream_t st);
 
 // Depthwise contraction over a CHW window tensor.
 hipError_t launch_conv_dw(const Geom& g, ciw_dtype in, ciw_dtype out, const void* xw,
                           const void* w, const void* bias, void* y, int n_images,
-                          bool generic, hipStream_t st);
+                          bool generic, const Epi& epi, hipStream_t st);
 
 }  // namespace ciw

@@ -25,7 +25,8 @@
  *   nothing has been launched and no buffer has been touched.
  * - Tensors are dense and contiguous: x is NCHW [N][C][H][W]; the filters w
  *   are KCRS [K][C/groups][R][S] (R = filter height, S = filter width); bias
- *   is [K] and may be NULL; y is NCHW [N][K][P][Q].
+ *   is [K] and may be NULL; y is NCHW [N][K][P][Q] ([N][K][P/2][Q/2] with
+ *   CIW_FLAG_MAXPOOL2).
  * - x, w, y and workspace must be 16-byte aligned; bias must be aligned to
  *   its element size.  Every tensor must hold fewer than 2^31 elements.
  * - Element types: input, filter and bias share `in_dtype`.  Allowed
@@ -87,11 +88,26 @@ typedef struct {
 #define CIW_FLAG_NO_SPLIT     0x2u  /* fp32 dense: never split the channel sum across
                                        workgroups (a single pass, no partial sums) */
 #define CIW_FLAG_GENERIC      0x4u  /* use the shape-generic kernels only (testing aid) */
+/* Fused epilogue ("CS149 L9: Running DNNs Efficiently on GPUs ...", "Fusion:
+ * keep intermediates out of memory": conv -> scale/bias -> max pool, with the
+ * ReLU and 2x2 pooling of its slides 14 and 23).  Applied to the biased fp32
+ * sums inside the contraction kernels, so the unpooled output never reaches
+ * memory.  Maxima are IEEE-754 maxNum (a NaN loses to a number). */
+#define CIW_FLAG_RELU         0x8u  /* y = max(y, 0) after the bias */
+#define CIW_FLAG_MAXPOOL2     0x10u /* y[n][k][j][i] = max of the 2x2 region at rows 2j..2j+1,
+                                       columns 2i..2i+1 (after the ReLU, if any): y is
+                                       [N][K][P/2][Q/2] (floor; an odd last row or column
+                                       is dropped).  CIW_ERR_INVALID_ARG if P or Q < 2. */
 
 /* Output extent: P = floor((H + 2 pad_h - dil_h (R-1) - 1) / stride_h) + 1,
  * Q likewise.  Returns CIW_ERR_INVALID_ARG if the descriptor is invalid or
  * the window does not fit the padded input. */
 ciw_status conv_im2win_output_dims(const ciw_conv_desc* desc, int64_t* P, int64_t* Q);
+
+/* Extent of the output conv2d_fwd / conv2d_dw_fwd write with these flags:
+ * (P, Q) as above, or (P/2, Q/2) with CIW_FLAG_MAXPOOL2 (CIW_ERR_INVALID_ARG
+ * if P or Q < 2).  Other flag bits are ignored here. */
+ciw_status conv2d_output_dims(const ciw_conv_desc* desc, uint32_t flags, int64_t* P, int64_t* Q);
 
 /* Geometry of the window tensor of ONE image: number of rows (C*P for CHW,
  * P for HWC), elements per row before padding, and the row pitch in

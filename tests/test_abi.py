@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     assert tuple(names) == _lib.ENTRY_POINTS
 
 
@@ -159,6 +159,35 @@ def test_misaligned_bias():
 
 def test_unknown_flags():
     assert call_fwd(valid_desc(), ws_bytes=1 << 30, flags=0x100) == _lib.CIW_ERR_INVALID_ARG
+    assert call_fwd(valid_desc(), ws_bytes=1 << 30, flags=0x20) == _lib.CIW_ERR_INVALID_ARG
+
+
+def test_pooled_output_dims_match_oracle():
+    rng = np.random.default_rng(1)
+    layers = list(workloads.LAYERS.values()) + [workloads.random_layer(rng) for _ in range(50)]
+    for L in layers:
+        P, Q = oracle.out_dims(L.x_shape, L.w_shape, L.stride, L.pad, L.dil)
+        d = desc_of(L)
+        assert m.conv2d_output_dims(d) == (P, Q)
+        assert m.conv2d_output_dims(d, m.CIW_FLAG_RELU) == (P, Q)
+        if P >= 2 and Q >= 2:
+            assert m.conv2d_output_dims(d, m.CIW_FLAG_MAXPOOL2) == oracle.pooled_dims(P, Q), L
+
+
+@pytest.mark.parametrize("H,W", [(1, 8), (8, 1), (1, 1)])
+def test_pool_needs_a_2x2_region(H, W):
+    # 1x1 filter, no padding: P = H, Q = W; a 1-wide output has no 2x2 region
+    d = valid_desc(H=H, W=W, R=1, S=1, pad_h=0, pad_w=0)
+    P, Q = ctypes.c_int64(), ctypes.c_int64()
+    assert lib().conv2d_output_dims(ctypes.byref(d), m.CIW_FLAG_MAXPOOL2, ctypes.byref(P),
+                                    ctypes.byref(Q)) == _lib.CIW_ERR_INVALID_ARG
+    for fn in ("conv2d_fwd", "conv2d_dw_fwd"):
+        dd = d if fn == "conv2d_fwd" else valid_desc(H=H, W=W, R=1, S=1, pad_h=0, pad_w=0,
+                                                      C=4, K=4, groups=4)
+        assert call_fwd(dd, ws_bytes=1 << 30, flags=m.CIW_FLAG_MAXPOOL2, fn=fn) == \
+            _lib.CIW_ERR_INVALID_ARG
+        assert call_fwd(dd, ws_bytes=1 << 30, flags=m.CIW_FLAG_MAXPOOL2 | m.CIW_FLAG_RELU,
+                        fn=fn) == _lib.CIW_ERR_INVALID_ARG
 
 
 def test_workspace_too_small():

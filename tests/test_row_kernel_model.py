@@ -16,7 +16,10 @@ layer, checking that
   equal the divided ones;
 - each wait count equals the number of the wave's vector-memory operations
   issued after the row's copy (so it waits for exactly that copy), and fits
-  the 6-bit counter.
+  the 6-bit counter;
+- with the fused 2x2 max-pool: runs are whole row pairs inside one image,
+  every window row read exists, the pooled stores read tile columns inside
+  the tile row, and the wait counts hold for stores after every second row.
 
 The plan is restated from conv_mfma_impl.hpp and must change with it; the
 first test ties it to the library: for half-precision layers the workspace
@@ -46,7 +49,7 @@ def pitch_b(L, Q):
     return (wwin * L.R * L.C + 7) // 8 * 8
 
 
-def plan(L, out_bytes):
+def plan(L, out_bytes, pool=False):
     """The row-kernel plan, or None when the layer goes to the generic kernel."""
     P, Q = out_dims(L)
     C, K, R, S, sw = L.C, L.K, L.R, L.S, L.stride[1]
@@ -93,17 +96,31 @@ def plan(L, out_bytes):
                 break
     if nbuf == 0:
         return None
-    vec = 1 if (Q % V == 0 and (P * Q) % V == 0) else 0
-    total = K * (Q // V) if vec else K * Q
-    ns = (total + TH - 1) // TH
+
+    def stores(Po, Qo):
+        vec = 1 if (Qo % V == 0 and (Po * Qo) % V == 0) else 0
+        total = K * (Qo // V) if vec else K * Qo
+        return vec, (total + TH - 1) // TH
+
+    nbuf_lds = nbuf
+    vec, ns = stores(P, Q)
     while nbuf > 2 and (nd + ns) * (nbuf - 1) > 63:
         nbuf -= 1
     if (nd + ns) * (nbuf - 1) > 63:
         return None
+    Po, Qo = P, Q
+    if pool:
+        Po, Qo = P // 2, Q // 2
+        vec, ns = stores(Po, Qo)
+        nbuf = nbuf_lds
+        while nbuf > 2 and (nd + ns) * (nbuf - 1) > 63:
+            nbuf -= 1
+        if (nd + ns) * (nbuf - 1) > 63:
+            return None
     return dict(P=P, Q=Q, K=K, D=D, T=T, nph=nph, nset=nset, steps=steps, mask=mask,
                 mblocks=mblocks, nchunks=nchunks, G=G, pad=pad, copy=copy, nd=nd, bufc=bufc,
                 V=V, ostride=ostride, nbuf=nbuf, wgs=wgs, lds=nbuf * bufc * 16 + tile, vec=vec,
-                ns=ns)
+                ns=ns, pool=pool, Po=Po, Qo=Qo)
 
 
 def pad_src(q, pad):
@@ -121,27 +138,69 @@ def step_off(s, pad):
     return 32 * s if pad == 1 else 32 * s + 16 * ((2 * s) // pad)
 
 
-def check_waits(nbuf, nd, ns, my_rows):
-    """Iteration it: wait, barrier, copy row it + nbuf - 1, stores of row
-    it - 1, multiplies; the prologue copies rows 0 .. nbuf - 2."""
+def has_store(it, pool):
+    """A store follows every row (of row it - 1), or with the pool every
+    second row (of pair it / 2 - 1, at even it)."""
+    return it >= 2 and it % 2 == 0 if pool else it >= 1
+
+
+def check_waits(nbuf, nd, ns, my_rows, pool=False):
+    """Iteration it: wait, barrier, copy row it + nbuf - 1, the stores due,
+    multiplies; the prologue copies rows 0 .. nbuf - 2."""
     ops = []
     for i in range(min(nbuf - 1, my_rows)):
         ops += [("c", i)] * nd
     for it in range(my_rows):
         later_rows = min(nbuf - 2, my_rows - 1 - it)
-        later_stores = max(0, it - max(it - nbuf + 1, 1))
+        lo = max(it - nbuf + 1, 1)
+        later_stores = max(0, it - lo)
+        if pool:
+            lo2 = max(lo, 2)
+            later_stores = (it - 1) // 2 - (lo2 - 1) // 2 if it - 1 >= lo2 else 0
         w = nd * later_rows + ns * later_stores
         assert 0 <= w <= 63
         last_copy = max(i for i, o in enumerate(ops) if o == ("c", it))
-        assert w == len(ops) - 1 - last_copy
+        assert w == len(ops) - 1 - last_copy, (nbuf, nd, ns, my_rows, pool, it)
         if it + nbuf - 1 < my_rows:
             ops += [("c", it + nbuf - 1)] * nd
-        if it > 0:
+        if has_store(it, pool):
             ops += [("s", it - 1)] * ns
 
 
-def check_layer(L, out_bytes):
-    p = plan(L, out_bytes)
+def check_pool_schedule(p, N, grid):
+    """Row units of every workgroup: whole pairs of one image, window rows in
+    range; tiles alternate per pair and a stored tile is never the one the
+    same iteration multiplies into or merges."""
+    P, Po = p["P"], p["Po"]
+    rows = N * 2 * Po
+    groups = rows // 2
+    per = (groups + grid - 1) // grid
+    seen = []
+    for b in range(grid):
+        first = b * per * 2
+        if first >= rows:
+            continue
+        my_rows = min(per * 2, rows - first)
+        assert first % 2 == 0 and my_rows % 2 == 0
+        for it in range(my_rows):
+            u = first + it
+            pr = u >> 1
+            n, j = divmod(pr, Po)
+            wrow = n * P + 2 * j + (u & 1)
+            assert n < N and 2 * j + 1 < P and 0 <= wrow < N * P
+            seen.append(u)
+            tile = (it >> 1) & 1
+            if has_store(it, True):
+                stored_pair = (first + it) // 2 - 1
+                assert stored_pair == pr - 1
+                assert ((it >> 1) - 1) & 1 != tile
+        # the epilogue stores the last pair
+        assert (first + my_rows) // 2 - 1 == (first + my_rows - 1) >> 1
+    assert sorted(seen) == list(range(rows))
+
+
+def check_layer(L, out_bytes, pool=False):
+    p = plan(L, out_bytes, pool)
     if p is None:
         return None
     bufc, pad, Q = p["bufc"], p["pad"], p["Q"]
@@ -184,9 +243,12 @@ def check_layer(L, out_bytes):
                     if not masked and w < Q:
                         assert delta <= t0 and t0 + 8 <= delta + p["T"]
                         assert held.get(pos) == (wr * p["D"] + t0 - delta) // 8
-    # stores: incremental (k, v) equal the divided ones
+    # stores: incremental (k, v) equal the divided ones; the tile columns a
+    # store reads (two per output with the pool) lie inside the tile row
     E = p["V"] if p["vec"] else 1
-    nq = Q // E
+    Qo = p["Qo"]
+    sc = 2 if pool else 1
+    nq = Qo // E
     total = L.K * nq
     dk, dv = TH // nq, TH % nq
     for tid in range(TH):
@@ -194,13 +256,20 @@ def check_layer(L, out_bytes):
         for j in range(p["ns"]):
             i = min(tid + j * TH, total - 1)
             kk = min(k, L.K - 1)
-            off = Q - E if kk < k else v * E
+            off = Qo - E if kk < k else v * E
             assert (kk, off) == (i // nq, (i % nq) * E)
+            src = sc * off
+            assert src % E == 0 and src + sc * E <= min(Q, p["ostride"])
             k, v = k + dk, v + dv
             if v >= nq:
                 v, k = v - nq, k + 1
     for my_rows in range(1, 9):
-        check_waits(p["nbuf"], p["nd"], p["ns"], my_rows)
+        if not pool or my_rows % 2 == 0:
+            check_waits(p["nbuf"], p["nd"], p["ns"], my_rows, pool)
+    if pool:
+        for N in (1, 2, 3):
+            for grid in (1, 2, 3, 7, 512):
+                check_pool_schedule(p, N, grid)
     return p
 
 
@@ -226,6 +295,7 @@ def test_plan_matches_library_filter_size():
 def test_model_full_layers(name):
     L = workloads.LAYERS[name]
     assert check_layer(L, 2) is not None and check_layer(L, 4) is not None
+    assert check_layer(L, 2, pool=True) is not None and check_layer(L, 4, pool=True) is not None
 
 
 def test_model_coverage_layers_reach_every_specialisation():
@@ -234,12 +304,17 @@ def test_model_coverage_layers_reach_every_specialisation():
         ob = 4 if L.out_dtype == "f32" else 2
         p = check_layer(L, ob)
         assert p is not None, L
+        if p["P"] >= 2 and p["Q"] >= 2:
+            pp = check_layer(L, ob, pool=True)
+            assert pp is not None, L
+            seen.add(("pool_vec", pp["vec"]))
         seen.add(("pad", p["pad"]))
         seen.add(("nset", p["nset"]))
         seen.add(("mask", p["mask"]))
         seen.add(("vec", p["vec"]))
     want = {("pad", 1), ("pad", 2), ("pad", 4), ("pad", 8), ("nset", 1), ("nset", 2),
-            ("nset", 4), ("mask", True), ("mask", False), ("vec", 0), ("vec", 1)}
+            ("nset", 4), ("mask", True), ("mask", False), ("vec", 0), ("vec", 1),
+            ("pool_vec", 0), ("pool_vec", 1)}
     assert want <= seen, want - seen
 
 
@@ -248,7 +323,10 @@ def test_model_random_layers():
     rows = 0
     for i in range(1200):
         L = workloads.random_layer(rng, dtype="f16", max_hw=40, max_c=70, max_k=80)
-        rows += check_layer(L, 2 if i % 2 else 4) is not None
+        p = check_layer(L, 2 if i % 2 else 4)
+        rows += p is not None
+        if p is not None and p["P"] >= 2 and p["Q"] >= 2 and i % 3 == 0:
+            check_layer(L, 2 if i % 2 else 4, pool=True)
     for i in range(300):
         L = workloads.random_layer(rng, dtype="f16", max_hw=300, max_c=8, max_k=64)
         rows += check_layer(L, 2 if i % 2 else 4) is not None
@@ -263,3 +341,5 @@ def test_wait_counts_every_ring_depth():
                     continue
                 for my_rows in range(1, 12):
                     check_waits(nbuf, nd, ns, my_rows)
+                    if my_rows % 2 == 0:
+                        check_waits(nbuf, nd, ns, my_rows, pool=True)
