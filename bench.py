@@ -6,7 +6,8 @@ C ABI on one HIP stream: the im2win repack (conv_im2win_transform) and the
 windowed contraction with its bias epilogue (conv2d_fwd / conv2d_dw_fwd on the
 ready window tensor).  Inputs are resident in HBM before timing starts.
 
-Prints ONE JSON line: TFLOP/s of the step (2*N*K*(C/G)*R*S*P*Q per second),
+Prints ONE JSON line: TFLOP/s of the step (2*N*K*(C/G)*R*S*P*Q per second;
+with the fused pool, P and Q count only the pixels its 2x2 regions cover),
 the dominant kernel's roofline position (timed with HIP events on its launch
 stream), and the CPU oracle's throughput on the host cores.
 
@@ -115,8 +116,12 @@ class Step:
 
     # ---- algorithmic work
     def flops(self) -> int:
+        # with the pool, only the pixels of the 2x2 regions reach an output
         L = self.L
-        return 2 * L.N * L.K * (L.C // L.groups) * L.R * L.S * self.P * self.Q
+        P, Q = self.P, self.Q
+        if self.epilogue == "relu_pool":
+            P, Q = 2 * (P // 2), 2 * (Q // 2)
+        return 2 * L.N * L.K * (L.C // L.groups) * L.R * L.S * P * Q
 
     def bytes_x(self):
         return self.x.numel() * self.x.element_size()

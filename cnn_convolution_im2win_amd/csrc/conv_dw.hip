@@ -133,34 +133,38 @@ __global__ __launch_bounds__(kThreads) void conv_dw_block_kernel(
 
     // 3. outputs of the block, contiguous in y: consecutive threads take
     //    consecutive outputs (adjacent columns read window elements R*SW
-    //    apart, an odd stride for odd R and SW: no bank conflicts)
+    //    apart, an odd stride for odd R and SW: no bank conflicts).  With
+    //    the pool, four neighbouring lanes take the four pixels of one
+    //    output's region (the work per lane stays one pixel) and two lane
+    //    exchanges give the max; a region's lanes are always active together
+    //    (256 is a multiple of 4).
     const int nout = nu * a.Qo;
+    const int sub_bits = a.pool ? 2 : 0;
     TOut* yb = y + (size_t)u0 * a.Qo;
-    for (int o = threadIdx.x; o < nout; o += kThreads) {
+    for (int t = threadIdx.x; t < (nout << sub_bits); t += kThreads) {
+        const int o = t >> sub_bits;
+        const int d = t & ((1 << sub_bits) - 1);   // pixel of the region: row d / 2, column d % 2
         const uint32_t ul = fdiv(o, a.fdQo);
         const int wo2 = o - ul * a.Qo;
         const uint32_t u = u0 + ul;
         const int cl = fdiv(u, a.fdPo) - nc_first;
-        const int tr = first_row(u) - r_lo;
+        const int trow = first_row(u) - r_lo + (d >> 1);
+        const int wo = a.pool ? 2 * wo2 + (d & 1) : wo2;
         const float* f = filt + cl * T;
-        const float b = filt[kDwMaxCh * T + cl];
-        auto dot = [&](int trow, int wo) {
-            const TIn* row = tile + trow * a.pitch + wo * a.sw * R;
-            float acc = 0.f;
+        const TIn* row = tile + trow * a.pitch + wo * a.sw * R;
+        float acc = 0.f;
 #pragma unroll
-            for (int q = 0; q < S; ++q)
+        for (int q = 0; q < S; ++q)
 #pragma unroll
-                for (int r = 0; r < R; ++r) acc = fmaf(to_f32(row[q * a.dw * R + r]), f[r * S + q], acc);
-            return act(acc, b, a.relu);
-        };
-        float v;
+            for (int r = 0; r < R; ++r) acc = fmaf(to_f32(row[q * a.dw * R + r]), f[r * S + q], acc);
+        float v = act(acc, filt[kDwMaxCh * T + cl], a.relu);
         if (a.pool) {
-            v = fmaxf(fmaxf(dot(tr, 2 * wo2), dot(tr, 2 * wo2 + 1)),
-                      fmaxf(dot(tr + 1, 2 * wo2), dot(tr + 1, 2 * wo2 + 1)));
+            v = fmaxf(v, __shfl_xor(v, 1));
+            v = fmaxf(v, __shfl_xor(v, 2));
+            if (d == 0) yb[o] = from_f32<TOut>(v);
         } else {
-            v = dot(tr, wo2);
+            yb[o] = from_f32<TOut>(v);
         }
-        yb[o] = from_f32<TOut>(v);
     }
 }
 

@@ -314,32 +314,48 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
     y[((size_t)n * K + k) * PQ + pix] = act(v, bias ? bias[k] : 0.f, relu);
 }
 
-// Pooled form: output (n, k, j, i) adds the slices of each of the four
-// pixels (2j + dy, 2i + dx) in slice order, then bias, ReLU and the max.
+// Pooled form.  One workgroup per (image n, region (j, i), 64 channels): wave
+// d adds, in slice order, the partial sums of pixel (2j + d / 2, 2i + d % 2)
+// for its 64 channels (64 consecutive floats per slice: coalesced), then
+// bias and ReLU; the region's max goes through LDS.
 __global__ __launch_bounds__(kThreads) void split_reduce_pool_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, float* __restrict__ y,
-    uint32_t per_split, uint32_t total, int splits, int P, int Q, int Po, int Qo, int K,
-    int relu, FastDiv fdK, FastDiv fdQo, FastDiv fdPo) {
-    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-    if (i >= total) return;
-    const uint32_t t = fdiv(i, fdK);
-    const int k = i - t * K;
-    const uint32_t t2 = fdiv(t, fdQo);
-    const int i2 = t - t2 * Qo;
+    uint32_t per_split, int splits, int P, int Q, int Po, int Qo, int K, int kblocks, int relu,
+    FastDiv fdKb, FastDiv fdQo, FastDiv fdPo) {
+    __shared__ float red[3][64];
+    const uint32_t bid = blockIdx.x;
+    const uint32_t t1 = fdiv(bid, fdKb);
+    const int kb = bid - t1 * kblocks;
+    const uint32_t t2 = fdiv(t1, fdQo);
+    const int i2 = t1 - t2 * Qo;
     const uint32_t n = fdiv(t2, fdPo);
     const int j = t2 - n * Po;
-    const float b = bias ? bias[k] : 0.f;
-    float m = 0.f;
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-        const int pix = (2 * j + (sub >> 1)) * Q + 2 * i2 + (sub & 1);
-        const float* pp = part + ((size_t)n * P * Q + pix) * K + k;
-        float v = 0.f;
-        for (int s = 0; s < splits; ++s) v += pp[(size_t)s * per_split];
-        v = act(v, b, relu);
-        m = sub ? fmaxf(m, v) : v;
+    const int lane = threadIdx.x & 63;
+    const int d = threadIdx.x >> 6;
+    const int k = kb * 64 + lane;
+    const int kk = min(k, K - 1);
+    const int pix = (2 * j + (d >> 1)) * Q + 2 * i2 + (d & 1);
+    const float* pp = part + ((size_t)n * P * Q + pix) * K + kk;
+    float v = 0.f;
+    int s = 0;
+    for (; s + 4 <= splits; s += 4) {
+        const float p0 = pp[(size_t)s * per_split];
+        const float p1 = pp[(size_t)(s + 1) * per_split];
+        const float p2 = pp[(size_t)(s + 2) * per_split];
+        const float p3 = pp[(size_t)(s + 3) * per_split];
+        v += p0;
+        v += p1;
+        v += p2;
+        v += p3;
     }
-    y[((size_t)n * K + k) * Po * Qo + j * Qo + i2] = m;
+    for (; s < splits; ++s) v += pp[(size_t)s * per_split];
+    v = act(v, bias ? bias[kk] : 0.f, relu);
+    if (d > 0) red[d - 1][lane] = v;
+    __syncthreads();
+    if (d == 0 && k < K) {
+        v = fmaxf(fmaxf(v, red[0][lane]), fmaxf(red[1][lane], red[2][lane]));
+        y[((size_t)n * K + k) * Po * Qo + j * Qo + i2] = v;
+    }
 }
 
 // ------------------------------------------------------------------ planning
@@ -358,15 +374,17 @@ struct KlVariant {
                     conv_fp32_klanes_kernel<R, S, SW, TN, true, true>}}
 // Column-tile widths per filter shape: the scalar window segment
 // ((TN-1)*SW + S)*R stays at or below 60 registers.
+// The even widths 12 and 6 serve pooled layers, whose computed width 2 (Q / 2)
+// is even (12 for the 13-wide layers).
 const KlVariant kKlVariants[] = {
-    CIW_KL(1, 1, 1, 16), CIW_KL(1, 1, 1, 14), CIW_KL(1, 1, 1, 13), CIW_KL(1, 1, 1, 8),
-    CIW_KL(1, 1, 1, 7),
-    CIW_KL(1, 1, 2, 16), CIW_KL(1, 1, 2, 14), CIW_KL(1, 1, 2, 13), CIW_KL(1, 1, 2, 8),
-    CIW_KL(1, 1, 2, 7),
-    CIW_KL(3, 3, 1, 16), CIW_KL(3, 3, 1, 14), CIW_KL(3, 3, 1, 13), CIW_KL(3, 3, 1, 8),
-    CIW_KL(3, 3, 1, 7),
-    CIW_KL(3, 3, 2, 8), CIW_KL(3, 3, 2, 7), CIW_KL(3, 3, 2, 4),
-    CIW_KL(5, 5, 1, 8), CIW_KL(5, 5, 1, 7), CIW_KL(5, 5, 1, 4),
+    CIW_KL(1, 1, 1, 16), CIW_KL(1, 1, 1, 14), CIW_KL(1, 1, 1, 13), CIW_KL(1, 1, 1, 12),
+    CIW_KL(1, 1, 1, 8), CIW_KL(1, 1, 1, 7), CIW_KL(1, 1, 1, 6),
+    CIW_KL(1, 1, 2, 16), CIW_KL(1, 1, 2, 14), CIW_KL(1, 1, 2, 13), CIW_KL(1, 1, 2, 12),
+    CIW_KL(1, 1, 2, 8), CIW_KL(1, 1, 2, 7), CIW_KL(1, 1, 2, 6),
+    CIW_KL(3, 3, 1, 16), CIW_KL(3, 3, 1, 14), CIW_KL(3, 3, 1, 13), CIW_KL(3, 3, 1, 12),
+    CIW_KL(3, 3, 1, 8), CIW_KL(3, 3, 1, 7), CIW_KL(3, 3, 1, 6),
+    CIW_KL(3, 3, 2, 8), CIW_KL(3, 3, 2, 7), CIW_KL(3, 3, 2, 6), CIW_KL(3, 3, 2, 4),
+    CIW_KL(5, 5, 1, 8), CIW_KL(5, 5, 1, 7), CIW_KL(5, 5, 1, 6), CIW_KL(5, 5, 1, 4),
 };
 #undef CIW_KL
 
@@ -543,11 +561,13 @@ hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, cons
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t per_split = (int64_t)n_images * g.K * g.P * g.Q;
     if (epi.pool) {
-        const int64_t total = (int64_t)n_images * g.K * Po * Qo;
-        hipLaunchKernelGGL(split_reduce_pool_kernel, dim3((uint32_t)((total + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, st, partials, bias, y, (uint32_t)per_split,
-                           (uint32_t)total, p.splits, g.P, g.Q, Po, Qo, g.K, (int)epi.relu,
-                           make_fastdiv(g.K), make_fastdiv(Qo), make_fastdiv(Po));
+        const int kblocks = (g.K + 63) / 64;
+        const int64_t blocks = (int64_t)n_images * Po * Qo * kblocks;
+        if (blocks >= (1ll << 31)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(split_reduce_pool_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, st,
+                           partials, bias, y, (uint32_t)per_split, p.splits, g.P, g.Q, Po, Qo,
+                           g.K, kblocks, (int)epi.relu, make_fastdiv(kblocks), make_fastdiv(Qo),
+                           make_fastdiv(Po));
     } else {
         hipLaunchKernelGGL(split_reduce_kernel, dim3((uint32_t)((per_split + kThreads - 1) / kThreads)),
                            dim3(kThreads), 0, st, partials, bias, y, (uint32_t)per_split, p.splits,

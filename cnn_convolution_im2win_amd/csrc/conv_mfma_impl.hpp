@@ -201,7 +201,8 @@ __global__ __launch_bounds__(kThreads) void conv_mfma_generic_kernel(
 struct MfRowArgs {
     int C, K, R, S, P, Q, pitch;   // pitch: window row pitch (elements)
     int D, T;                      // window start stride, window length
-    int nph, mblocks;              // pixel phases, 32-pixel blocks per phase
+    int nph, mblocks;              // pixel phases (1, 2, 4 or 8), 32-pixel blocks per phase
+    int nph_log2;
     int G;                         // chunks between window starts (nph == 1)
     int nchunks;                   // 16-byte chunks of a window row
     int copy_chunks;               // LDS chunk positions of a row (pads included)
@@ -345,23 +346,40 @@ __device__ __forceinline__ float4 get4<float>(const float* p) {
 }
 
 // 2x2 pooling, horizontal half: 2V adjacent outputs (the 16-byte vectors lo,
-// hi) to the V maxima of their pairs.  Values come from the output type, so
-// converting a maximum back is exact.
+// hi) to the V maxima of their pairs, each also maxed with `lo3` (0 for the
+// ReLU, or a quiet NaN, which maxNum ignores).  Values come from the output
+// type, so converting a maximum back is exact.
 template <typename TOut>
-__device__ __forceinline__ uint4 pool_pairs(uint4 lo, uint4 hi) {
-    auto word = [](uint32_t u0, uint32_t u1) {
+__device__ __forceinline__ uint4 pool_pairs(uint4 lo, uint4 hi, float lo3) {
+    auto word = [&](uint32_t u0, uint32_t u1) {
         const float2 a = unpack2<TOut>(u0), b = unpack2<TOut>(u1);
-        return pack2<TOut>(fmaxf(a.x, a.y), fmaxf(b.x, b.y));
+        return pack2<TOut>(fmaxf(fmaxf(a.x, a.y), lo3), fmaxf(fmaxf(b.x, b.y), lo3));
     };
     return make_uint4(word(lo.x, lo.y), word(lo.z, lo.w), word(hi.x, hi.y), word(hi.z, hi.w));
 }
 
 template <>
-__device__ __forceinline__ uint4 pool_pairs<float>(uint4 lo, uint4 hi) {
-    auto m = [](uint32_t a, uint32_t b) {
-        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+__device__ __forceinline__ uint4 pool_pairs<float>(uint4 lo, uint4 hi, float lo3) {
+    auto m = [&](uint32_t a, uint32_t b) {
+        return __float_as_uint(fmaxf(fmaxf(__uint_as_float(a), __uint_as_float(b)), lo3));
     };
     return make_uint4(m(lo.x, lo.y), m(lo.z, lo.w), m(hi.x, hi.y), m(hi.z, hi.w));
+}
+
+// ReLU of one 16-byte vector of outputs.
+template <typename TOut>
+__device__ __forceinline__ uint4 relu_vec(uint4 v) {
+    auto word = [](uint32_t u) {
+        const float2 a = unpack2<TOut>(u);
+        return pack2<TOut>(fmaxf(a.x, 0.f), fmaxf(a.y, 0.f));
+    };
+    return make_uint4(word(v.x), word(v.y), word(v.z), word(v.w));
+}
+
+template <>
+__device__ __forceinline__ uint4 relu_vec<float>(uint4 v) {
+    auto m = [](uint32_t a) { return __float_as_uint(fmaxf(__uint_as_float(a), 0.f)); };
+    return make_uint4(m(v.x), m(v.y), m(v.z), m(v.w));
 }
 
 // s_waitcnt with a run-time vector-memory count (the instruction takes an
@@ -428,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
 #pragma unroll
     for (int j = 0; j < NSET; ++j) {
         const int pb = min(pb0 * NSET + j, npb - 1);   // set j serves phase pb % nph
-        const uint16_t* fp = aperm + ((size_t)((pb % a.nph) * 2 + kh) * STEPS * 64 + lane) * 8;
+        const uint16_t* fp = aperm + ((size_t)((pb & (a.nph - 1)) * 2 + kh) * STEPS * 64 + lane) * 8;
 #pragma unroll
         for (int s2 = 0; s2 < STEPS; ++s2)
             F[j][s2] = *reinterpret_cast<const uint4*>(fp + 512 * s2);
@@ -512,7 +530,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
     int sfj[NSET];
 #pragma unroll
     for (int j = 0; j < NSET; ++j) {
-        const int dj = (((pb0 * NSET + j) % a.nph) * a.D) & 7;
+        const int dj = (((pb0 * NSET + j) & (a.nph - 1)) * a.D) & 7;
         sfj[j] = (dj + a.T) / 16;
         mkf[j] = make_uint4(~0u, ~0u, ~0u, ~0u);
         mkt[j] = mkf[j];
@@ -530,6 +548,11 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
     const int sk0 = tid / nq, sv0 = tid - sk0 * nq;
     const int dk = kThreads / nq, dv = kThreads - dk * nq;
     const int sc = POOL ? 2 : 1;                // tile columns per output column
+    // ReLU is applied to the tile's values as they are stored (ReLU and
+    // rounding are monotone, so this equals ReLU before rounding, and it
+    // commutes with the pool's max).  With the pool it is a third operand of
+    // the pair's max: 0, or a quiet NaN, which maxNum ignores.
+    const float relu_lo = a.relu ? 0.f : __builtin_nanf("");
 
     // ---- output row (n, h) from a tile: K rows of Qo contiguous elements.
     // With the pool the tile already holds the max of the region's two rows
@@ -559,10 +582,12 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
         };
         auto vec_at = [&](int i) {
             const uint4 lo = *reinterpret_cast<const uint4*>(tl + i);
-            return POOL ? pool_pairs<TOut>(lo, *reinterpret_cast<const uint4*>(tl + i + V)) : lo;
+            if (POOL) return pool_pairs<TOut>(lo, *reinterpret_cast<const uint4*>(tl + i + V), relu_lo);
+            return a.relu ? relu_vec<TOut>(lo) : lo;
         };
         auto elem_at = [&](int i) {
-            return POOL ? from_f32<TOut>(fmaxf(to_f32(tl[i]), to_f32(tl[i + 1]))) : tl[i];
+            if (POOL) return from_f32<TOut>(fmaxf(fmaxf(to_f32(tl[i]), to_f32(tl[i + 1])), relu_lo));
+            return a.relu ? from_f32<TOut>(fmaxf(to_f32(tl[i]), 0.f)) : tl[i];
         };
         take();
         if (a.vec_store) {
@@ -602,9 +627,6 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
     // entries it wrote), and the pair is stored while the next pair's first
     // row multiplies into the other tile.
     const int tile_elems = a.K * a.ostride;
-    // ReLU without a branch: maxNum against 0, or against a quiet NaN, which
-    // returns the other operand unchanged (a NaN sum stays NaN)
-    const float relu_lo = a.relu ? 0.f : __builtin_nanf("");
     for (int it = 0; it < my_rows; ++it) {
         const int buf = it % a.nbuf;
         // wait for this row's copy: allow the copies of the rows after it
@@ -643,13 +665,13 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
             for (int j = 0; j < NSET; ++j) {
             const int pb = (pb0 + 2 * base) * NSET + j;
             if (NSET == 1 && pb >= npb) break;
-            const int ph = pb % a.nph;
-            const int mb = pb / a.nph;
+            const int ph = pb & (a.nph - 1);
+            const int mb = pb >> a.nph_log2;
             const int delta = (ph * a.D) & 7;
             const int wpix = a.nph * (32 * mb + ml) + ph;
             // pixels past the row end (never stored) read the last pixel of
             // their phase instead, so reads stay inside the row buffer
-            const int wlast = a.Q - 1 >= ph ? a.Q - 1 - (a.Q - 1 - ph) % a.nph : ph;
+            const int wlast = a.Q - 1 >= ph ? a.Q - 1 - ((a.Q - 1 - ph) & (a.nph - 1)) : ph;
             const int wread = min(wpix, wlast);
             // LDS chunk position of the lane's step-0 read: the window start
             // minus delta (a multiple of 8 elements), plus 8 elements for g
@@ -713,36 +735,46 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
             }
             // lane holds D[m][n] for channel n = lane % 32 and block pixel
             // m = 8 (i / 4) + 4 (lane / 32) + i % 4; pixels past the row end
-            // land in tile columns that are never stored.  The bias (unless
-            // it seeded the sum: adding "+ 0" would not be free, the
-            // compiler must keep it for the sign of a zero sum), then ReLU.
+            // land in tile columns that are never stored.  The bias is added
+            // unless it seeded the sum (adding "+ 0" would not be free: the
+            // compiler must keep it for the sign of a zero sum).  The second
+            // row of a pooled pair reads back what the first wrote at the
+            // same places, all reads before one wait.
             if (!kLean) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[i] += bias_k;
             }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[i] = fmaxf(acc[i], relu_lo);
             const int k = kh * 32 + ml;
             if (NSET == 1) {
                 if (k < a.K) {
                     TOut* orow = otile + k * a.ostride + a.nph * 32 * mb + ph;
                     if (a.nph == 1) {
+                        if (merge) {
+                            float4 o[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            TOut* tp = orow + 8 * q + 4 * g;
-                            float v0 = acc[4 * q], v1 = acc[4 * q + 1], v2 = acc[4 * q + 2], v3 = acc[4 * q + 3];
-                            if (merge) {
-                                const float4 o = get4<TOut>(tp);
-                                v0 = fmaxf(v0, o.x); v1 = fmaxf(v1, o.y); v2 = fmaxf(v2, o.z); v3 = fmaxf(v3, o.w);
-                            }
-                            put4<TOut>(tp, v0, v1, v2, v3);
+                            for (int q = 0; q < 4; ++q) o[q] = get4<TOut>(orow + 8 * q + 4 * g);
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                put4<TOut>(orow + 8 * q + 4 * g, fmaxf(acc[4 * q], o[q].x),
+                                           fmaxf(acc[4 * q + 1], o[q].y), fmaxf(acc[4 * q + 2], o[q].z),
+                                           fmaxf(acc[4 * q + 3], o[q].w));
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                put4<TOut>(orow + 8 * q + 4 * g, acc[4 * q], acc[4 * q + 1],
+                                           acc[4 * q + 2], acc[4 * q + 3]);
                         }
                     } else {
+                        auto at = [&](int i) { return orow + a.nph * (8 * (i >> 2) + 4 * g + (i & 3)); };
+                        if (merge) {
+                            float o[16];
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            TOut* tp = orow + a.nph * (8 * (i >> 2) + 4 * g + (i & 3));
-                            const float v = merge ? fmaxf(acc[i], to_f32(*tp)) : acc[i];
-                            *tp = from_f32<TOut>(v);
+                            for (int i = 0; i < 16; ++i) o[i] = to_f32(*at(i));
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) *at(i) = from_f32<TOut>(fmaxf(acc[i], o[i]));
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) *at(i) = from_f32<TOut>(acc[i]);
                         }
                     }
                 }
@@ -751,16 +783,17 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
             } else if (k < a.K) {
                 // blocks j - 1 and j: phases ph - 1 and ph, neighbouring pixels
                 TOut* orow = otile + k * a.ostride + kNph * (32 * mb + 4 * g) + ph - 1;
+                auto at = [&](int i) { return orow + kNph * (8 * (i >> 2) + (i & 3)); };
+                if (merge) {
+                    float2 o[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    TOut* tp = orow + kNph * (8 * (i >> 2) + (i & 3));
-                    float v0 = accp[i], v1 = acc[i];
-                    if (merge) {
-                        const float2 o = get2<TOut>(tp);
-                        v0 = fmaxf(v0, o.x);
-                        v1 = fmaxf(v1, o.y);
-                    }
-                    put2<TOut>(tp, v0, v1);
+                    for (int i = 0; i < 16; ++i) o[i] = get2<TOut>(at(i));
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        put2<TOut>(at(i), fmaxf(accp[i], o[i].x), fmaxf(acc[i], o[i].y));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) put2<TOut>(at(i), accp[i], acc[i]);
                 }
             }
             }
@@ -927,6 +960,7 @@ bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl, const Epi& epi = E
     a.pitch = g.pitchB;
     a.D = D; a.T = T;
     a.nph = nph; a.mblocks = mblocks;
+    a.nph_log2 = nph == 1 ? 0 : nph == 2 ? 1 : nph == 4 ? 2 : 3;
     a.G = G;
     a.nchunks = nchunks;
     a.copy_chunks = copy_chunks;
