@@ -306,6 +306,16 @@ __device__ __forceinline__ void put4<float>(float* p, float a0, float a1, float 
     *reinterpret_cast<float4*>(p) = make_float4(a0, a1, a2, a3);
 }
 
+// maxNum of two floats as one v_max_f32.  fmaxf would first quiet both
+// operands (two more instructions each), which only matters for signaling
+// NaNs; the values here are results of arithmetic or stored outputs, whose
+// NaNs are quiet.
+__device__ __forceinline__ float max_q(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // The two 16-bit outputs of a packed word, as floats (exact).
 template <typename TOut>
 __device__ __forceinline__ float2 unpack2(uint32_t u);
@@ -353,7 +363,7 @@ template <typename TOut>
 __device__ __forceinline__ uint4 pool_pairs(uint4 lo, uint4 hi, float lo3) {
     auto word = [&](uint32_t u0, uint32_t u1) {
         const float2 a = unpack2<TOut>(u0), b = unpack2<TOut>(u1);
-        return pack2<TOut>(fmaxf(fmaxf(a.x, a.y), lo3), fmaxf(fmaxf(b.x, b.y), lo3));
+        return pack2<TOut>(max_q(max_q(a.x, a.y), lo3), max_q(max_q(b.x, b.y), lo3));
     };
     return make_uint4(word(lo.x, lo.y), word(lo.z, lo.w), word(hi.x, hi.y), word(hi.z, hi.w));
 }
@@ -361,7 +371,7 @@ __device__ __forceinline__ uint4 pool_pairs(uint4 lo, uint4 hi, float lo3) {
 template <>
 __device__ __forceinline__ uint4 pool_pairs<float>(uint4 lo, uint4 hi, float lo3) {
     auto m = [&](uint32_t a, uint32_t b) {
-        return __float_as_uint(fmaxf(fmaxf(__uint_as_float(a), __uint_as_float(b)), lo3));
+        return __float_as_uint(max_q(max_q(__uint_as_float(a), __uint_as_float(b)), lo3));
     };
     return make_uint4(m(lo.x, lo.y), m(lo.z, lo.w), m(hi.x, hi.y), m(hi.z, hi.w));
 }
@@ -371,14 +381,14 @@ template <typename TOut>
 __device__ __forceinline__ uint4 relu_vec(uint4 v) {
     auto word = [](uint32_t u) {
         const float2 a = unpack2<TOut>(u);
-        return pack2<TOut>(fmaxf(a.x, 0.f), fmaxf(a.y, 0.f));
+        return pack2<TOut>(max_q(a.x, 0.f), max_q(a.y, 0.f));
     };
     return make_uint4(word(v.x), word(v.y), word(v.z), word(v.w));
 }
 
 template <>
 __device__ __forceinline__ uint4 relu_vec<float>(uint4 v) {
-    auto m = [](uint32_t a) { return __float_as_uint(fmaxf(__uint_as_float(a), 0.f)); };
+    auto m = [](uint32_t a) { return __float_as_uint(max_q(__uint_as_float(a), 0.f)); };
     return make_uint4(m(v.x), m(v.y), m(v.z), m(v.w));
 }
 
@@ -586,8 +596,8 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
             return a.relu ? relu_vec<TOut>(lo) : lo;
         };
         auto elem_at = [&](int i) {
-            if (POOL) return from_f32<TOut>(fmaxf(fmaxf(to_f32(tl[i]), to_f32(tl[i + 1])), relu_lo));
-            return a.relu ? from_f32<TOut>(fmaxf(to_f32(tl[i]), 0.f)) : tl[i];
+            if (POOL) return from_f32<TOut>(max_q(max_q(to_f32(tl[i]), to_f32(tl[i + 1])), relu_lo));
+            return a.relu ? from_f32<TOut>(max_q(to_f32(tl[i]), 0.f)) : tl[i];
         };
         take();
         if (a.vec_store) {
@@ -750,14 +760,15 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
                     TOut* orow = otile + k * a.ostride + a.nph * 32 * mb + ph;
                     if (a.nph == 1) {
                         if (merge) {
+                            asm volatile("" ::: "memory");   // keep the reads on this path
                             float4 o[4];
 #pragma unroll
                             for (int q = 0; q < 4; ++q) o[q] = get4<TOut>(orow + 8 * q + 4 * g);
 #pragma unroll
                             for (int q = 0; q < 4; ++q)
-                                put4<TOut>(orow + 8 * q + 4 * g, fmaxf(acc[4 * q], o[q].x),
-                                           fmaxf(acc[4 * q + 1], o[q].y), fmaxf(acc[4 * q + 2], o[q].z),
-                                           fmaxf(acc[4 * q + 3], o[q].w));
+                                put4<TOut>(orow + 8 * q + 4 * g, max_q(acc[4 * q], o[q].x),
+                                           max_q(acc[4 * q + 1], o[q].y), max_q(acc[4 * q + 2], o[q].z),
+                                           max_q(acc[4 * q + 3], o[q].w));
                         } else {
 #pragma unroll
                             for (int q = 0; q < 4; ++q)
@@ -767,11 +778,12 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
                     } else {
                         auto at = [&](int i) { return orow + a.nph * (8 * (i >> 2) + 4 * g + (i & 3)); };
                         if (merge) {
+                            asm volatile("" ::: "memory");
                             float o[16];
 #pragma unroll
                             for (int i = 0; i < 16; ++i) o[i] = to_f32(*at(i));
 #pragma unroll
-                            for (int i = 0; i < 16; ++i) *at(i) = from_f32<TOut>(fmaxf(acc[i], o[i]));
+                            for (int i = 0; i < 16; ++i) *at(i) = from_f32<TOut>(max_q(acc[i], o[i]));
                         } else {
 #pragma unroll
                             for (int i = 0; i < 16; ++i) *at(i) = from_f32<TOut>(acc[i]);
@@ -785,12 +797,13 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
                 TOut* orow = otile + k * a.ostride + kNph * (32 * mb + 4 * g) + ph - 1;
                 auto at = [&](int i) { return orow + kNph * (8 * (i >> 2) + (i & 3)); };
                 if (merge) {
+                    asm volatile("" ::: "memory");
                     float2 o[16];
 #pragma unroll
                     for (int i = 0; i < 16; ++i) o[i] = get2<TOut>(at(i));
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
-                        put2<TOut>(at(i), fmaxf(accp[i], o[i].x), fmaxf(acc[i], o[i].y));
+                        put2<TOut>(at(i), max_q(accp[i], o[i].x), max_q(acc[i], o[i].y));
                 } else {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) put2<TOut>(at(i), accp[i], acc[i]);
