@@ -16,6 +16,11 @@ stream), and the CPU oracle's throughput on the host cores.
 
 --workload picks one of the five synthetic layers (default: the 1x512x13x13
 -> 1024, 3x3 layer); --layers adds a per-layer summary of all five.
+--memory adds, per layer, the peak device memory (the paper's MaxRSS, here
+from torch's allocator) and time of one conv2d_fwd call per processing
+strategy: the whole batch in one chunk, 16-image chunks and single images;
+the im2col matrix an im2col convolution would materialise (computed); and
+MIOpen's convolution (torch.nn.functional.conv2d), as context.
 --epilogue fuses ReLU, or ReLU and the 2x2 max-pool, into the contraction
 (CIW_FLAG_RELU / CIW_FLAG_MAXPOOL2); each layer then also reports, as
 context, the same result computed unfused: the plain convolution followed by
@@ -284,6 +289,95 @@ def time_unfused(L: workloads.Layer, epilogue: str, steps: int, warmup: int) -> 
     return sum(e[0].elapsed_time(e[1]) for e in ev) / steps
 
 
+def memory_report(L: workloads.Layer, steps: int = 5) -> dict:
+    """Peak device memory and time per call of each processing strategy.
+
+    The library allocates nothing: a call's footprint is x, w, b and y plus
+    the workspace, whose size follows from how many images one chunk
+    repacks (conv2d_workspace_bytes).  Peaks are read from torch's caching
+    allocator around a fresh allocation of every buffer."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+    import cnn_convolution_im2win_amd as ciw
+
+    code = {"f32": ciw.CIW_F32, "f16": ciw.CIW_F16, "bf16": ciw.CIW_BF16}[L.dtype]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    x, w, b = workloads.make_inputs(L)
+
+    def dev(a):
+        if a is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if L.dtype == "bf16" else a))
+        t = t.to("cuda")
+        return t.view(torch.bfloat16) if L.dtype == "bf16" else t
+
+    desc = ciw.make_desc(L.x_shape, L.w_shape, L.stride, L.pad, L.dil, L.groups)
+    P, Q = ciw.conv_im2win_output_dims(desc)
+    eb = workloads.ELEM_BYTES[L.dtype]
+    io_bytes = (L.N * L.C * L.H * L.W + L.K * (L.C // L.groups) * L.R * L.S
+                + (L.K if L.b_dist is not None else 0)) * eb + \
+        L.N * L.K * P * Q * workloads.ELEM_BYTES[L.out_dtype]
+
+    def peak_and_time(run_once):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        state = run_once(None)                 # allocates every buffer, runs once
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run_once(state)
+        e1.record()
+        torch.cuda.synchronize()
+        del state
+        return peak, e0.elapsed_time(e1) / steps
+
+    def im2win(n_chunk):
+        ws_bytes = ciw.conv2d_workspace_bytes(desc, code, n_chunk)
+
+        def run_once(state):
+            if state is None:
+                xd, wd, bd = dev(x), dev(w), dev(b)
+                y = torch.empty((L.N, L.K, P, Q), dtype=tdt[L.out_dtype], device="cuda")
+                ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+                state = (xd, wd, bd, y, ws)
+            xd, wd, bd, y, ws = state
+            fn = ciw.conv2d_dw_fwd if L.groups > 1 else ciw.conv2d_fwd
+            fn(xd, wd, bd, y, ws, L.stride, L.pad, L.dil)
+            return state
+
+        peak, ms = peak_and_time(run_once)
+        return {"chunk_images": n_chunk, "workspace_bytes": ws_bytes, "peak_bytes": peak,
+                "ms": round(ms, 4)}
+
+    out = {"inputs_outputs_bytes": io_bytes}
+    for tag, n in (("im2win_full_batch", L.N), ("im2win_chunk16", min(L.N, 16)),
+                   ("im2win_single_image", 1)):
+        if tag != "im2win_full_batch" and n == L.N:
+            continue
+        out[tag] = im2win(n)
+    per_image = (L.C // L.groups) * L.groups * L.R * L.S * P * Q * eb
+    out["im2col_matrix_bytes"] = {"single_image": per_image, "full_batch": per_image * L.N}
+
+    def miopen(state):
+        if state is None:
+            state = (dev(x), dev(w), dev(b))
+        xd, wd, bd = state
+        F.conv2d(xd, wd, bd, L.stride, L.pad, L.dil, L.groups)
+        return state
+
+    try:
+        peak, ms = peak_and_time(miopen)
+        out["miopen_conv2d"] = {"peak_bytes": peak, "ms": round(ms, 4)}
+    except Exception as e:   # context only
+        out["miopen_conv2d"] = {"error": str(e)[:200]}
+    return out
+
+
 def measure_layer(L: workloads.Layer, steps: int, warmup: int, epilogue: str = "none",
                   unfused: bool = True) -> dict:
     import statistics
@@ -321,6 +415,8 @@ def main():
     ap.add_argument("--layers", action="store_true", help="also summarise all five layers")
     ap.add_argument("--epilogue", default="none", choices=EPILOGUES,
                     help="fuse ReLU / ReLU + 2x2 max-pool into the contraction")
+    ap.add_argument("--memory", action="store_true",
+                    help="with --layers, add peak memory and time per processing strategy")
     ap.add_argument("--no-unfused", action="store_true",
                     help="with --epilogue, skip the unfused comparison (e.g. under a profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -367,6 +463,14 @@ def main():
                                  args.epilogue, not args.no_unfused)
             layers[name] = r
             print(f"# {name}: {json.dumps(r)}", file=sys.stderr, flush=True)
+        if args.memory:
+            del step
+            for name in workloads.LAYER_ORDER:
+                print(f"# memory {name}", file=sys.stderr, flush=True)
+                layers[name]["memory"] = memory_report(workloads.LAYERS[name])
+                print(f"# memory {name}: {json.dumps(layers[name]['memory'])}", file=sys.stderr,
+                      flush=True)
+            step = Step(L, args.epilogue)
 
     cpu = None
     if not args.no_cpu_baseline:
