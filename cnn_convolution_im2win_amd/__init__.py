@@ -8,6 +8,7 @@ supplies device memory and streams.
 
     y = conv2d(x, w, b, stride=1, padding=1)          # F.conv2d-style helper
     y = conv2d(x, w, b, 1, 1, flags=CIW_FLAG_RELU | CIW_FLAG_MAXPOOL2)   # fused epilogue
+    y = conv2d(x, w, None, 1, 1, flags=CIW_FLAG_IMPLICIT)  # window rows built in LDS
     y = conv2d_fwd(x, w, b, y, workspace, ...)        # the C entry point
     xw = conv_im2win_transform(x, R, S, ...)          # the repack alone
 """
@@ -17,7 +18,8 @@ import ctypes
 from typing import Optional, Sequence, Tuple, Union
 
 from . import _lib
-from ._lib import (CIW_BF16, CIW_F16, CIW_F32, CIW_FLAG_GENERIC, CIW_FLAG_MAXPOOL2,
+from ._lib import (CIW_BF16, CIW_F16, CIW_F32, CIW_FLAG_GENERIC, CIW_FLAG_IMPLICIT,
+                   CIW_FLAG_MAXPOOL2,
                    CIW_FLAG_NO_SPLIT, CIW_FLAG_RELU, CIW_FLAG_WINDOW_READY, CIW_WIN_CHW,
                    CIW_WIN_HWC, ConvDesc, Im2winError, LIB_PATH, status_string)
 
@@ -27,10 +29,10 @@ __all__ = [
     "conv2d", "conv2d_fwd", "conv2d_dw_fwd", "conv_im2win_transform",
     "conv_im2win_output_dims", "conv2d_output_dims", "conv_im2win_window_geometry",
     "conv_im2win_window_bytes",
-    "conv2d_workspace_bytes", "make_desc", "Im2winError", "status_string", "LIB_PATH",
+    "conv2d_workspace_bytes", "conv2d_implicit_workspace_bytes", "make_desc", "Im2winError", "status_string", "LIB_PATH",
     "CIW_F32", "CIW_F16", "CIW_BF16", "CIW_WIN_CHW", "CIW_WIN_HWC",
     "CIW_FLAG_WINDOW_READY", "CIW_FLAG_NO_SPLIT", "CIW_FLAG_GENERIC", "CIW_FLAG_RELU",
-    "CIW_FLAG_MAXPOOL2",
+    "CIW_FLAG_MAXPOOL2", "CIW_FLAG_IMPLICIT",
 ]
 
 
@@ -112,6 +114,17 @@ def conv2d_workspace_bytes(desc: ConvDesc, in_dtype: int, n_images: int) -> int:
     out = ctypes.c_size_t()
     _lib.check(_lib.load().conv2d_workspace_bytes(ctypes.byref(desc), in_dtype, int(n_images),
                                                   ctypes.byref(out)), "conv2d_workspace_bytes")
+    return out.value
+
+
+def conv2d_implicit_workspace_bytes(desc: ConvDesc, in_dtype: int, out_dtype: int,
+                                    flags: int = 0) -> int:
+    """Workspace of conv2d_fwd with CIW_FLAG_IMPLICIT (window rows built in
+    LDS); raises Im2winError (unsupported) for layers that kernel does not run."""
+    out = ctypes.c_size_t()
+    _lib.check(_lib.load().conv2d_implicit_workspace_bytes(
+        ctypes.byref(desc), in_dtype, out_dtype, int(flags), ctypes.byref(out)),
+        "conv2d_implicit_workspace_bytes")
     return out.value
 
 
@@ -202,7 +215,11 @@ def conv2d(x, weight, bias=None, stride: IntPair = 1, padding: IntPair = 0,
     out_dtype = x.dtype if out_dtype is None else out_dtype
     y = torch.empty((x.shape[0], weight.shape[0], P, Q), dtype=out_dtype, device=x.device)
     depthwise = groups > 1
-    if workspace is None:
+    if workspace is None and flags & CIW_FLAG_IMPLICIT:
+        nbytes = conv2d_implicit_workspace_bytes(desc, _dtype_code(x.dtype), _dtype_code(out_dtype),
+                                                 flags)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    elif workspace is None:
         nbytes = conv2d_workspace_bytes(desc, _dtype_code(x.dtype), max(int(x.shape[0]), 1))
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
     fn = conv2d_dw_fwd if depthwise else conv2d_fwd

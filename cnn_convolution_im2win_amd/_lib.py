@@ -25,6 +25,7 @@ CIW_FLAG_NO_SPLIT = 0x2
 CIW_FLAG_GENERIC = 0x4
 CIW_FLAG_RELU = 0x8
 CIW_FLAG_MAXPOOL2 = 0x10
+CIW_FLAG_IMPLICIT = 0x20
 
 # the exported entry points, in header order
 ENTRY_POINTS = (
@@ -34,6 +35,7 @@ ENTRY_POINTS = (
     "conv_im2win_window_bytes",
     "conv_im2win_transform",
     "conv2d_workspace_bytes",
+    "conv2d_implicit_workspace_bytes",
     "conv2d_fwd",
     "conv2d_dw_fwd",
     "conv_im2win_status_string",
@@ -84,6 +86,7 @@ def load():
         "conv_im2win_window_bytes": [D, i32, i32, i64, psz],
         "conv_im2win_transform": [D, i32, i32, P, P, P],
         "conv2d_workspace_bytes": [D, i32, i64, psz],
+        "conv2d_implicit_workspace_bytes": [D, i32, i32, u32, psz],
         "conv2d_fwd": [D, i32, i32, P, P, P, P, P, ctypes.c_size_t, u32, P],
         "conv2d_dw_fwd": [D, i32, i32, P, P, P, P, P, ctypes.c_size_t, u32, P],
     }

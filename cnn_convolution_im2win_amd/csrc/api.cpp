@@ -107,7 +107,10 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
     // allowed (in -> out) pairs
     if (in == CIW_F32 ? out != CIW_F32 : (out != in && out != CIW_F32)) return CIW_ERR_INVALID_ARG;
     if (flags & ~(CIW_FLAG_WINDOW_READY | CIW_FLAG_NO_SPLIT | CIW_FLAG_GENERIC | CIW_FLAG_RELU |
-                  CIW_FLAG_MAXPOOL2))
+                  CIW_FLAG_MAXPOOL2 | CIW_FLAG_IMPLICIT))
+        return CIW_ERR_INVALID_ARG;
+    const bool implicit = (flags & CIW_FLAG_IMPLICIT) != 0;
+    if (implicit && (depthwise || (flags & (CIW_FLAG_WINDOW_READY | CIW_FLAG_GENERIC))))
         return CIW_ERR_INVALID_ARG;
     Epi epi;
     epi.relu = (flags & CIW_FLAG_RELU) != 0;
@@ -124,6 +127,17 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
     if ((x && !aligned(x, 16)) || !aligned(w, 16) || !aligned(y, 16) || !aligned(ws, 16) ||
         (bias && !aligned(bias, elem_bytes(in))))
         return CIW_ERR_INVALID_ARG;
+
+    if (implicit) {
+        // window rows built in LDS from x: no chunks, the workspace holds
+        // only the re-laid-out filter
+        if (in == CIW_F32) return CIW_ERR_UNSUPPORTED;
+        const size_t need = implicit_workspace_bytes(g, out, epi);
+        if (need == 0) return CIW_ERR_UNSUPPORTED;
+        if (ws_bytes < need) return CIW_ERR_WORKSPACE;
+        (void)hipGetLastError();
+        return from_hip(launch_conv_implicit(g, in, out, x, w, bias, y, ws, epi, (hipStream_t)stream));
+    }
 
     const Path p = path_of(g, in, depthwise);
     const ciw_win_layout lay = layout_of(p);
@@ -258,6 +272,25 @@ ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
     bool dw = g.G > 1;
     if (dw && !(g.G == g.C && g.K == g.C)) return CIW_ERR_UNSUPPORTED;
     *bytes = (size_t)chunk_workspace(g, path_of(g, in_dtype, dw), n_images);
+    return CIW_OK;
+}
+
+ciw_status conv2d_implicit_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
+                                           ciw_dtype out_dtype, uint32_t flags, size_t* bytes) {
+    if (!bytes || !dtype_ok(out_dtype)) return CIW_ERR_INVALID_ARG;
+    Geom g;
+    ciw_status s = resolve(desc, in_dtype, &g);
+    if (s != CIW_OK) return s;
+    if (in_dtype == CIW_F32 ? out_dtype != CIW_F32 : (out_dtype != in_dtype && out_dtype != CIW_F32))
+        return CIW_ERR_INVALID_ARG;
+    Epi epi;
+    epi.relu = (flags & CIW_FLAG_RELU) != 0;
+    epi.pool = (flags & CIW_FLAG_MAXPOOL2) != 0;
+    if (epi.pool && (g.P < 2 || g.Q < 2)) return CIW_ERR_INVALID_ARG;
+    if (g.G != 1 || in_dtype == CIW_F32) return CIW_ERR_UNSUPPORTED;
+    const size_t need = implicit_workspace_bytes(g, out_dtype, epi);
+    if (need == 0) return CIW_ERR_UNSUPPORTED;
+    *bytes = need;
     return CIW_OK;
 }
 

@@ -91,6 +91,15 @@ hipError_t launch_conv_mfma(const Geom& g, ciw_dtype in, ciw_dtype out, const vo
                             const void* w, const void* aperm, const void* bias, void* y,
                             int n_images, bool generic, const Epi& epi, hipStream_t st);
 
+// fp16/bf16 dense contraction that builds its window rows in LDS from x
+// (no window tensor in memory).  implicit_workspace_bytes is 0 for layers
+// the kernel does not run; otherwise the workspace holds the re-laid-out
+// filter, which launch_conv_implicit writes before the contraction.
+size_t implicit_workspace_bytes(const Geom& g, ciw_dtype out, const Epi& epi);
+hipError_t launch_conv_implicit(const Geom& g, ciw_dtype in, ciw_dtype out, const void* x,
+                                const void* w, const void* bias, void* y, void* ws,
+                                const Epi& epi, hipStream_t st);
+
 // Depthwise contraction over a CHW window tensor.
 hipError_t launch_conv_dw(const Geom& g, ciw_dtype in, ciw_dtype out, const void* xw,
                           const void* w, const void* bias, void* y, int n_images,

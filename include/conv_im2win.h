@@ -99,6 +99,18 @@ typedef struct {
                                        [N][K][P/2][Q/2] (floor; an odd last row or column
                                        is dropped).  CIW_ERR_INVALID_ARG if P or Q < 2. */
 
+/* On-the-fly window rows (conv2d_fwd, fp16/bf16 only).  The contraction
+ * kernel builds the window rows of each band of output rows in LDS straight
+ * from x and never writes the window tensor to memory; the result is the
+ * same sum in another order (the im2win paper's memory concern, §III-B and
+ * the processing strategies of §IV-D1, taken to its end: no window tensor).
+ * The workspace then holds only a re-laid-out copy of the filter
+ * (conv2d_implicit_workspace_bytes).  Layers the kernel does not run return
+ * CIW_ERR_UNSUPPORTED, see conv2d_implicit_workspace_bytes.  Not allowed
+ * with CIW_FLAG_WINDOW_READY or CIW_FLAG_GENERIC, nor for conv2d_dw_fwd
+ * (CIW_ERR_INVALID_ARG). */
+#define CIW_FLAG_IMPLICIT     0x20u
+
 /* Output extent: P = floor((H + 2 pad_h - dil_h (R-1) - 1) / stride_h) + 1,
  * Q likewise.  Returns CIW_ERR_INVALID_ARG if the descriptor is invalid or
  * the window does not fit the padded input. */
@@ -135,6 +147,16 @@ ciw_status conv_im2win_transform(const ciw_conv_desc* desc, ciw_dtype dtype,
 ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
                                   int64_t n_images, size_t* bytes);
 
+/* Workspace conv2d_fwd needs with CIW_FLAG_IMPLICIT for this layer, output
+ * type and epilogue flags (the re-laid-out filter; independent of N).
+ * CIW_ERR_UNSUPPORTED if the in-LDS kernel does not run the layer: it needs
+ * an fp16/bf16 input, groups == 1, C a multiple of 16, K <= 64, W a
+ * multiple of 8, stride_h == 1, a 3x3 filter with C <= 64 or a 1x1 filter
+ * with C in {16, 32, 64}, at most 1024 outputs of a row per 256 threads
+ * (K * Q), no CIW_FLAG_MAXPOOL2, and fewer than 2^31 bytes per image of x. */
+ciw_status conv2d_implicit_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
+                                           ciw_dtype out_dtype, uint32_t flags, size_t* bytes);
+
 /* Dense forward convolution (groups == 1), im2win method: for each batch
  * chunk, the repack into `workspace` followed by the windowed contraction
  * (the im2win paper §III-C..§III-F).  fp32 uses the CHW window layout and
@@ -143,7 +165,9 @@ ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
  * workspace (conv2d_workspace_bytes) fits in workspace_bytes, capped at N;
  * CIW_ERR_WORKSPACE if not even one image fits.  With
  * CIW_FLAG_WINDOW_READY the workspace must hold the full-batch window
- * tensor at offset 0 and be at least conv2d_workspace_bytes(desc, in, N). */
+ * tensor at offset 0 and be at least conv2d_workspace_bytes(desc, in, N).
+ * With CIW_FLAG_IMPLICIT the window rows are built in LDS instead (see that
+ * flag) and the workspace must hold conv2d_implicit_workspace_bytes. */
 ciw_status conv2d_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype out_dtype,
                       const void* x, const void* w, const void* bias, void* y,
                       void* workspace, size_t workspace_bytes, uint32_t flags,

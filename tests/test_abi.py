@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     assert tuple(names) == _lib.ENTRY_POINTS
 
 

@@ -1,0 +1,159 @@
+"""GPU parity of the in-LDS window path (conv2d_fwd with CIW_FLAG_IMPLICIT).
+
+The kernel builds its window rows in LDS from x and never writes the window
+tensor; it must meet the same bar as the materialised path against the fp64
+oracle: max|y - ref| <= 2e-2 * max|ref| for fp16/bf16 inputs.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_util import TOL, rel_err, sample_indices, to_dev, to_host_f64, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import cnn_convolution_im2win_amd as ciw  # noqa: E402
+
+CODE = {"f32": ciw.CIW_F32, "f16": ciw.CIW_F16, "bf16": ciw.CIW_BF16}
+IMP = ciw.CIW_FLAG_IMPLICIT
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(a, dt):
+    return None if a is None else workloads.to_f64(a, dt)
+
+
+def run(L, x, w, b, flags=IMP, out_dtype=None):
+    xd, wd, bd = to_dev(x, L.dtype), to_dev(w, L.dtype), to_dev(b, L.dtype)
+    od = torch_dtype(out_dtype or L.out_dtype)
+    y = ciw.conv2d(xd, wd, bd, L.stride, L.pad, L.dil, 1, out_dtype=od, flags=flags)
+    torch.cuda.synchronize()
+    return y
+
+
+def check(got, ref, what):
+    e = rel_err(got, ref)
+    say(f"  {what}: rel err {e:.3e}")
+    assert got.shape == ref.shape
+    assert np.all(np.isfinite(got))
+    assert e <= TOL["f16"], what
+
+
+RESNET = workloads.LAYERS["resnet_3x3_fp16"]
+
+
+@pytest.mark.parametrize("n", [1, 3])
+def test_resnet_layer_reduced_batch_full(n):
+    L = RESNET.replace(N=n)
+    say(f"implicit resnet_3x3_fp16 N={n}, every output")
+    x, w, b = workloads.make_inputs(L)
+    got = to_host_f64(run(L, x, w, b))
+    ref = oracle.conv2d(f64(x, "f16"), f64(w, "f16"), None, L.stride, L.pad, L.dil, 1)
+    check(got, ref, f"N={n}")
+
+
+def test_resnet_layer_full_size_sampled():
+    """The full batch in the launch configuration the benchmark times;
+    outputs checked at sampled points the oracle computes one by one, and
+    every output against the materialised path."""
+    L = RESNET
+    say("implicit resnet_3x3_fp16 full size, sampled")
+    x, w, b = workloads.make_inputs(L)
+    y = run(L, x, w, b)
+    got_all = to_host_f64(y)
+    rng = np.random.default_rng(91)
+    idx = sample_indices(got_all.shape, 3000, rng)
+    ref = oracle.conv2d_points(f64(x, "f16"), f64(w, "f16"), None, idx, L.stride, L.pad, L.dil, 1)
+    check(got_all[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]], ref, "sampled")
+    explicit = to_host_f64(run(L, x, w, b, flags=0))
+    check(got_all, explicit, "against the materialised path")
+
+
+# (N, C, H, W, K, R, stride_w, pad, dil) -- every combination of compiled
+# filter shape, channel-half count, partial pixel blocks, padding, stride and
+# dilation the kernel distinguishes
+SHAPES = [
+    (2, 16, 9, 16, 8, 3, 1, 1, 1),
+    (1, 32, 7, 24, 40, 3, 1, 1, 1),
+    (2, 48, 6, 8, 33, 3, 2, 2, 1),
+    (1, 64, 5, 40, 64, 3, 1, 1, 1),
+    (3, 64, 12, 32, 17, 3, 1, 1, 1),
+    (1, 16, 11, 16, 24, 3, 1, 2, 2),
+    (2, 32, 4, 8, 64, 1, 1, 0, 1),
+    (1, 64, 6, 72, 24, 1, 2, 1, 1),
+    (1, 16, 3, 8, 1, 1, 1, 0, 1),
+    (1, 64, 2, 8, 64, 3, 1, 1, 1),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("dtype,out", [("f16", "f16"), ("bf16", "bf16"), ("f16", "f32"),
+                                       ("bf16", "f32")])
+def test_shapes_against_oracle(shape, dtype, out):
+    N, C, H, W, K, R, sw, pad, dil = shape
+    L = workloads.Layer("imp", N=N, C=C, H=H, W=W, K=K, R=R, S=R, stride=(1, sw),
+                        pad=(pad, pad), dil=(dil, dil), dtype=dtype, out_dtype=out,
+                        x_dist=("normal", 0.0, 1.0), seed=sum(shape))
+    say(f"implicit {shape} {dtype}->{out}")
+    x, w, b = workloads.make_inputs(L)
+    got = to_host_f64(run(L, x, w, b))
+    ref = oracle.conv2d(f64(x, dtype), f64(w, dtype), f64(b, dtype), L.stride, L.pad, L.dil, 1)
+    check(got, ref, f"{shape} {dtype}->{out}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_relu_and_no_bias(dtype):
+    L = workloads.Layer("imp", N=2, C=64, H=10, W=16, K=48, R=3, S=3, stride=(1, 1),
+                        pad=(1, 1), dtype=dtype, out_dtype=dtype, x_dist=("normal", 0.0, 1.0),
+                        b_dist=None, seed=5)
+    x, w, _ = workloads.make_inputs(L)
+    got = to_host_f64(run(L, x, w, None, flags=IMP | ciw.CIW_FLAG_RELU))
+    ref = np.maximum(oracle.conv2d(f64(x, dtype), f64(w, dtype), None, L.stride, L.pad, L.dil, 1), 0)
+    check(got, ref, f"relu {dtype}")
+    assert np.all(got >= 0)
+
+
+def test_empty_batch():
+    L = RESNET.replace(N=0)
+    xd = torch.empty(L.x_shape, dtype=torch.float16, device="cuda")
+    wd = torch.zeros(L.w_shape, dtype=torch.float16, device="cuda")
+    y = ciw.conv2d(xd, wd, None, 1, 1, flags=IMP)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, 64, 56, 56)
+
+
+def test_errors():
+    def st(flags, dtype=torch.float16, C=64, W=56, sh=1, groups=1, ws_bytes=None):
+        x = torch.zeros((1, C, 8, W), dtype=dtype, device="cuda")
+        w = torch.zeros((C if groups > 1 else 64, C // groups, 3, 3), dtype=dtype, device="cuda")
+        desc = ciw.make_desc(x.shape, w.shape, (sh, 1), 1, 1, groups)
+        P, Q = ciw.conv2d_output_dims(desc, flags)
+        y = torch.empty((1, w.shape[0], P, Q), dtype=dtype, device="cuda")
+        ws = torch.empty(ws_bytes or (1 << 20), dtype=torch.uint8, device="cuda")
+        fn = ciw._lib.load().conv2d_dw_fwd if groups > 1 else ciw._lib.load().conv2d_fwd
+        import ctypes
+        code = {torch.float16: ciw.CIW_F16, torch.float32: ciw.CIW_F32}[dtype]
+        return fn(ctypes.byref(desc), code, code, x.data_ptr(), w.data_ptr(), None, y.data_ptr(),
+                  ws.data_ptr(), ws.numel(), flags, None)
+    assert st(IMP) == 0
+    assert st(IMP | ciw.CIW_FLAG_MAXPOOL2) == ciw._lib.CIW_ERR_UNSUPPORTED
+    assert st(IMP, C=24) == ciw._lib.CIW_ERR_UNSUPPORTED
+    assert st(IMP, W=52) == ciw._lib.CIW_ERR_UNSUPPORTED
+    assert st(IMP, sh=2) == ciw._lib.CIW_ERR_UNSUPPORTED
+    assert st(IMP, dtype=torch.float32) == ciw._lib.CIW_ERR_UNSUPPORTED
+    assert st(IMP | ciw.CIW_FLAG_WINDOW_READY) == ciw._lib.CIW_ERR_INVALID_ARG
+    assert st(IMP | ciw.CIW_FLAG_GENERIC) == ciw._lib.CIW_ERR_INVALID_ARG
+    assert st(IMP, groups=64) == ciw._lib.CIW_ERR_INVALID_ARG
+    assert st(IMP, ws_bytes=1024) == ciw._lib.CIW_ERR_WORKSPACE
+    torch.cuda.synchronize()

@@ -1,0 +1,346 @@
+"""CPU model of the in-LDS window kernel (conv_mfma_implicit_kernel).
+
+Host-logic test: the kernel's launch plan, every address it computes (row
+copies into the staging ring, the 8x8 transposes into the window-row
+buffers, the window-fragment reads, the output tile and the stores) and its
+hand-placed wait counts are replayed here in Python on small layers, each
+access bounds-checked against the buffer it must stay in.  The replay also
+carries the data: staged rows, transposed rows and the fragment products are
+evaluated in numpy and the result is compared with the fp64 oracle, so a
+wrong index (a transposed operand, a wrong tap or channel) fails here before
+the kernel ever runs on a GPU.  The plan is tied to the library through
+conv2d_implicit_workspace_bytes (eligibility and workspace size).
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+
+THREADS = 256
+MAX_COPIES = 4
+MAX_STORES = 4
+LDS_CU = 160 * 1024
+
+
+class G:   # resolved geometry, as the library's resolve() computes it
+    def __init__(self, N, C, H, W, K, R, S, sh=1, sw=1, ph=0, pw=0, dh=1, dw=1):
+        self.N, self.C, self.H, self.W, self.K, self.R, self.S = N, C, H, W, K, R, S
+        self.sh, self.sw, self.ph, self.pw, self.dh, self.dw = sh, sw, ph, pw, dh, dw
+        self.P = (H + 2 * ph - dh * (R - 1) - 1) // sh + 1
+        self.Q = (W + 2 * pw - dw * (S - 1) - 1) // sw + 1
+        self.Wwin = (self.Q - 1) * sw + dw * (S - 1) + 1
+
+
+def compiled(R, S, CB):
+    if (R, S) == (3, 3):
+        return 1 <= CB <= 4
+    if (R, S) == (1, 1):
+        return CB in (1, 2, 4)
+    return False
+
+
+def plan(g, out_bytes, relu=False, pool=False, cus=256):
+    if g.C % 16 or g.K > 64 or g.W % 8 or g.sh != 1 or pool:
+        return None
+    CB = g.C // 16
+    if not compiled(g.R, g.S, CB):
+        return None
+    if g.C * g.H * g.W * 2 >= 2 ** 31:
+        return None
+    a = dict(span=(g.R - 1) * g.dh + 1, cg=g.C // 8, wv=g.W // 8)
+    a["CS"] = a["cg"] | 1
+    wb = max(g.Wwin, g.pw + g.W)
+    a["wb"] = wb
+    a["row_bytes"] = wb * a["CS"] * 16
+    a["nchunks"] = g.C * g.W // 8
+    a["nd"] = -(-a["nchunks"] // THREADS)
+    if a["nd"] > MAX_COPIES:
+        return None
+    a["stage_bytes"] = max(a["nchunks"], THREADS) * 16
+    a["plane_bytes"] = g.H * g.W * 2
+    a["nblk"] = -(-g.Q // 32)
+    a["nkh"] = 2 if g.K > 32 else 1
+    V = 16 // out_bytes
+    ost = -(-(32 * a["nblk"]) // V) * V
+    if (ost * out_bytes // 16) % 2 == 0:
+        ost += V
+    a["ostride"] = ost
+    a["vec"] = 1 if g.Q % V == 0 else 0
+    a["nq"] = g.Q // V if a["vec"] else g.Q
+    a["nsv"] = -(-(g.K * a["nq"]) // THREADS)
+    if a["nsv"] > MAX_STORES:
+        return None
+    tile = 2 * g.K * ost * out_bytes
+    lds = wgs = pf = 0
+    for w in (2, 1):
+        for p in (3, 2, 1):
+            b = a["span"] * a["row_bytes"] + (p + 1) * a["stage_bytes"] + tile + 256
+            if b * w <= LDS_CU:
+                lds, wgs, pf = b, w, p
+                break
+        if wgs:
+            break
+    if not wgs:
+        return None
+    a.update(pf=pf, nstage=pf + 1, lds=lds, wgs=wgs, tile=tile)
+    a["off_stage"] = a["span"] * a["row_bytes"]
+    a["off_tile"] = a["off_stage"] + a["nstage"] * a["stage_bytes"]
+    a["off_bias"] = a["off_tile"] + tile
+    target = cus * wgs
+    nb = min(g.P, max(1, (target + g.N // 2) // max(g.N, 1)))
+    a["band"] = max(-(-g.P // nb), min(g.P, 4))
+    a["nbands"] = -(-g.P // a["band"])
+    a["ntask"] = g.N * a["nbands"]
+    a["steps"] = g.R * g.S * CB
+    a["CB"] = CB
+    a["out_bytes"] = out_bytes
+    return a
+
+
+def prep_filter(w16, g, a):
+    """mfma_implicit_filter_kernel: aperm[kh][s][lane][e]."""
+    steps, CB = a["steps"], a["CB"]
+    wbits = np.ascontiguousarray(w16).view(np.uint16)
+    out = np.zeros(2 * steps * 512, dtype=np.uint16)
+    for i in range(out.size):
+        e, lane, rest = i & 7, (i >> 3) & 63, i >> 9
+        kh, s = divmod(rest, steps)
+        k = kh * 32 + (lane & 31)
+        cb, q, r = s % CB, (s // CB) % g.S, s // (CB * g.S)
+        c = 16 * cb + 8 * (lane >> 5) + e
+        if k < g.K:
+            out[i] = wbits[k, c, r, q]
+    return out
+
+
+def later_ops(u, a, J):
+    pf, nd, nsv, span = a["pf"], a["nd"], a["nsv"], a["span"]
+    dma = lambda v: nd if v + pf < J else 0
+    st = lambda v: nsv if v >= span else 0
+    if u < pf:
+        c = nd * (min(pf, J) - 1 - u)
+        c += sum(dma(v) + st(v) for v in range(u))
+    else:
+        c = st(u - pf) + sum(dma(v) + st(v) for v in range(u - pf + 1, u))
+    return c
+
+
+def emulate(x16, w16, b, g, a, relu):
+    """Replays the kernel on the CPU; returns y (fp64, before output rounding
+    is applied by the caller) and checks every access."""
+    N, C, H, W, K = g.N, g.C, g.H, g.W, g.K
+    xbytes = x16.reshape(-1).view(np.uint8)
+    img_bytes = C * H * W * 2
+    aperm = prep_filter(w16, g, a)
+    y = np.full((N, K, g.P, g.Q), np.nan)
+    seen = np.zeros(a["ntask"], dtype=bool)
+    span, cg, CS, wv = a["span"], a["cg"], a["CS"], a["wv"]
+    nd, nchunks = a["nd"], a["nchunks"]
+    steps, CB = a["steps"], a["CB"]
+    # filter as the kernel's registers see it: F[kh][s] -> [lane][8]
+    Freg = aperm.reshape(2, steps, 64, 8).view(np.float16).astype(np.float64)
+    bias = np.zeros(64) if b is None else np.concatenate([b.astype(np.float64), np.zeros(64 - K)])
+    for blk in range(a["ntask"]):
+        task = (blk & 7) * (a["ntask"] >> 3) + (blk >> 3) if a["ntask"] % 8 == 0 else blk
+        assert 0 <= task < a["ntask"] and not seen[task]
+        seen[task] = True
+        n, band = divmod(task, a["nbands"])
+        h0 = band * a["band"]
+        rows = min(a["band"], g.P - h0)
+        J = rows + span - 1
+        lds = np.zeros(a["lds"], dtype=np.uint8)
+        # copy plan
+        pos_base, src_off = [], []
+        for j in range(MAX_COPIES):
+            pb = nchunks - THREADS if (j == nd - 1 and nd > 1) else j * THREADS
+            pos_base.append(pb)
+            offs = []
+            for tid in range(THREADS):
+                p = min(pb + tid, nchunks - 1)
+                gi, rest = p % cg, p // cg
+                offs.append((8 * gi + (rest & 7)) * a["plane_bytes"] + 16 * (rest >> 3))
+            src_off.append(offs)
+
+        def copy_row(j):
+            hin = min(max(h0 - g.ph + j, 0), H - 1)
+            src = n * img_bytes + hin * W * 2
+            slot0 = a["off_stage"] + (j % a["nstage"]) * a["stage_bytes"]
+            for jj in range(nd):
+                for tid in range(THREADS):
+                    wave, lane = divmod(tid, 64)
+                    dst = slot0 + 1024 * wave + 16 * pos_base[jj] + 16 * lane
+                    assert slot0 <= dst and dst + 16 <= slot0 + a["stage_bytes"]
+                    s0 = src_off[jj][tid]
+                    assert 0 <= s0 and hin * W * 2 + s0 + 16 <= img_bytes
+                    lds[dst:dst + 16] = xbytes[src + s0:src + s0 + 16]
+
+        def transpose_row(j):
+            hin = h0 - g.ph + j
+            inside = 0 <= hin < H
+            t0 = (j % span) * a["row_bytes"]
+            s0 = a["off_stage"] + (j % a["nstage"]) * a["stage_bytes"]
+            for it in range(cg * wv):
+                gi, xv = it % cg, it // cg
+                blk8 = np.zeros((8, 8), dtype=np.uint16)
+                for e in range(8):
+                    o = s0 + 16 * ((xv * 8 + e) * cg + gi)
+                    assert s0 <= o and o + 16 <= s0 + a["stage_bytes"]
+                    if inside:
+                        blk8[e] = lds[o:o + 16].view(np.uint16)
+                for c in range(8):   # column c of the vector: 8 channels
+                    o = t0 + 16 * ((g.pw + 8 * xv + c) * CS + gi)
+                    assert t0 <= o and o + 16 <= t0 + a["row_bytes"]
+                    lds[o:o + 16] = blk8[:, c].copy().view(np.uint8)
+
+        for j in range(min(a["pf"], J)):
+            copy_row(j)
+        assert later_ops(0, a, J) >= 0
+        for u in range(J):
+            assert later_ops(u, a, J) >= 0
+            transpose_row(u)
+            if u + a["pf"] < J:
+                copy_row(u + a["pf"])
+            i = u - span + 1
+            if i < 0:
+                continue
+            # the rows output row i reads are transposed by now
+            for r in range(g.R):
+                assert i + r * g.dh <= u
+            soff = [((i + r * g.dh) % span) * a["row_bytes"] for r in range(g.R)]
+            for kh in range(a["nkh"]):
+                for bb in range(a["nblk"]):
+                    acc = np.tile(bias[kh * 32:kh * 32 + 32], (32, 1))   # [pixel][channel]
+                    for s in range(steps):
+                        cb, q, r = s % CB, (s // CB) % g.S, s // (CB * g.S)
+                        A = np.zeros((32, 16))
+                        for lane in range(64):
+                            ml, gg = lane & 31, lane >> 5
+                            wr = min(32 * bb + ml, g.Q - 1)
+                            o = (wr * g.sw * CS + gg) * 16 + soff[r] + q * g.dw * CS * 16 + 32 * cb
+                            assert soff[r] <= o and o + 16 <= soff[r] + a["row_bytes"]
+                            A[ml, 8 * gg:8 * gg + 8] = lds[o:o + 16].view(np.float16).astype(np.float64)
+                        Bm = np.zeros((16, 32))
+                        for lane in range(64):
+                            Bm[8 * (lane >> 5):8 * (lane >> 5) + 8, lane & 31] = Freg[kh, s, lane]
+                        acc += A @ Bm
+                    if relu:
+                        acc = np.maximum(acc, 0)
+                    for ml in range(32):
+                        w_ = 32 * bb + ml
+                        assert w_ < a["ostride"]
+                        if w_ < g.Q:
+                            for kk in range(32):
+                                k = kh * 32 + kk
+                                if k < K:
+                                    y[n, k, h0 + i, w_] = acc[ml, kk]
+    assert seen.all()
+    return y
+
+
+def store_indices_ok(g, a):
+    """The store plan: every (k, vector) of an output row exactly covered,
+    reads inside the tile row, writes inside the output row block."""
+    E = (16 // a["out_bytes"]) if a["vec"] else 1
+    covered = set()
+    for tid in range(THREADS):
+        for j in range(a["nsv"]):
+            idx = min(tid + THREADS * j, g.K * a["nq"] - 1)
+            k, v = divmod(idx, a["nq"])
+            src, dst = k * a["ostride"] + v * E, k * g.P * g.Q + v * E
+            assert src + E <= g.K * a["ostride"] and (src + E - 1) // a["ostride"] == k
+            assert v * E + E <= g.Q and dst + E <= g.K * g.P * g.Q
+            covered.add((k, v))
+    assert len(covered) == g.K * a["nq"]
+
+
+CASES = [
+    # N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw
+    (1, 16, 5, 8, 8, 3, 3, 1, 1, 1, 1, 1, 1),
+    (2, 32, 7, 16, 40, 3, 3, 1, 1, 1, 1, 1, 1),
+    (1, 64, 6, 8, 64, 3, 3, 1, 1, 0, 0, 1, 1),
+    (2, 48, 5, 8, 33, 3, 3, 1, 2, 2, 1, 1, 1),
+    (1, 16, 9, 16, 24, 3, 3, 1, 1, 2, 2, 2, 2),
+    (3, 32, 4, 8, 64, 1, 1, 1, 1, 0, 0, 1, 1),
+    (1, 64, 3, 40, 64, 3, 3, 1, 1, 1, 1, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("out_bytes,cus", [(2, 256), (4, 256), (2, 1)])
+def test_emulated_kernel_matches_oracle(case, out_bytes, cus):
+    N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw = case
+    g = G(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw)
+    a = plan(g, out_bytes, cus=cus)
+    assert a is not None
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((N, C, H, W)).astype(np.float16)
+    w = (rng.standard_normal((K, C, R, S)) * 0.2).astype(np.float16)
+    b = rng.uniform(-0.1, 0.1, K).astype(np.float16)
+    relu = out_bytes == 4
+    got = emulate(x, w, b, g, a, relu)
+    ref = oracle.conv2d(x.astype(np.float64), w.astype(np.float64), b.astype(np.float64),
+                        (sh, sw), (ph, pw), (dh, dw), 1)
+    if relu:
+        ref = np.maximum(ref, 0)
+    assert not np.isnan(got).any()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-9 * max(1.0, np.abs(ref).max()))
+    store_indices_ok(g, a)
+
+
+@pytest.mark.parametrize("out_bytes", [2, 4])
+def test_plan_resnet_layer(out_bytes):
+    """The 128x64x56x56 -> 64 3x3 layer: two workgroups per CU, 512 bands of
+    14 rows, every address of a whole band in bounds (one task replayed
+    per image position: first, middle, last band)."""
+    g = G(128, 64, 56, 56, 64, 3, 3, 1, 1, 1, 1, 1, 1)
+    a = plan(g, out_bytes)
+    assert a is not None and a["wgs"] == 2 and a["ntask"] == 512 and a["band"] == 14
+    assert a["lds"] * 2 <= LDS_CU
+    store_indices_ok(g, a)
+    for u in range(a["band"] + a["span"] - 1):
+        assert later_ops(u, a, a["band"] + a["span"] - 1) >= 0
+
+
+def test_plan_agrees_with_library():
+    """Eligibility and workspace: this model's plan and the library agree."""
+    import cnn_convolution_im2win_amd as ciw
+    from cnn_convolution_im2win_amd import _lib
+    rng = np.random.default_rng(3)
+    shapes = list(CASES) + [
+        (128, 64, 56, 56, 64, 3, 3, 1, 1, 1, 1, 1, 1),
+        (1, 24, 8, 8, 8, 3, 3, 1, 1, 1, 1, 1, 1),      # C not a multiple of 16
+        (1, 16, 8, 12, 8, 3, 3, 1, 1, 1, 1, 1, 1),     # W not a multiple of 8
+        (1, 16, 8, 8, 80, 3, 3, 1, 1, 1, 1, 1, 1),     # K > 64
+        (1, 16, 9, 8, 8, 3, 3, 2, 1, 1, 1, 1, 1),      # stride_h 2
+        (1, 80, 8, 8, 8, 3, 3, 1, 1, 1, 1, 1, 1),      # C/16 = 5 not compiled
+        (1, 16, 8, 8, 8, 5, 5, 1, 1, 2, 2, 1, 1),      # 5x5 not compiled
+        (1, 32, 8, 8, 8, 1, 1, 1, 1, 0, 0, 1, 1),
+        (1, 48, 8, 8, 8, 1, 1, 1, 1, 0, 0, 1, 1),      # 1x1 with C/16 = 3 not compiled
+        (2, 64, 4, 256, 64, 3, 3, 1, 1, 1, 1, 1, 1),   # too many stores per thread
+    ]
+    for _ in range(40):
+        C = int(rng.choice([16, 32, 48, 64]))
+        R = int(rng.choice([1, 3]))
+        shapes.append((int(rng.integers(1, 4)), C, int(rng.integers(3, 20)),
+                       8 * int(rng.integers(1, 12)), int(rng.integers(1, 70)), R, R, 1,
+                       int(rng.integers(1, 3)), int(rng.integers(0, 3)),
+                       int(rng.integers(0, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 3))))
+    for s in shapes:
+        N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw = s
+        g = G(*s)
+        if g.P < 1 or g.Q < 1:
+            continue
+        desc = ciw.make_desc((N, C, H, W), (K, C, R, S), (sh, sw), (ph, pw), (dh, dw), 1)
+        for dt, ob in ((ciw.CIW_F16, 2), (ciw.CIW_BF16, 2), (ciw.CIW_F16, 4)):
+            out_dt = dt if ob == 2 else ciw.CIW_F32
+            a = plan(g, ob)
+            out = ctypes.c_size_t()
+            st = _lib.load().conv2d_implicit_workspace_bytes(ctypes.byref(desc), dt, out_dt, 0,
+                                                             ctypes.byref(out))
+            if a is None:
+                assert st == _lib.CIW_ERR_UNSUPPORTED, s
+            else:
+                assert st == 0, s
+                assert out.value == 2 * a["steps"] * 512 * 2
