@@ -159,7 +159,15 @@ def test_misaligned_bias():
 
 def test_unknown_flags():
     assert call_fwd(valid_desc(), ws_bytes=1 << 30, flags=0x100) == _lib.CIW_ERR_INVALID_ARG
-    assert call_fwd(valid_desc(), ws_bytes=1 << 30, flags=0x20) == _lib.CIW_ERR_INVALID_ARG
+    assert call_fwd(valid_desc(), ws_bytes=1 << 30, flags=0x40) == _lib.CIW_ERR_INVALID_ARG
+
+
+def test_implicit_flag_host_checks():
+    # fp32 has no in-LDS window kernel; the flag combinations it forbids
+    assert call_fwd(valid_desc(), ws_bytes=1 << 30, flags=_lib.CIW_FLAG_IMPLICIT) == \
+        _lib.CIW_ERR_UNSUPPORTED
+    both = _lib.CIW_FLAG_IMPLICIT | _lib.CIW_FLAG_WINDOW_READY
+    assert call_fwd(valid_desc(), ws_bytes=1 << 30, flags=both) == _lib.CIW_ERR_INVALID_ARG
 
 
 def test_pooled_output_dims_match_oracle():
