@@ -378,6 +378,51 @@ def memory_report(L: workloads.Layer, steps: int = 5) -> dict:
     return out
 
 
+def time_implicit(step: Step, steps: int, warmup: int):
+    """conv2d_fwd with CIW_FLAG_IMPLICIT (window rows built in LDS from x,
+    filter re-layout included) on the step's stream, K timed calls with HIP
+    events; None when the layer is not one that kernel runs."""
+    import statistics
+    import torch
+    ciw = step.ciw
+    flags = ciw.CIW_FLAG_IMPLICIT | step.epi_flags
+    try:
+        nbytes = ciw.conv2d_implicit_workspace_bytes(step.desc, step.in_code, step.out_code, flags)
+    except ciw.Im2winError:
+        return None
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    args = (step.dref, step.in_code, step.out_code, step.x.data_ptr(), step.w.data_ptr(),
+            None if step.b is None else step.b.data_ptr(), step.y.data_ptr(), ws.data_ptr(),
+            nbytes, flags, step.sp)
+
+    def call():
+        st = step.fn(*args)
+        if st != 0:
+            raise RuntimeError(f"conv2d_fwd (implicit): status {st}")
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(step.stream)
+        call()
+        ev[i][1].record(step.stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
+    fl = step.flops()
+    byt = step.bytes_x() + step.bytes_w() + step.bytes_b() + step.bytes_y()
+    return {
+        "step_ms": round(wall, 5),
+        "call_ms": round(ms, 5),
+        "tflops": round(fl / (wall * 1e-3) / 1e12, 3),
+        "mfma_frac": round(fl / (wall * 1e-3) / 1e12 / PEAK_TFLOPS["mfma_" + step.L.dtype], 4),
+        "hbm_gbs": round(byt / (wall * 1e-3) / 1e9, 1),
+        "hbm_bytes": byt,
+    }
+
+
 def measure_layer(L: workloads.Layer, steps: int, warmup: int, epilogue: str = "none",
                   unfused: bool = True) -> dict:
     import statistics
@@ -398,6 +443,9 @@ def measure_layer(L: workloads.Layer, steps: int, warmup: int, epilogue: str = "
     res["roofline"]["traffic"] = stored_traffic(traffic_key(L, epilogue))
     if not step.depthwise and L.dtype != "f32":
         res["mfma_frac"] = round(res["contract_tflops"] / PEAK_TFLOPS["mfma_" + L.dtype], 4)
+        imp = time_implicit(step, steps, warmup)
+        if imp is not None:
+            res["implicit"] = imp
     if epilogue != "none":
         res["epilogue"] = epilogue
         res["output_bytes"] = step.bytes_y()

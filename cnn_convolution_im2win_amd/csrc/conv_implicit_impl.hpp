@@ -41,6 +41,7 @@ struct MfImpArgs {
     int span;            // input rows one output row reads: (R - 1) * dil_h + 1
     int CS;              // 16-byte chunks per column of a window-row buffer (odd)
     int row_bytes;       // bytes of one window-row buffer
+    int nt;              // window-row buffers: span + 1
     int stage_bytes;     // bytes of one staged input row
     int nstage, pf;      // staging buffers, input rows copied ahead (nstage = pf + 1)
     int nd;              // copy instructions per wave per input row
@@ -180,24 +181,33 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
         }
     };
 
-    // ---- staged row j -> window-row buffer j % span, [column][channel]
+    // ---- staged row j -> window-row buffer j % nt, [column][channel].
+    // Piece (jp, gi, xv): channels 8 gi .. 8 gi + 7 at columns 8 xv + 2 jp
+    // and 8 xv + 2 jp + 1, one dword of each channel in, one 16-byte chunk
+    // per column out; the pieces of a row are spread over every thread.
     auto transpose_row = [&](int j) {
         const int hin = h0 - a.ph + j;
         const bool inside = hin >= 0 && hin < a.H;
-        char* trow = lb + (j % a.span) * a.row_bytes;
+        char* trow = lb + (j % a.nt) * a.row_bytes;
         const char* srow = lb + a.off_stage + (j % a.nstage) * a.stage_bytes;
-        for (int it = tid; it < a.cg * a.wv; it += kThreads) {
-            const int gi = it % a.cg;
-            const int xv = it / a.cg;
-            uint4 in[8], out[8];
+        for (int it = tid; it < 4 * a.cg * a.wv; it += kThreads) {
+            const int jp = it & 3;
+            const int rest = it >> 2;
+            const int gi = rest % a.cg;
+            const int xv = rest / a.cg;
+            uint32_t v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                in[e] = inside ? *reinterpret_cast<const uint4*>(srow + 16 * ((xv * 8 + e) * a.cg + gi))
-                               : make_uint4(0u, 0u, 0u, 0u);
-            transpose8x8(in, out);
-            char* dst = trow + 16 * ((a.pw + 8 * xv) * a.CS + gi);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(dst + 16 * a.CS * c) = out[c];
+                v[e] = inside ? *reinterpret_cast<const uint32_t*>(srow + 16 * ((xv * 8 + e) * a.cg + gi) + 4 * jp)
+                              : 0u;
+            // column 2 jp: low halves; column 2 jp + 1: high halves
+            const uint4 lo = make_uint4((v[0] & 0xffffu) | (v[1] << 16), (v[2] & 0xffffu) | (v[3] << 16),
+                                        (v[4] & 0xffffu) | (v[5] << 16), (v[6] & 0xffffu) | (v[7] << 16));
+            const uint4 hi = make_uint4((v[0] >> 16) | (v[1] & 0xffff0000u), (v[2] >> 16) | (v[3] & 0xffff0000u),
+                                        (v[4] >> 16) | (v[5] & 0xffff0000u), (v[6] >> 16) | (v[7] & 0xffff0000u));
+            char* dst = trow + 16 * ((a.pw + 8 * xv + 2 * jp) * a.CS + gi);
+            *reinterpret_cast<uint4*>(dst) = lo;
+            *reinterpret_cast<uint4*>(dst + 16 * a.CS) = hi;
         }
     };
 
@@ -232,59 +242,64 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
         }
     };
 
-    // prologue: copies of the first pf input rows; zero every window-row
-    // buffer (padding columns stay zero: the transpose writes only columns
+    // prologue: copies of input rows 0 .. pf; zero every window-row buffer
+    // (padding columns stay zero: the transpose writes only columns
     // pw .. pw + W - 1)
-    for (int j = 0; j < a.pf && j < J; ++j) copy_row(j);
-    for (int o = 16 * tid; o < a.span * a.row_bytes; o += 16 * kThreads)
+    for (int j = 0; j <= a.pf && j < J; ++j) copy_row(j);
+    for (int o = 16 * tid; o < a.nt * a.row_bytes; o += 16 * kThreads)
         *reinterpret_cast<uint4*>(lb + o) = make_uint4(0u, 0u, 0u, 0u);
-    wg_barrier_lds();
-    const float bias_k = bias_l[kh * 32 + ml];
     f32x16 bias_vec;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) bias_vec[i] = bias_k;
 
     // byte offsets of the filter columns q within a buffer
     int coff[S];
 #pragma unroll
     for (int q = 0; q < S; ++q) coff[q] = q * a.dw * a.CS * 16;
 
-    // Vector-memory operations this wave issues after the copy of row u:
-    // copies of later rows and output stores, in issue order (prologue
-    // copies; then per step v the copy of row v + pf, then the stores of
-    // output row v - span).  Waiting for at most that many lets them stay
-    // in flight.
-    auto dma_of = [&](int v) { return v + a.pf < J ? a.nd : 0; };
+    // Vector-memory operations this wave issues after the copy of row j:
+    // copies of later rows and output stores, in issue order (the prologue
+    // copies rows 0 .. pf; step v copies row v + pf + 1, then stores output
+    // row v - span).  Waiting for at most that many lets them stay in
+    // flight.
+    auto dma_of = [&](int v) { return v + a.pf + 1 < J ? a.nd : 0; };
     auto st_of = [&](int v) { return v >= a.span ? a.nsv : 0; };
-    auto later_ops = [&](int u) {
+    auto later_ops = [&](int j) {
         int c = 0;
-        if (u < a.pf) {
-            c = a.nd * (min(a.pf, J) - 1 - u);
-            for (int v = 0; v < u; ++v) c += dma_of(v) + st_of(v);
+        if (j <= a.pf) {
+            c = a.nd * (min(a.pf + 1, J) - 1 - j);
+            for (int v = 0; v < j - 1; ++v) c += dma_of(v) + st_of(v);
         } else {
-            c = st_of(u - a.pf);
-            for (int v = u - a.pf + 1; v < u; ++v) c += dma_of(v) + st_of(v);
+            c = st_of(j - a.pf - 1);
+            for (int v = j - a.pf; v < j - 1; ++v) c += dma_of(v) + st_of(v);
         }
         return c;
     };
 
-    // Step u: row u's copy has landed (wait, barrier); transpose it into
-    // buffer u % span; issue the copy of row u + pf into the staging buffer
-    // row u - 1 used; barrier; store output row i - 1 from its tile while
-    // output row i = u - span + 1 multiplies into the other tile.
+    // row 0 into its buffer, once every buffer is zeroed (and the bias
+    // staged)
+    wait_vm_lgkm(later_ops(0));
+    wg_barrier();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) bias_vec[e] = bias_l[kh * 32 + ml];
+    transpose_row(0);
+
+    // Step u: row u + 1's copy has landed and every wave is done with step
+    // u - 1 (wait, barrier); copy row u + pf + 1 into the staging buffer row
+    // u used; store output row i - 1 from its tile; transpose row u + 1 into
+    // the buffer output row i - 1 used; multiply output row i = u - span + 1
+    // (rows i .. u, transposed in earlier steps) into the other tile.  One
+    // barrier a step: transposes and multiplies of different waves overlap.
     for (int u = 0; u < J; ++u) {
-        wait_vm_lgkm(later_ops(u));
+        wait_vm_lgkm(u + 1 < J ? later_ops(u + 1) : 0);
         wg_barrier();
-        transpose_row(u);
-        if (u + a.pf < J) copy_row(u + a.pf);
-        wg_barrier_lds();
+        if (u + a.pf + 1 < J) copy_row(u + a.pf + 1);
         const int i = u - a.span + 1;
         if (i >= 1) store_row(i - 1);
+        if (u + 1 < J) transpose_row(u + 1);
         if (i < 0) continue;
 
         int soff[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) soff[r] = ((i + r * a.dh) % a.span) * a.row_bytes;
+        for (int r = 0; r < R; ++r) soff[r] = ((i + r * a.dh) % a.nt) * a.row_bytes;
         TOut* tile = tile0 + (i & 1) * tile_elems;
         for (int b = pb0; b < a.nblk; b += npb) {
             // pixels past the row end read the last pixel (never stored)
@@ -312,9 +327,12 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
             }
             // lane holds channel k = 32 kh + ml at block pixels
             // 8 (i / 4) + 4 g + i % 4
+            // ReLU as maxNum against 0.  fmaxf, not inline asm: a vector
+            // instruction reading a fresh MFMA result needs wait states the
+            // compiler inserts only for instructions it sees
             if (a.relu) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[e] = max_q(acc[e], 0.f);
+                for (int e = 0; e < 16; ++e) acc[e] = fmaxf(acc[e], 0.f);
             }
             const int k = kh * 32 + ml;
             if (k < a.K) {
@@ -362,6 +380,7 @@ inline bool mf_imp_plan(const Geom& g, int out_bytes, const Epi& epi, int cus, M
     a.cg = g.C / 8;
     a.wv = g.W / 8;
     a.CS = a.cg | 1;   // an odd chunk stride: consecutive pixels hit distinct banks
+    a.nt = a.span + 1;
     const int wb = std::max(g.Wwin, g.pw + g.W);
     a.row_bytes = wb * a.CS * 16;
     a.nchunks = g.C * g.W / 8;
@@ -386,7 +405,7 @@ inline bool mf_imp_plan(const Geom& g, int out_bytes, const Epi& epi, int cus, M
     int wgs = 0, pf = 0;
     for (int w = 2; w >= 1 && wgs == 0; --w)
         for (int p = 3; p >= 1; --p) {
-            const size_t bytes = (size_t)a.span * a.row_bytes + (size_t)(p + 1) * a.stage_bytes + tile + 256;
+            const size_t bytes = (size_t)a.nt * a.row_bytes + (size_t)(p + 1) * a.stage_bytes + tile + 256;
             if (bytes * w <= 160 * 1024) {
                 lds = bytes;
                 wgs = w;
@@ -397,7 +416,7 @@ inline bool mf_imp_plan(const Geom& g, int out_bytes, const Epi& epi, int cus, M
     if (wgs == 0) return false;
     a.pf = pf;
     a.nstage = pf + 1;
-    a.off_stage = a.span * a.row_bytes;
+    a.off_stage = a.nt * a.row_bytes;
     a.off_tile = a.off_stage + a.nstage * a.stage_bytes;
     a.off_bias = a.off_tile + (int)tile;
     // bands: about wgs_per_cu workgroups per CU in total, and at least 4

@@ -78,3 +78,41 @@ def test_graph_replays_match_eager(name):
         torch.cuda.synchronize()
         got = to_host_bits(y)
         assert np.array_equal(got, ref), f"{name}: replay {rep} differs from the eager result"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_graph_replays_match_eager_implicit(dtype):
+    """conv2d_fwd with the window rows built in LDS (filter re-layout, then
+    the contraction) captured and replayed the same way."""
+    L = workloads.LAYERS["resnet_3x3_fp16"].replace(N=4, dtype=dtype, out_dtype=dtype)
+    say(f"graph replay implicit {dtype} N={L.N}")
+    lib = _lib.load()
+    x, w, _ = (to_dev(a, L.dtype) for a in workloads.make_inputs(L))
+    desc = ciw.make_desc(L.x_shape, L.w_shape, L.stride, L.pad, L.dil, 1)
+    y = torch.empty((L.N, L.K, 56, 56), dtype=torch_dtype(dtype), device="cuda")
+    flags = ciw.CIW_FLAG_IMPLICIT | ciw.CIW_FLAG_RELU
+    ws_bytes = ciw.conv2d_implicit_workspace_bytes(desc, CODE[dtype], CODE[dtype], flags)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+
+    def step():
+        st = lib.conv2d_fwd(ctypes.byref(desc), CODE[dtype], CODE[dtype], x.data_ptr(), w.data_ptr(),
+                            None, y.data_ptr(), ws.data_ptr(), ws_bytes, flags, s.cuda_stream)
+        assert st == 0
+
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    ref = to_host_bits(y).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s, capture_error_mode="relaxed"):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        with torch.cuda.stream(s):
+            y.view(torch.uint8).fill_(0x5A)
+            ws.fill_((29 * rep + 3) & 0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(y), ref), f"implicit {dtype}: replay {rep} differs"

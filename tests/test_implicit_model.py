@@ -50,6 +50,7 @@ def plan(g, out_bytes, relu=False, pool=False, cus=256):
     if g.C * g.H * g.W * 2 >= 2 ** 31:
         return None
     a = dict(span=(g.R - 1) * g.dh + 1, cg=g.C // 8, wv=g.W // 8)
+    a["nt"] = a["span"] + 1
     a["CS"] = a["cg"] | 1
     wb = max(g.Wwin, g.pw + g.W)
     a["wb"] = wb
@@ -76,7 +77,7 @@ def plan(g, out_bytes, relu=False, pool=False, cus=256):
     lds = wgs = pf = 0
     for w in (2, 1):
         for p in (3, 2, 1):
-            b = a["span"] * a["row_bytes"] + (p + 1) * a["stage_bytes"] + tile + 256
+            b = a["nt"] * a["row_bytes"] + (p + 1) * a["stage_bytes"] + tile + 256
             if b * w <= LDS_CU:
                 lds, wgs, pf = b, w, p
                 break
@@ -85,7 +86,7 @@ def plan(g, out_bytes, relu=False, pool=False, cus=256):
     if not wgs:
         return None
     a.update(pf=pf, nstage=pf + 1, lds=lds, wgs=wgs, tile=tile)
-    a["off_stage"] = a["span"] * a["row_bytes"]
+    a["off_stage"] = a["nt"] * a["row_bytes"]
     a["off_tile"] = a["off_stage"] + a["nstage"] * a["stage_bytes"]
     a["off_bias"] = a["off_tile"] + tile
     target = cus * wgs
@@ -115,16 +116,35 @@ def prep_filter(w16, g, a):
     return out
 
 
-def later_ops(u, a, J):
+def later_ops(j, a, J):
+    """Vector-memory operations a wave issues after the copy of row j, up to
+    the wait for it (prologue copies rows 0..pf; step v copies row
+    v + pf + 1, then stores output row v - span)."""
     pf, nd, nsv, span = a["pf"], a["nd"], a["nsv"], a["span"]
-    dma = lambda v: nd if v + pf < J else 0
+    dma = lambda v: nd if v + pf + 1 < J else 0
     st = lambda v: nsv if v >= span else 0
-    if u < pf:
-        c = nd * (min(pf, J) - 1 - u)
-        c += sum(dma(v) + st(v) for v in range(u))
+    if j <= pf:
+        c = nd * (min(pf + 1, J) - 1 - j)
+        c += sum(dma(v) + st(v) for v in range(j - 1))
     else:
-        c = st(u - pf) + sum(dma(v) + st(v) for v in range(u - pf + 1, u))
+        c = st(j - pf - 1) + sum(dma(v) + st(v) for v in range(j - pf, j - 1))
     return c
+
+
+def issue_log(a, J):
+    """The kernel's vector-memory issue order for one band: ('dma', row) and
+    ('st', output row) events, and the index of each wait's target."""
+    log = [("dma", j) for j in range(min(a["pf"] + 1, J))]
+    waits = {0: len(log)}
+    for v in range(J):
+        if v + 1 < J:
+            waits[v + 1] = len(log)
+        if v + a["pf"] + 1 < J:
+            log += [("dma", v + a["pf"] + 1)] * 1
+        i = v - a["span"] + 1
+        if i >= 1:
+            log += [("st", i - 1)]
+    return log, waits
 
 
 def emulate(x16, w16, b, g, a, relu):
@@ -179,36 +199,51 @@ def emulate(x16, w16, b, g, a, relu):
         def transpose_row(j):
             hin = h0 - g.ph + j
             inside = 0 <= hin < H
-            t0 = (j % span) * a["row_bytes"]
+            t0 = (j % a["nt"]) * a["row_bytes"]
             s0 = a["off_stage"] + (j % a["nstage"]) * a["stage_bytes"]
-            for it in range(cg * wv):
-                gi, xv = it % cg, it // cg
-                blk8 = np.zeros((8, 8), dtype=np.uint16)
+            for it in range(4 * cg * wv):
+                jp, rest = it & 3, it >> 2
+                gi, xv = rest % cg, rest // cg
+                v = np.zeros((8, 2), dtype=np.uint16)   # [channel e][column 2jp + c]
                 for e in range(8):
-                    o = s0 + 16 * ((xv * 8 + e) * cg + gi)
-                    assert s0 <= o and o + 16 <= s0 + a["stage_bytes"]
+                    o = s0 + 16 * ((xv * 8 + e) * cg + gi) + 4 * jp
+                    assert s0 <= o and o + 4 <= s0 + a["stage_bytes"]
                     if inside:
-                        blk8[e] = lds[o:o + 16].view(np.uint16)
-                for c in range(8):   # column c of the vector: 8 channels
-                    o = t0 + 16 * ((g.pw + 8 * xv + c) * CS + gi)
+                        v[e] = lds[o:o + 4].view(np.uint16)
+                for c in range(2):
+                    o = t0 + 16 * ((g.pw + 8 * xv + 2 * jp + c) * CS + gi)
                     assert t0 <= o and o + 16 <= t0 + a["row_bytes"]
-                    lds[o:o + 16] = blk8[:, c].copy().view(np.uint8)
+                    lds[o:o + 16] = v[:, c].copy().view(np.uint8)
 
-        for j in range(min(a["pf"], J)):
+        for j in range(min(a["pf"] + 1, J)):
             copy_row(j)
-        assert later_ops(0, a, J) >= 0
+        # the wait counts: the op waited for is exactly later_ops back from
+        # the end of what has been issued
+        log, waits = issue_log(a, J)
+        for j, pos in waits.items():
+            ops = [e for e in log[:pos]]
+            k = max(idx for idx, e in enumerate(ops) if e == ("dma", j))
+            assert sum(nd if e[0] == "dma" else a["nsv"] for e in ops[k + 1:]) == later_ops(j, a, J)
+        transpose_row(0)
+        done = {0}
         for u in range(J):
-            assert later_ops(u, a, J) >= 0
-            transpose_row(u)
-            if u + a["pf"] < J:
-                copy_row(u + a["pf"])
+            if u + a["pf"] + 1 < J:
+                # the staging buffer it overwrites held row u, transposed already
+                assert u in done
+                copy_row(u + a["pf"] + 1)
             i = u - span + 1
+            if u + 1 < J:
+                # the buffer it overwrites held row u + 1 - nt, whose last reader
+                # (output row u + 1 - nt) was multiplied in an earlier step
+                assert u + 1 - a["nt"] < i or u + 1 - a["nt"] < 0
+                transpose_row(u + 1)
+                done.add(u + 1)
             if i < 0:
                 continue
-            # the rows output row i reads are transposed by now
+            # the rows output row i reads were transposed in earlier steps
             for r in range(g.R):
-                assert i + r * g.dh <= u
-            soff = [((i + r * g.dh) % span) * a["row_bytes"] for r in range(g.R)]
+                assert i + r * g.dh <= u and (i + r * g.dh) in done
+            soff = [((i + r * g.dh) % a["nt"]) * a["row_bytes"] for r in range(g.R)]
             for kh in range(a["nkh"]):
                 for bb in range(a["nblk"]):
                     acc = np.tile(bias[kh * 32:kh * 32 + 32], (32, 1))   # [pixel][channel]
@@ -291,16 +326,19 @@ def test_emulated_kernel_matches_oracle(case, out_bytes, cus):
 
 @pytest.mark.parametrize("out_bytes", [2, 4])
 def test_plan_resnet_layer(out_bytes):
-    """The 128x64x56x56 -> 64 3x3 layer: two workgroups per CU, 512 bands of
-    14 rows, every address of a whole band in bounds (one task replayed
-    per image position: first, middle, last band)."""
+    """The 128x64x56x56 -> 64 3x3 layer: with fp16 output two workgroups per
+    CU and 512 bands of 14 rows; with fp32 output (a tile twice the size)
+    one workgroup per CU.  Store plan and wait counts valid."""
     g = G(128, 64, 56, 56, 64, 3, 3, 1, 1, 1, 1, 1, 1)
     a = plan(g, out_bytes)
-    assert a is not None and a["wgs"] == 2 and a["ntask"] == 512 and a["band"] == 14
-    assert a["lds"] * 2 <= LDS_CU
+    assert a is not None
+    if out_bytes == 2:
+        assert a["wgs"] == 2 and a["ntask"] == 512 and a["band"] == 14
+    assert a["lds"] * a["wgs"] <= LDS_CU
     store_indices_ok(g, a)
-    for u in range(a["band"] + a["span"] - 1):
-        assert later_ops(u, a, a["band"] + a["span"] - 1) >= 0
+    J = a["band"] + a["span"] - 1
+    for j in range(J):
+        assert later_ops(j, a, J) >= 0
 
 
 def test_plan_agrees_with_library():
