@@ -423,6 +423,44 @@ def time_implicit(step: Step, steps: int, warmup: int):
     }
 
 
+def time_fp32_kernels(step: Step, steps: int, warmup: int):
+    """The fp32 contraction (window ready) with each kernel forced: matrix
+    cores (CIW_FLAG_FP32_MFMA) and vector ALUs (CIW_FLAG_FP32_VALU), K timed
+    calls each with HIP events on the step's stream; the automatic choice is
+    the step's own contraction.  None for layers the matrix-core kernel does
+    not run."""
+    import statistics
+    import torch
+    ciw = step.ciw
+    L = step.L
+    if L.dtype != "f32" or step.depthwise or step.epilogue == "relu_pool" or \
+            L.R != L.S or L.R not in (1, 3) or step.Q > 192:
+        return None
+    step.transform()
+    out = {}
+    for name, flag in (("matrix", ciw.CIW_FLAG_FP32_MFMA), ("vector", ciw.CIW_FLAG_FP32_VALU)):
+        args = list(step.args_fwd)
+        args[9] = args[9] | flag
+
+        def call():
+            st = step.fn(*args)
+            if st != 0:
+                raise RuntimeError(f"conv2d_fwd ({name}): status {st}")
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(step.stream)
+            call()
+            ev[i][1].record(step.stream)
+        torch.cuda.synchronize()
+        ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
+        out[name] = {"contract_ms": round(ms, 5),
+                     "contract_tflops": round(step.flops() / (ms * 1e-3) / 1e12, 3)}
+    return out
+
+
 def measure_layer(L: workloads.Layer, steps: int, warmup: int, epilogue: str = "none",
                   unfused: bool = True) -> dict:
     import statistics
@@ -441,6 +479,9 @@ def measure_layer(L: workloads.Layer, steps: int, warmup: int, epilogue: str = "
         "roofline": step.contraction_roofline(co_ms),
     }
     res["roofline"]["traffic"] = stored_traffic(traffic_key(L, epilogue))
+    k32 = time_fp32_kernels(step, steps, warmup)
+    if k32 is not None:
+        res["fp32_kernels"] = k32
     if not step.depthwise and L.dtype != "f32":
         res["mfma_frac"] = round(res["contract_tflops"] / PEAK_TFLOPS["mfma_" + L.dtype], 4)
         imp = time_implicit(step, steps, warmup)

@@ -18,8 +18,9 @@ import ctypes
 from typing import Optional, Sequence, Tuple, Union
 
 from . import _lib
-from ._lib import (CIW_BF16, CIW_F16, CIW_F32, CIW_FLAG_GENERIC, CIW_FLAG_IMPLICIT,
-                   CIW_FLAG_MAXPOOL2,
+from ._lib import (CIW_BF16, CIW_F16, CIW_F32, CIW_FLAG_FP32_MFMA, CIW_FLAG_FP32_VALU,
+                   CIW_FLAG_GENERIC,
+                   CIW_FLAG_IMPLICIT, CIW_FLAG_MAXPOOL2,
                    CIW_FLAG_NO_SPLIT, CIW_FLAG_RELU, CIW_FLAG_WINDOW_READY, CIW_WIN_CHW,
                    CIW_WIN_HWC, ConvDesc, Im2winError, LIB_PATH, status_string)
 
@@ -32,7 +33,7 @@ __all__ = [
     "conv2d_workspace_bytes", "conv2d_implicit_workspace_bytes", "make_desc", "Im2winError", "status_string", "LIB_PATH",
     "CIW_F32", "CIW_F16", "CIW_BF16", "CIW_WIN_CHW", "CIW_WIN_HWC",
     "CIW_FLAG_WINDOW_READY", "CIW_FLAG_NO_SPLIT", "CIW_FLAG_GENERIC", "CIW_FLAG_RELU",
-    "CIW_FLAG_MAXPOOL2", "CIW_FLAG_IMPLICIT",
+    "CIW_FLAG_MAXPOOL2", "CIW_FLAG_IMPLICIT", "CIW_FLAG_FP32_MFMA", "CIW_FLAG_FP32_VALU",
 ]
 
 

@@ -26,6 +26,8 @@ CIW_FLAG_GENERIC = 0x4
 CIW_FLAG_RELU = 0x8
 CIW_FLAG_MAXPOOL2 = 0x10
 CIW_FLAG_IMPLICIT = 0x20
+CIW_FLAG_FP32_MFMA = 0x40
+CIW_FLAG_FP32_VALU = 0x80
 
 # the exported entry points, in header order
 ENTRY_POINTS = (

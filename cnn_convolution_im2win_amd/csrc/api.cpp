@@ -107,9 +107,10 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
     // allowed (in -> out) pairs
     if (in == CIW_F32 ? out != CIW_F32 : (out != in && out != CIW_F32)) return CIW_ERR_INVALID_ARG;
     if (flags & ~(CIW_FLAG_WINDOW_READY | CIW_FLAG_NO_SPLIT | CIW_FLAG_GENERIC | CIW_FLAG_RELU |
-                  CIW_FLAG_MAXPOOL2 | CIW_FLAG_IMPLICIT))
+                  CIW_FLAG_MAXPOOL2 | CIW_FLAG_IMPLICIT | CIW_FLAG_FP32_MFMA | CIW_FLAG_FP32_VALU))
         return CIW_ERR_INVALID_ARG;
     const bool implicit = (flags & CIW_FLAG_IMPLICIT) != 0;
+    if ((flags & CIW_FLAG_FP32_MFMA) && (flags & CIW_FLAG_FP32_VALU)) return CIW_ERR_INVALID_ARG;
     if (implicit && (depthwise || (flags & (CIW_FLAG_WINDOW_READY | CIW_FLAG_GENERIC))))
         return CIW_ERR_INVALID_ARG;
     Epi epi;
@@ -143,6 +144,8 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
     const ciw_win_layout lay = layout_of(p);
     const bool no_split = (flags & CIW_FLAG_NO_SPLIT) != 0;
     const bool generic = (flags & CIW_FLAG_GENERIC) != 0;
+    const Fp32Kernel fp32_kernel = (flags & CIW_FLAG_FP32_MFMA) ? FP32_MATRIX
+                                   : (flags & CIW_FLAG_FP32_VALU) ? FP32_VECTOR : FP32_AUTO;
 
     // chunk size: the most images whose workspace fits (the full batch if it does)
     int64_t nc = 0;
@@ -189,7 +192,7 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
             int splits = no_split ? 1 : fp32_splits(g, (int)nc);
             float* partials = (float*)(wsb + round_up(window_bytes_per_image(g, lay) * nc, 256));
             e = launch_conv_fp32(g, (const float*)wsb, (const float*)w, (const float*)bias,
-                                 (float*)yc, n, partials, splits, generic, epi, st);
+                                 (float*)yc, n, partials, splits, generic, fp32_kernel, epi, st);
         } else if (p == PATH_MFMA) {
             e = launch_conv_mfma(g, in, out, wsb, w, aperm, bias, yc, n, generic, epi, st);
         } else {

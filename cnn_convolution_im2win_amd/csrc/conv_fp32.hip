@@ -495,13 +495,24 @@ int fp32_splits(const Geom& g, int n_images) {
     // is cut down to this count at launch)
     int a = plan(g, n_images, false, Epi{}).splits;
     int b = plan(g, n_images, true, Epi{}).splits;
-    return a > b ? a : b;
+    int m = fp32_mfma_splits(g, n_images);
+    return std::max(std::max(a, b), m);
 }
 
 hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, const float* bias,
                             float* y, int n_images, float* partials, int max_splits,
-                            bool generic, const Epi& epi, hipStream_t st) {
+                            bool generic, Fp32Kernel kernel, const Epi& epi, hipStream_t st) {
     if (n_images == 0) return hipSuccess;
+    // the matrix-core kernel when it runs the layer (not with the pool, the
+    // single-pass request or the generic-kernel request): forced, or by
+    // default when its channel sum splits into at least 4 slices (below
+    // that the layer is too small to fill the GPU through it, and the
+    // vector kernel was measured faster)
+    if (kernel != FP32_VECTOR && !generic && !epi.pool && max_splits > 1) {
+        const int ms = fp32_mfma_splits(g, n_images);
+        if (ms > 0 && ms <= max_splits && (kernel == FP32_MATRIX || ms >= 4))
+            return launch_conv_fp32_mfma(g, xw, w, bias, y, n_images, partials, max_splits, epi, st);
+    }
     Fp32Plan p = plan(g, n_images, generic, epi);
     const int Po = out_rows(g, epi), Qo = out_cols(g, epi);
     if (max_splits <= 1) {   // single pass requested

@@ -75,10 +75,24 @@ hipError_t launch_transform(const Geom& g, ciw_dtype dt, ciw_win_layout lay, con
 // fp32 dense contraction over a CHW window tensor.  splits > 1 sums the
 // channels in `splits` slices into `partials` ([splits][n][K][P][Q] fp32)
 // and a second kernel reduces them in slice order (deterministic).
+// Kernel choice for the fp32 contraction: automatic (the matrix cores when
+// their plan has at least 4 channel slices), or forced.
+enum Fp32Kernel { FP32_AUTO = 0, FP32_MATRIX = 1, FP32_VECTOR = 2 };
 int fp32_splits(const Geom& g, int n_images);
 hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, const float* bias,
                             float* y, int n_images, float* partials, int splits, bool generic,
-                            const Epi& epi, hipStream_t st);
+                            Fp32Kernel kernel, const Epi& epi, hipStream_t st);
+
+// fp32 dense contraction over a CHW window tensor on the matrix cores (3x3
+// and 1x1 filters, output rows of at most 192 pixels, no pooling).
+// fp32_mfma_splits is its channel-slice count (partials [splits][n][K][P*Q]
+// in the workspace), 0 for layers it does not run; launch_conv_fp32 takes it
+// by the Fp32Kernel choice when it runs the layer in at most max_splits
+// slices.
+int fp32_mfma_splits(const Geom& g, int n_images);
+hipError_t launch_conv_fp32_mfma(const Geom& g, const float* xw, const float* w, const float* bias,
+                                 float* y, int n_images, float* partials, int max_splits,
+                                 const Epi& epi, hipStream_t st);
 
 // fp16/bf16 dense contraction over an HWC window tensor on the matrix cores.
 // The row kernel multiplies a re-laid-out copy of the filter (`aperm`,

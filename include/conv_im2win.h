@@ -110,6 +110,18 @@ typedef struct {
  * with CIW_FLAG_WINDOW_READY or CIW_FLAG_GENERIC, nor for conv2d_dw_fwd
  * (CIW_ERR_INVALID_ARG). */
 #define CIW_FLAG_IMPLICIT     0x20u
+/* fp32 dense (conv2d_fwd) kernel choice.  By default the contraction runs
+ * on the matrix cores (v_mfma_f32_32x32x2_f32) when that kernel runs the
+ * layer (3x3 and 1x1 filters, output rows of at most 192 pixels, no
+ * CIW_FLAG_MAXPOOL2) and its plan splits the channel sum into at least 4
+ * slices (a channel sum long enough to fill the GPU); otherwise on the
+ * vector ALUs.  CIW_FLAG_FP32_MFMA forces the matrix cores wherever that
+ * kernel runs the layer, CIW_FLAG_FP32_VALU forces the vector ALUs (both:
+ * CIW_ERR_INVALID_ARG).  Either way the sum is deterministic (slices added
+ * in a fixed order) and the same sum in another order.  Ignored for
+ * fp16/bf16; CIW_FLAG_GENERIC and CIW_FLAG_NO_SPLIT imply the vector ALUs. */
+#define CIW_FLAG_FP32_MFMA    0x40u
+#define CIW_FLAG_FP32_VALU    0x80u
 
 /* Output extent: P = floor((H + 2 pad_h - dil_h (R-1) - 1) / stride_h) + 1,
  * Q likewise.  Returns CIW_ERR_INVALID_ARG if the descriptor is invalid or

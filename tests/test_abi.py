@@ -159,7 +159,8 @@ def test_misaligned_bias():
 
 def test_unknown_flags():
     assert call_fwd(valid_desc(), ws_bytes=1 << 30, flags=0x100) == _lib.CIW_ERR_INVALID_ARG
-    assert call_fwd(valid_desc(), ws_bytes=1 << 30, flags=0x40) == _lib.CIW_ERR_INVALID_ARG
+    both = _lib.CIW_FLAG_FP32_MFMA | _lib.CIW_FLAG_FP32_VALU
+    assert call_fwd(valid_desc(), ws_bytes=1 << 30, flags=both) == _lib.CIW_ERR_INVALID_ARG
 
 
 def test_implicit_flag_host_checks():
