@@ -413,14 +413,17 @@ def time_implicit(step: Step, steps: int, warmup: int):
     ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
     fl = step.flops()
     byt = step.bytes_x() + step.bytes_w() + step.bytes_b() + step.bytes_y()
-    return {
+    res = {
         "step_ms": round(wall, 5),
         "call_ms": round(ms, 5),
         "tflops": round(fl / (wall * 1e-3) / 1e12, 3),
-        "mfma_frac": round(fl / (wall * 1e-3) / 1e12 / PEAK_TFLOPS["mfma_" + step.L.dtype], 4),
         "hbm_gbs": round(byt / (wall * 1e-3) / 1e9, 1),
+        "hbm_frac": round(byt / (wall * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "hbm_bytes": byt,
     }
+    if not step.depthwise:
+        res["mfma_frac"] = round(fl / (wall * 1e-3) / 1e12 / PEAK_TFLOPS["mfma_" + step.L.dtype], 4)
+    return res
 
 
 def time_fp32_kernels(step: Step, steps: int, warmup: int):
@@ -484,6 +487,7 @@ def measure_layer(L: workloads.Layer, steps: int, warmup: int, epilogue: str = "
         res["fp32_kernels"] = k32
     if not step.depthwise and L.dtype != "f32":
         res["mfma_frac"] = round(res["contract_tflops"] / PEAK_TFLOPS["mfma_" + L.dtype], 4)
+    if step.depthwise or L.dtype != "f32":
         imp = time_implicit(step, steps, warmup)
         if imp is not None:
             res["implicit"] = imp

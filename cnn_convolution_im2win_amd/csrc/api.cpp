@@ -111,8 +111,7 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
         return CIW_ERR_INVALID_ARG;
     const bool implicit = (flags & CIW_FLAG_IMPLICIT) != 0;
     if ((flags & CIW_FLAG_FP32_MFMA) && (flags & CIW_FLAG_FP32_VALU)) return CIW_ERR_INVALID_ARG;
-    if (implicit && (depthwise || (flags & (CIW_FLAG_WINDOW_READY | CIW_FLAG_GENERIC))))
-        return CIW_ERR_INVALID_ARG;
+    if (implicit && (flags & (CIW_FLAG_WINDOW_READY | CIW_FLAG_GENERIC))) return CIW_ERR_INVALID_ARG;
     Epi epi;
     epi.relu = (flags & CIW_FLAG_RELU) != 0;
     epi.pool = (flags & CIW_FLAG_MAXPOOL2) != 0;
@@ -121,6 +120,16 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
         if (!(g.G == g.C && g.K == g.C)) return g.G == 1 ? CIW_ERR_INVALID_ARG : CIW_ERR_UNSUPPORTED;
     } else if (g.G != 1) {
         return CIW_ERR_UNSUPPORTED;
+    }
+    if (implicit && depthwise) {
+        // windows built in LDS from x; no workspace
+        if (!dw_implicit_supported(g, epi)) return CIW_ERR_UNSUPPORTED;
+        if (g.N == 0) return CIW_OK;
+        if (!x || !w || !y || !aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) ||
+            (bias && !aligned(bias, elem_bytes(in))))
+            return CIW_ERR_INVALID_ARG;
+        (void)hipGetLastError();
+        return from_hip(launch_conv_dw_implicit(g, in, out, x, w, bias, y, epi, (hipStream_t)stream));
     }
     if (g.N == 0) return CIW_OK;   // empty batch: nothing to do
     const bool ready = (flags & CIW_FLAG_WINDOW_READY) != 0;
@@ -290,7 +299,12 @@ ciw_status conv2d_implicit_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype 
     epi.relu = (flags & CIW_FLAG_RELU) != 0;
     epi.pool = (flags & CIW_FLAG_MAXPOOL2) != 0;
     if (epi.pool && (g.P < 2 || g.Q < 2)) return CIW_ERR_INVALID_ARG;
-    if (g.G != 1 || in_dtype == CIW_F32) return CIW_ERR_UNSUPPORTED;
+    if (g.G > 1) {   // depthwise: no workspace
+        if (!(g.G == g.C && g.K == g.C) || !dw_implicit_supported(g, epi)) return CIW_ERR_UNSUPPORTED;
+        *bytes = 0;
+        return CIW_OK;
+    }
+    if (in_dtype == CIW_F32) return CIW_ERR_UNSUPPORTED;
     const size_t need = implicit_workspace_bytes(g, out_dtype, epi);
     if (need == 0) return CIW_ERR_UNSUPPORTED;
     *bytes = need;

@@ -1,0 +1,177 @@
+// conv_dw_implicit.hip -- depthwise convolution (groups = C = K) with the
+// windows built in LDS from x: no window tensor in memory.
+//
+// Depthwise work is a per-channel windowed dot product ("Diagonalwise
+// Refactorization", abstract: one filter per input channel), with about one
+// multiply-add per byte moved, so the HBM traffic decides its time.  The
+// materialised path writes the window tensor (about R/stride_h times x) and
+// reads it back; here a workgroup copies a run of whole input planes
+// (n, c), which are contiguous in NCHW, into LDS with zero padding around
+// each plane, so every window of the im2win paper (§III-C: for output
+// (h, w), the R x S inputs at rows h*stride_h + r*dil_h, columns
+// w*stride_w + q*dil_w of the padded plane) is read from LDS, and x and y
+// each cross HBM once.  Loads and stores are consecutive across lanes.
+// The epilogue is the library's: bias in fp32, optional ReLU (maxNum
+// against 0) and 2x2 max-pool, one rounding to the output type.
+#include <algorithm>
+
+#include "internal.hpp"
+#include "device_common.hpp"
+
+namespace ciw {
+namespace {
+
+constexpr int kDThreads = 256;
+constexpr int kDwLdsBytes = 48 * 1024;   // staged planes per workgroup: at most this
+
+struct DwImpArgs {
+    int C, H, W, P, Q, R, S;
+    int sh, sw, ph, pw, dh, dw;
+    int Hp, Wp;          // padded plane extent in LDS
+    int planes;          // total planes N * C
+    int per;             // planes per workgroup
+    int Po, Qo;          // output extent (pooled or not)
+    int relu, pool;
+    FastDiv fdHW, fdW, fdPQo, fdQo;
+};
+
+template <typename TIn, typename TOut>
+__global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
+    const TIn* __restrict__ x, const TIn* __restrict__ w, const TIn* __restrict__ bias,
+    TOut* __restrict__ y, DwImpArgs a) {
+    extern __shared__ __align__(16) float pl[];   // [per][Hp][Wp], then per * R * S filter taps
+    const int tid = threadIdx.x;
+    const int p0 = blockIdx.x * a.per;             // first plane (n * C + c)
+    const int np = min(a.per, a.planes - p0);
+    const int HW = a.H * a.W, HpWp = a.Hp * a.Wp, RS = a.R * a.S;
+    float* wl = pl + a.per * HpWp;
+
+    // zero the padding ring of every plane (the interior is overwritten)
+    for (int e = tid; e < np * HpWp; e += kDThreads) {
+        const int r = e % HpWp;
+        const int hh = r / a.Wp, ww = r - hh * a.Wp;
+        if (hh < a.ph || hh >= a.ph + a.H || ww < a.pw || ww >= a.pw + a.W) pl[e] = 0.f;
+    }
+    // the planes: consecutive elements of x, consecutive lanes
+    const TIn* xs = x + (size_t)p0 * HW;
+    const int total = np * HW;
+    for (int e0 = tid; e0 < total; e0 += 4 * kDThreads) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u * kDThreads;
+            v[u] = e < total ? to_f32(xs[e]) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u * kDThreads;
+            if (e < total) {
+                const uint32_t q = fdiv((uint32_t)e, a.fdHW);
+                const int r = e - (int)q * HW;
+                const uint32_t hh = fdiv((uint32_t)r, a.fdW);
+                const int ww = r - (int)hh * a.W;
+                pl[q * HpWp + (hh + a.ph) * a.Wp + ww + a.pw] = v[u];
+            }
+        }
+    }
+    for (int e = tid; e < np * RS; e += kDThreads) {
+        const int c = (p0 + e / RS) % a.C;
+        wl[e] = to_f32(w[(size_t)c * RS + e % RS]);
+    }
+    __syncthreads();
+
+    // outputs: consecutive elements of y, consecutive lanes
+    const int PQo = a.Po * a.Qo;
+    TOut* ys = y + (size_t)p0 * PQo;
+    for (int o = tid; o < np * PQo; o += kDThreads) {
+        const uint32_t q = fdiv((uint32_t)o, a.fdPQo);
+        const int r = o - (int)q * PQo;
+        const uint32_t oh = fdiv((uint32_t)r, a.fdQo);
+        const int ow = r - (int)oh * a.Qo;
+        const int c = (p0 + (int)q) % a.C;
+        const float b = bias ? to_f32(bias[c]) : 0.f;
+        const float* src = pl + q * HpWp;
+        const float* wt = wl + q * RS;
+        auto conv_at = [&](int h, int ww) {
+            float acc = 0.f;
+            const float* s0 = src + h * a.sh * a.Wp + ww * a.sw;
+            for (int rr = 0; rr < a.R; ++rr)
+                for (int qq = 0; qq < a.S; ++qq)
+                    acc = fmaf(s0[rr * a.dh * a.Wp + qq * a.dw], wt[rr * a.S + qq], acc);
+            const float v = acc + b;
+            return a.relu ? fmaxf(v, 0.f) : v;   // bias, then ReLU (maxNum against 0)
+        };
+        float v;
+        if (a.pool) {
+            const int h = 2 * (int)oh, ww = 2 * ow;
+            v = fmaxf(fmaxf(conv_at(h, ww), conv_at(h, ww + 1)),
+                      fmaxf(conv_at(h + 1, ww), conv_at(h + 1, ww + 1)));
+        } else {
+            v = conv_at((int)oh, ow);
+        }
+        ys[o] = from_f32<TOut>(v);
+    }
+}
+
+bool dw_imp_plan(const Geom& g, const Epi& epi, int n_images, DwImpArgs& a, size_t& lds, int64_t& grid) {
+    a.C = g.C; a.H = g.H; a.W = g.W; a.P = g.P; a.Q = g.Q; a.R = g.R; a.S = g.S;
+    a.sh = g.sh; a.sw = g.sw; a.ph = g.ph; a.pw = g.pw; a.dh = g.dh; a.dw = g.dw;
+    a.Hp = g.H + 2 * g.ph;
+    a.Wp = g.W + 2 * g.pw;
+    const int64_t plane_bytes = ((int64_t)a.Hp * a.Wp + (int64_t)g.R * g.S) * 4;
+    if (plane_bytes > kDwLdsBytes) return false;
+    const int64_t planes = (int64_t)n_images * g.C;
+    if (planes * std::max<int64_t>((int64_t)g.H * g.W, (int64_t)g.P * g.Q) >= ((int64_t)1 << 31)) return false;
+    a.planes = (int)planes;
+    // as many planes as fit, up to about 4 input elements per thread, and
+    // enough workgroups to fill the GPU
+    int per = (int)std::min<int64_t>(kDwLdsBytes / plane_bytes, std::max<int64_t>(1, 4 * kDThreads / ((int64_t)g.H * g.W)));
+    per = std::max(1, std::min<int>(per, (int)std::max<int64_t>(1, planes / 512)));
+    a.per = per;
+    a.relu = epi.relu;
+    a.pool = epi.pool;
+    a.Po = out_rows(g, epi);
+    a.Qo = out_cols(g, epi);
+    a.fdHW = make_fastdiv((uint32_t)(g.H * g.W));
+    a.fdW = make_fastdiv((uint32_t)g.W);
+    a.fdPQo = make_fastdiv((uint32_t)(a.Po * a.Qo));
+    a.fdQo = make_fastdiv((uint32_t)a.Qo);
+    lds = (size_t)per * plane_bytes;
+    grid = (planes + per - 1) / per;
+    return true;
+}
+
+template <typename TIn, typename TOut>
+hipError_t launch_dwi(const Geom& g, const void* x, const void* w, const void* bias, void* y,
+                      const Epi& epi, hipStream_t st) {
+    DwImpArgs a;
+    size_t lds = 0;
+    int64_t grid = 0;
+    if (!dw_imp_plan(g, epi, g.N, a, lds, grid)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((conv_dw_implicit_kernel<TIn, TOut>), dim3((uint32_t)grid), dim3(kDThreads), lds, st,
+                       (const TIn*)x, (const TIn*)w, (const TIn*)bias, (TOut*)y, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool dw_implicit_supported(const Geom& g, const Epi& epi) {
+    DwImpArgs a;
+    size_t lds = 0;
+    int64_t grid = 0;
+    return dw_imp_plan(g, epi, std::max(g.N, 1), a, lds, grid);
+}
+
+hipError_t launch_conv_dw_implicit(const Geom& g, ciw_dtype in, ciw_dtype out, const void* x,
+                                   const void* w, const void* bias, void* y, const Epi& epi,
+                                   hipStream_t st) {
+    if (g.N == 0) return hipSuccess;
+    if (in == CIW_F32) return launch_dwi<float, float>(g, x, w, bias, y, epi, st);
+    if (in == CIW_F16)
+        return out == CIW_F32 ? launch_dwi<half_t, float>(g, x, w, bias, y, epi, st)
+                              : launch_dwi<half_t, half_t>(g, x, w, bias, y, epi, st);
+    return out == CIW_F32 ? launch_dwi<bf16_t, float>(g, x, w, bias, y, epi, st)
+                          : launch_dwi<bf16_t, bf16_t>(g, x, w, bias, y, epi, st);
+}
+
+}  // namespace ciw

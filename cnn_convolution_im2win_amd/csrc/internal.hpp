@@ -114,6 +114,14 @@ hipError_t launch_conv_implicit(const Geom& g, ciw_dtype in, ciw_dtype out, cons
                                 const void* w, const void* bias, void* y, void* ws,
                                 const Epi& epi, hipStream_t st);
 
+// Depthwise convolution with the windows built in LDS from x (no window
+// tensor, no workspace); dw_implicit_supported is false when a padded
+// input plane does not fit the kernel's LDS budget.
+bool dw_implicit_supported(const Geom& g, const Epi& epi);
+hipError_t launch_conv_dw_implicit(const Geom& g, ciw_dtype in, ciw_dtype out, const void* x,
+                                   const void* w, const void* bias, void* y, const Epi& epi,
+                                   hipStream_t st);
+
 // Depthwise contraction over a CHW window tensor.
 hipError_t launch_conv_dw(const Geom& g, ciw_dtype in, ciw_dtype out, const void* xw,
                           const void* w, const void* bias, void* y, int n_images,

@@ -99,15 +99,17 @@ typedef struct {
                                        [N][K][P/2][Q/2] (floor; an odd last row or column
                                        is dropped).  CIW_ERR_INVALID_ARG if P or Q < 2. */
 
-/* On-the-fly window rows (conv2d_fwd, fp16/bf16 only).  The contraction
- * kernel builds the window rows of each band of output rows in LDS straight
- * from x and never writes the window tensor to memory; the result is the
- * same sum in another order (the im2win paper's memory concern, §III-B and
- * the processing strategies of §IV-D1, taken to its end: no window tensor).
- * The workspace then holds only a re-laid-out copy of the filter
- * (conv2d_implicit_workspace_bytes).  Layers the kernel does not run return
- * CIW_ERR_UNSUPPORTED, see conv2d_implicit_workspace_bytes.  Not allowed
- * with CIW_FLAG_WINDOW_READY or CIW_FLAG_GENERIC, nor for conv2d_dw_fwd
+/* On-the-fly windows.  conv2d_fwd (fp16/bf16): the contraction kernel
+ * builds the window rows of each band of output rows in LDS straight from x
+ * and never writes the window tensor to memory; the workspace then holds
+ * only a re-laid-out copy of the filter (conv2d_implicit_workspace_bytes).
+ * conv2d_dw_fwd (any input type): each workgroup stages whole zero-padded
+ * input planes in LDS and computes their outputs there; no workspace
+ * (workspace may be NULL).  The result is the same sum in another order
+ * (the im2win paper's memory concern, §III-B and the processing strategies
+ * of §IV-D1, taken to its end: no window tensor).  Layers these kernels do
+ * not run return CIW_ERR_UNSUPPORTED, see conv2d_implicit_workspace_bytes.
+ * Not allowed with CIW_FLAG_WINDOW_READY or CIW_FLAG_GENERIC
  * (CIW_ERR_INVALID_ARG). */
 #define CIW_FLAG_IMPLICIT     0x20u
 /* fp32 dense (conv2d_fwd) kernel choice.  By default the contraction runs
@@ -159,13 +161,16 @@ ciw_status conv_im2win_transform(const ciw_conv_desc* desc, ciw_dtype dtype,
 ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
                                   int64_t n_images, size_t* bytes);
 
-/* Workspace conv2d_fwd needs with CIW_FLAG_IMPLICIT for this layer, output
- * type and epilogue flags (the re-laid-out filter; independent of N).
- * CIW_ERR_UNSUPPORTED if the in-LDS kernel does not run the layer: it needs
- * an fp16/bf16 input, groups == 1, C a multiple of 16, K <= 64, W a
- * multiple of 8, stride_h == 1, a 3x3 filter with C <= 64 or a 1x1 filter
- * with C in {16, 32, 64}, at most 1024 outputs of a row per 256 threads
- * (K * Q), no CIW_FLAG_MAXPOOL2, and fewer than 2^31 bytes per image of x. */
+/* Workspace conv2d_fwd / conv2d_dw_fwd need with CIW_FLAG_IMPLICIT for this
+ * layer, output type and epilogue flags (independent of N).  Depthwise
+ * (groups == C == K): 0 bytes; CIW_ERR_UNSUPPORTED if a zero-padded input
+ * plane and its filter exceed 48 KB of LDS.  Dense: the re-laid-out filter;
+ * CIW_ERR_UNSUPPORTED unless the input is fp16/bf16, groups == 1, C is a
+ * multiple of 16, K <= 64, W a multiple of 8, stride_h == 1, the filter is
+ * 3x3 with C <= 64 or 1x1 with C in {16, 32, 64}, an output row needs at
+ * most 4 stores per thread (K*Q/V <= 1024 with V = 16 / output element
+ * bytes when Q is a multiple of V, else K*Q <= 1024), no
+ * CIW_FLAG_MAXPOOL2, and an image of x has fewer than 2^31 bytes. */
 ciw_status conv2d_implicit_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
                                            ciw_dtype out_dtype, uint32_t flags, size_t* bytes);
 

@@ -1,8 +1,10 @@
-"""GPU parity of the in-LDS window path (conv2d_fwd with CIW_FLAG_IMPLICIT).
+"""GPU parity of the in-LDS window paths (CIW_FLAG_IMPLICIT): conv2d_fwd for
+fp16/bf16 and conv2d_dw_fwd for every input type.
 
-The kernel builds its window rows in LDS from x and never writes the window
-tensor; it must meet the same bar as the materialised path against the fp64
-oracle: max|y - ref| <= 2e-2 * max|ref| for fp16/bf16 inputs.
+The kernels build their windows in LDS from x and never write the window
+tensor; they must meet the same bar as the materialised path against the
+fp64 oracle: max|y - ref| <= tol * max|ref|, tol 1e-4 for fp32 and 2e-2 for
+fp16/bf16 inputs.
 """
 import sys
 
@@ -154,6 +156,74 @@ def test_errors():
     assert st(IMP, dtype=torch.float32) == ciw._lib.CIW_ERR_UNSUPPORTED
     assert st(IMP | ciw.CIW_FLAG_WINDOW_READY) == ciw._lib.CIW_ERR_INVALID_ARG
     assert st(IMP | ciw.CIW_FLAG_GENERIC) == ciw._lib.CIW_ERR_INVALID_ARG
-    assert st(IMP, groups=64) == ciw._lib.CIW_ERR_INVALID_ARG
+    assert st(IMP, groups=64) == 0                       # depthwise: windows in LDS too
     assert st(IMP, ws_bytes=1024) == ciw._lib.CIW_ERR_WORKSPACE
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ depthwise
+DW = workloads.LAYERS["dw_3x3_fp32"]
+
+
+def run_dw(L, x, w, b, flags=IMP):
+    od = torch_dtype(L.out_dtype)
+    y = ciw.conv2d(to_dev(x, L.dtype), to_dev(w, L.dtype), to_dev(b, L.dtype), L.stride, L.pad,
+                   L.dil, L.groups, out_dtype=od, flags=flags)
+    torch.cuda.synchronize()
+    return y
+
+
+def test_dw_layer_full_size_sampled():
+    """The 128x512x14x14 depthwise layer at full size: sampled outputs
+    against the oracle, every output against the materialised path."""
+    L = DW
+    say("implicit dw_3x3_fp32 full size, sampled")
+    x, w, b = workloads.make_inputs(L)
+    got = to_host_f64(run_dw(L, x, w, b))
+    rng = np.random.default_rng(93)
+    idx = sample_indices(got.shape, 3000, rng)
+    f = lambda a: a.astype(np.float64)
+    ref = oracle.conv2d_points(f(x), f(w), f(b), idx, L.stride, L.pad, L.dil, L.groups)
+    e = rel_err(got[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]], ref)
+    say(f"  sampled: rel err {e:.3e}")
+    assert e <= TOL["f32"]
+    explicit = to_host_f64(run_dw(L, x, w, b, flags=0))
+    e = rel_err(got, explicit)
+    say(f"  against the materialised path: rel err {e:.3e}")
+    assert e <= TOL["f32"] and np.all(np.isfinite(got))
+
+
+# (N, C, H, W, R, stride, pad, dil, dtype, out)
+DW_SHAPES = [
+    (2, 512, 14, 14, 3, 1, 1, 1, "f32", "f32"),
+    (3, 7, 9, 11, 3, 2, 1, 1, "f32", "f32"),
+    (2, 5, 17, 13, 5, 1, 2, 2, "f16", "f16"),
+    (1, 9, 30, 30, 7, 2, 3, 1, "bf16", "bf16"),
+    (2, 6, 12, 10, 3, 1, 0, 1, "f16", "f32"),
+    (1, 3, 64, 64, 3, 1, 1, 1, "bf16", "f32"),
+    (4, 33, 1, 1, 1, 1, 0, 1, "f32", "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", DW_SHAPES)
+@pytest.mark.parametrize("epi", ["none", "relu", "relu_pool"])
+def test_dw_shapes_against_oracle(shape, epi):
+    N, C, H, W, R, s, p, d, dt, out = shape
+    L = workloads.Layer("dwimp", N=N, C=C, H=H, W=W, K=C, R=R, S=R, stride=(s, s), pad=(p, p),
+                        dil=(d, d), groups=C, dtype=dt, out_dtype=out,
+                        x_dist=("normal", 0.0, 1.0), seed=sum(shape[:8]))
+    P = (H + 2 * p - d * (R - 1) - 1) // s + 1
+    if epi == "relu_pool" and P < 2:
+        pytest.skip("no 2x2 region")
+    say(f"implicit dw {shape} {epi}")
+    x, w, b = workloads.make_inputs(L)
+    flags = IMP | {"none": 0, "relu": ciw.CIW_FLAG_RELU,
+                   "relu_pool": ciw.CIW_FLAG_RELU | ciw.CIW_FLAG_MAXPOOL2}[epi]
+    got = to_host_f64(run_dw(L, x, w, b, flags))
+    ref = oracle.conv2d(f64(x, dt), f64(w, dt), f64(b, dt), L.stride, L.pad, L.dil, L.groups)
+    if epi != "none":
+        ref = oracle.relu_pool(ref, relu=True, pool=epi == "relu_pool")
+    e = rel_err(got, ref)
+    say(f"  rel err {e:.3e}")
+    assert got.shape == ref.shape and np.all(np.isfinite(got))
+    assert e <= TOL[dt]
