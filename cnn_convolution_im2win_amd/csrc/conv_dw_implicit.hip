@@ -35,35 +35,53 @@ struct DwImpArgs {
     FastDiv fdHW, fdW, fdPQo, fdQo;
 };
 
-template <typename TIn, typename TOut>
+// KR x KS: the filter extent when fixed at compile time (0: run time).
+// Every LDS access has consecutive lanes on consecutive words (no bank
+// conflicts): the planes are zeroed with consecutive 16-byte stores, then x
+// is copied element by element (consecutive lanes, consecutive elements:
+// coalesced), and lane i of a pass computes output o0 + i.
+template <typename TIn, typename TOut, int KR, int KS>
 __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ w, const TIn* __restrict__ bias,
     TOut* __restrict__ y, DwImpArgs a) {
-    extern __shared__ __align__(16) float pl[];   // [per][Hp][Wp], then per * R * S filter taps
+    extern __shared__ __align__(16) float pl[];   // [per][Hp][Wp], per * R * S taps, per biases
     const int tid = threadIdx.x;
     const int p0 = blockIdx.x * a.per;             // first plane (n * C + c)
     const int np = min(a.per, a.planes - p0);
-    const int HW = a.H * a.W, HpWp = a.Hp * a.Wp, RS = a.R * a.S;
+    const int R = KR ? KR : a.R, S = KS ? KS : a.S;
+    const int HW = a.H * a.W, HpWp = a.Hp * a.Wp, RS = R * S;
     float* wl = pl + a.per * HpWp;
+    float* bl = wl + a.per * RS;
 
-    // zero the padding ring of every plane (the interior is overwritten)
-    for (int e = tid; e < np * HpWp; e += kDThreads) {
-        const int r = e % HpWp;
-        const int hh = r / a.Wp, ww = r - hh * a.Wp;
-        if (hh < a.ph || hh >= a.ph + a.H || ww < a.pw || ww >= a.pw + a.W) pl[e] = 0.f;
-    }
-    // the planes: consecutive elements of x, consecutive lanes
+    // x's elements go to registers first (consecutive elements on
+    // consecutive lanes: coalesced), so the zeroing and the filter staging
+    // run while they are in flight
     const TIn* xs = x + (size_t)p0 * HW;
     const int total = np * HW;
-    for (int e0 = tid; e0 < total; e0 += 4 * kDThreads) {
-        float v[4];
+    constexpr int kU = 16;
+    float v[kU];
+    auto load = [&](int e0) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kU; ++u) {
             const int e = e0 + u * kDThreads;
             v[u] = e < total ? to_f32(xs[e]) : 0.f;
         }
+    };
+    load(tid);
+    // zero the planes (padding included; a.per * HpWp is a multiple of 4)
+    for (int e = tid; 4 * e < np * HpWp; e += kDThreads)
+        reinterpret_cast<float4*>(pl)[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int e = tid; e < np * RS; e += kDThreads) {
+        const int c = (p0 + e / RS) % a.C;
+        wl[e] = to_f32(w[(size_t)c * RS + e % RS]);
+    }
+    for (int e = tid; e < np; e += kDThreads) bl[e] = bias ? to_f32(bias[(p0 + e) % a.C]) : 0.f;
+    __syncthreads();
+    // the planes' interiors
+    for (int e0 = tid; e0 < total; e0 += kU * kDThreads) {
+        if (e0 != tid) load(e0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kU; ++u) {
             const int e = e0 + u * kDThreads;
             if (e < total) {
                 const uint32_t q = fdiv((uint32_t)e, a.fdHW);
@@ -74,13 +92,9 @@ __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
             }
         }
     }
-    for (int e = tid; e < np * RS; e += kDThreads) {
-        const int c = (p0 + e / RS) % a.C;
-        wl[e] = to_f32(w[(size_t)c * RS + e % RS]);
-    }
     __syncthreads();
 
-    // outputs: consecutive elements of y, consecutive lanes
+    // outputs: consecutive elements of y on consecutive lanes
     const int PQo = a.Po * a.Qo;
     TOut* ys = y + (size_t)p0 * PQo;
     for (int o = tid; o < np * PQo; o += kDThreads) {
@@ -88,16 +102,17 @@ __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
         const int r = o - (int)q * PQo;
         const uint32_t oh = fdiv((uint32_t)r, a.fdQo);
         const int ow = r - (int)oh * a.Qo;
-        const int c = (p0 + (int)q) % a.C;
-        const float b = bias ? to_f32(bias[c]) : 0.f;
+        const float b = bl[q];
         const float* src = pl + q * HpWp;
         const float* wt = wl + q * RS;
         auto conv_at = [&](int h, int ww) {
             float acc = 0.f;
             const float* s0 = src + h * a.sh * a.Wp + ww * a.sw;
-            for (int rr = 0; rr < a.R; ++rr)
-                for (int qq = 0; qq < a.S; ++qq)
-                    acc = fmaf(s0[rr * a.dh * a.Wp + qq * a.dw], wt[rr * a.S + qq], acc);
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                for (int qq = 0; qq < S; ++qq)
+                    acc = fmaf(s0[rr * a.dh * a.Wp + qq * a.dw], wt[rr * S + qq], acc);
             const float v = acc + b;
             return a.relu ? fmaxf(v, 0.f) : v;   // bias, then ReLU (maxNum against 0)
         };
@@ -118,15 +133,17 @@ bool dw_imp_plan(const Geom& g, const Epi& epi, int n_images, DwImpArgs& a, size
     a.sh = g.sh; a.sw = g.sw; a.ph = g.ph; a.pw = g.pw; a.dh = g.dh; a.dw = g.dw;
     a.Hp = g.H + 2 * g.ph;
     a.Wp = g.W + 2 * g.pw;
-    const int64_t plane_bytes = ((int64_t)a.Hp * a.Wp + (int64_t)g.R * g.S) * 4;
+    // LDS plane area a multiple of 4 words (the zeroing writes 16 bytes)
+    while ((a.Hp * a.Wp) % 4) ++a.Hp;
+    const int64_t plane_bytes = ((int64_t)a.Hp * a.Wp + (int64_t)g.R * g.S + 1) * 4;
     if (plane_bytes > kDwLdsBytes) return false;
     const int64_t planes = (int64_t)n_images * g.C;
     if (planes * std::max<int64_t>((int64_t)g.H * g.W, (int64_t)g.P * g.Q) >= ((int64_t)1 << 31)) return false;
     a.planes = (int)planes;
-    // as many planes as fit, up to about 4 input elements per thread, and
-    // enough workgroups to fill the GPU
-    int per = (int)std::min<int64_t>(kDwLdsBytes / plane_bytes, std::max<int64_t>(1, 4 * kDThreads / ((int64_t)g.H * g.W)));
-    per = std::max(1, std::min<int>(per, (int)std::max<int64_t>(1, planes / 512)));
+    // as many planes as fit, up to about 16 input elements per thread, and
+    // at least about 1024 workgroups
+    int per = (int)std::min<int64_t>(kDwLdsBytes / plane_bytes, std::max<int64_t>(1, 16 * kDThreads / ((int64_t)g.H * g.W)));
+    per = std::max(1, std::min<int>(per, (int)std::max<int64_t>(1, planes / 1024)));
     a.per = per;
     a.relu = epi.relu;
     a.pool = epi.pool;
@@ -148,7 +165,10 @@ hipError_t launch_dwi(const Geom& g, const void* x, const void* w, const void* b
     size_t lds = 0;
     int64_t grid = 0;
     if (!dw_imp_plan(g, epi, g.N, a, lds, grid)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((conv_dw_implicit_kernel<TIn, TOut>), dim3((uint32_t)grid), dim3(kDThreads), lds, st,
+    void (*kfn)(const TIn*, const TIn*, const TIn*, TOut*, DwImpArgs) =
+        (g.R == 3 && g.S == 3) ? conv_dw_implicit_kernel<TIn, TOut, 3, 3>
+                               : conv_dw_implicit_kernel<TIn, TOut, 0, 0>;
+    hipLaunchKernelGGL(kfn, dim3((uint32_t)grid), dim3(kDThreads), lds, st,
                        (const TIn*)x, (const TIn*)w, (const TIn*)bias, (TOut*)y, a);
     return hipGetLastError();
 }
