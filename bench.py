@@ -423,6 +423,7 @@ def time_implicit(step: Step, steps: int, warmup: int):
     }
     if not step.depthwise:
         res["mfma_frac"] = round(fl / (wall * 1e-3) / 1e12 / PEAK_TFLOPS["mfma_" + step.L.dtype], 4)
+    res["traffic"] = stored_traffic(traffic_key(step.L, step.epilogue) + "+implicit")
     return res
 
 
@@ -485,6 +486,14 @@ def measure_layer(L: workloads.Layer, steps: int, warmup: int, epilogue: str = "
     k32 = time_fp32_kernels(step, steps, warmup)
     if k32 is not None:
         res["fp32_kernels"] = k32
+        # the library picks the fp32 kernel itself; the step's contraction
+        # is the one whose forced timing it matches (the matrix cores:
+        # bound by the fp32 MFMA peak, the same 157.3 TFLOP/s)
+        if abs(co_ms - k32["matrix"]["contract_ms"]) < abs(co_ms - k32["vector"]["contract_ms"]):
+            res["roofline"]["bound"] = "mfma"
+            res["fp32_kernel"] = "matrix"
+        else:
+            res["fp32_kernel"] = "vector"
     if not step.depthwise and L.dtype != "f32":
         res["mfma_frac"] = round(res["contract_tflops"] / PEAK_TFLOPS["mfma_" + L.dtype], 4)
     if step.depthwise or L.dtype != "f32":
