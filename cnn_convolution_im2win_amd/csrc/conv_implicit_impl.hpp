@@ -28,9 +28,28 @@
 // window fragments (first operand) by register-resident filter fragments of
 // 32 output channels (second operand), v_mfma_f32_32x32x16, fp32
 // accumulation, bias seeding the accumulators, one rounding at the store.
+//
+// Ablation switches (the im2win paper §IV-E ablates double buffering,
+// asynchronous copies and its zig-zag order; cnn_convolution_im2win_amd/
+// ablation.py builds and times each), all 0 in the library:
+//   CIW_ABLATE_NO_DOUBLE: input row u + 1 is copied at the step that needs
+//     it and waited for at once (no copy ahead);
+//   CIW_ABLATE_NO_ASYNC: rows go global memory -> registers -> LDS instead
+//     of straight into LDS;
+//   CIW_ABLATE_NO_XCD: bands in dispatch order (no XCD-aware placement).
 #pragma once
 
 #include "conv_mfma_impl.hpp"
+
+#ifndef CIW_ABLATE_NO_DOUBLE
+#define CIW_ABLATE_NO_DOUBLE 0
+#endif
+#ifndef CIW_ABLATE_NO_ASYNC
+#define CIW_ABLATE_NO_ASYNC 0
+#endif
+#ifndef CIW_ABLATE_NO_XCD
+#define CIW_ABLATE_NO_XCD 0
+#endif
 
 namespace ciw {
 namespace {
@@ -128,7 +147,8 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
     // are dispatched round-robin over the 8 XCDs), so the input rows that
     // neighbouring bands share meet in that XCD's L2.
     int task = blockIdx.x;
-    if ((a.ntask & 7) == 0) task = (int)(blockIdx.x & 7) * (a.ntask >> 3) + (int)(blockIdx.x >> 3);
+    if (!CIW_ABLATE_NO_XCD && (a.ntask & 7) == 0)
+        task = (int)(blockIdx.x & 7) * (a.ntask >> 3) + (int)(blockIdx.x >> 3);
     const int n = task / a.nbands;
     const int h0 = (task - n * a.nbands) * a.band;
     const int rows = min(a.band, a.P - h0);
@@ -174,9 +194,18 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
 #pragma unroll
         for (int jj = 0; jj < kImpMaxCopies; ++jj) {
             if (jj < a.nd) {
-                const uint32_t dst = __builtin_amdgcn_readfirstlane(dst0 + 16u * (uint32_t)pos_base[jj]);
-                asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
-                             :: "v"(src_off[jj]), "s"(dst), "s"(src) : "memory");
+                if (CIW_ABLATE_NO_ASYNC) {
+                    // through registers: lane tid's chunk lands at the
+                    // position the direct copy would write
+                    const uint4 v = *reinterpret_cast<const uint4*>(
+                        reinterpret_cast<const char*>(src) + src_off[jj]);
+                    *reinterpret_cast<uint4*>(lb + a.off_stage + (j % a.nstage) * a.stage_bytes +
+                                              16 * (pos_base[jj] + tid)) = v;
+                } else {
+                    const uint32_t dst = __builtin_amdgcn_readfirstlane(dst0 + 16u * (uint32_t)pos_base[jj]);
+                    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+                                 :: "v"(src_off[jj]), "s"(dst), "s"(src) : "memory");
+                }
             }
         }
     };
@@ -245,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
     // prologue: copies of input rows 0 .. pf; zero every window-row buffer
     // (padding columns stay zero: the transpose writes only columns
     // pw .. pw + W - 1)
-    for (int j = 0; j <= a.pf && j < J; ++j) copy_row(j);
+    for (int j = 0; j <= (CIW_ABLATE_NO_DOUBLE ? 0 : a.pf) && j < J; ++j) copy_row(j);
     for (int o = 16 * tid; o < a.nt * a.row_bytes; o += 16 * kThreads)
         *reinterpret_cast<uint4*>(lb + o) = make_uint4(0u, 0u, 0u, 0u);
     f32x16 bias_vec;
@@ -276,7 +305,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
 
     // row 0 into its buffer, once every buffer is zeroed (and the bias
     // staged)
-    wait_vm_lgkm(later_ops(0));
+    wait_vm_lgkm(CIW_ABLATE_NO_DOUBLE ? 0 : later_ops(0));
     wg_barrier();
 #pragma unroll
     for (int e = 0; e < 16; ++e) bias_vec[e] = bias_l[kh * 32 + ml];
@@ -289,9 +318,15 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
     // (rows i .. u, transposed in earlier steps) into the other tile.  One
     // barrier a step: transposes and multiplies of different waves overlap.
     for (int u = 0; u < J; ++u) {
-        wait_vm_lgkm(u + 1 < J ? later_ops(u + 1) : 0);
+        if (CIW_ABLATE_NO_DOUBLE) {
+            // the row this step transposes, copied now and waited for
+            if (u + 1 < J) copy_row(u + 1);
+            wait_vm_lgkm(0);
+        } else {
+            wait_vm_lgkm(u + 1 < J ? later_ops(u + 1) : 0);
+        }
         wg_barrier();
-        if (u + a.pf + 1 < J) copy_row(u + a.pf + 1);
+        if (!CIW_ABLATE_NO_DOUBLE && u + a.pf + 1 < J) copy_row(u + a.pf + 1);
         const int i = u - a.span + 1;
         if (i >= 1) store_row(i - 1);
         if (u + 1 < J) transpose_row(u + 1);
