@@ -255,17 +255,49 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
     }
 }
 
-// y[i] = bias[k] + sum over slices s (in order) of part[s][i], i = (n*K + k)*PQ + pix
+// y[i] = bias[k] + sum over slices s (in order) of part[s][i], i = (n*K + k)*PQ + pix.
+// VEC (a slice holds a multiple of 4 outputs, so every slice starts 16-byte
+// aligned): four consecutive outputs per thread with 16-byte loads and
+// stores, every slice's loads issued before the sums, which then run in
+// slice order.  Otherwise one output per thread.
+constexpr int kRedMax = 32;   // slices a thread holds in registers at once
+template <bool VEC>
 __global__ __launch_bounds__(256) void split_reduce_nkp_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, float* __restrict__ y,
     uint32_t per_split, int splits, int PQ, int K, int relu) {
-    const uint32_t i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= per_split) return;
-    float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += part[(size_t)s * per_split + i];
-    const int k = (int)((i / (uint32_t)PQ) % (uint32_t)K);
-    v += bias ? bias[k] : 0.f;
-    y[i] = relu ? fmaxf(v, 0.f) : v;
+    const uint32_t t = blockIdx.x * 256 + threadIdx.x;
+    if (!VEC) {
+        if (t >= per_split) return;
+        float v = 0.f;
+        for (int s = 0; s < splits; ++s) v += part[(size_t)s * per_split + t];
+        const int k = (int)((t / (uint32_t)PQ) % (uint32_t)K);
+        v += bias ? bias[k] : 0.f;
+        y[t] = relu ? fmaxf(v, 0.f) : v;
+        return;
+    }
+    if (4 * t >= per_split) return;
+    const float4* p4 = reinterpret_cast<const float4*>(part) + t;
+    const uint32_t stride4 = per_split / 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < splits; s0 += kRedMax) {
+        float4 v[kRedMax];
+#pragma unroll
+        for (int s = 0; s < kRedMax; ++s)
+            if (s0 + s < splits) v[s] = p4[(size_t)(s0 + s) * stride4];
+#pragma unroll
+        for (int s = 0; s < kRedMax; ++s)
+            if (s0 + s < splits) {
+                acc.x += v[s].x; acc.y += v[s].y; acc.z += v[s].z; acc.w += v[s].w;
+            }
+    }
+    float* a = &acc.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int k = (int)(((4 * t + e) / (uint32_t)PQ) % (uint32_t)K);
+        const float v = a[e] + (bias ? bias[k] : 0.f);
+        a[e] = relu ? fmaxf(v, 0.f) : v;
+    }
+    reinterpret_cast<float4*>(y)[t] = acc;
 }
 
 struct F32MPlan {
@@ -343,7 +375,10 @@ hipError_t launch_conv_fp32_mfma(const Geom& g, const float* xw, const float* w,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || pl.a.splits == 1) return e;
     const int64_t per_split = (int64_t)n_images * g.K * g.P * g.Q;
-    hipLaunchKernelGGL(split_reduce_nkp_kernel, dim3((uint32_t)((per_split + 255) / 256)), dim3(256), 0,
+    const bool vec = per_split % 4 == 0;
+    const int64_t threads = vec ? per_split / 4 : per_split;
+    hipLaunchKernelGGL(vec ? split_reduce_nkp_kernel<true> : split_reduce_nkp_kernel<false>,
+                       dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0,
                        st, partials, bias, y, (uint32_t)per_split, pl.a.splits, g.P * g.Q, g.K,
                        (int)epi.relu);
     return hipGetLastError();
