@@ -33,6 +33,7 @@ struct DwImpArgs {
     int Po, Qo;          // output extent (pooled or not)
     int relu, pool;
     FastDiv fdHW, fdW, fdPQo, fdQo;
+    FastDiv fdStrip;     // Qo * ceil(P / kSH): strip items per plane
 };
 
 // KR x KS: the filter extent when fixed at compile time (0: run time).
@@ -40,7 +41,9 @@ struct DwImpArgs {
 // conflicts): the planes are zeroed with consecutive 16-byte stores, then x
 // is copied element by element (consecutive lanes, consecutive elements:
 // coalesced), and lane i of a pass computes output o0 + i.
-template <typename TIn, typename TOut, int KR, int KS>
+constexpr int kSH = 7;   // outputs per lane down a column (strip form)
+
+template <typename TIn, typename TOut, int KR, int KS, bool STRIP>
 __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
     const TIn* __restrict__ x, const TIn* __restrict__ w, const TIn* __restrict__ bias,
     TOut* __restrict__ y, DwImpArgs a) {
@@ -94,9 +97,49 @@ __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
     }
     __syncthreads();
 
-    // outputs: consecutive elements of y on consecutive lanes
     const int PQo = a.Po * a.Qo;
     TOut* ys = y + (size_t)p0 * PQo;
+    if (STRIP) {
+        // 3x3, stride 1, dilation 1, no pool: a lane computes kSH outputs
+        // down one column (consecutive lanes: consecutive columns), reading
+        // the (kSH + 2) x 3 inputs and the 9 taps once
+        const int nstrip = (a.P + kSH - 1) / kSH;
+        const int per_plane = a.Qo * nstrip;
+        for (int it = tid; it < np * per_plane; it += kDThreads) {
+            const uint32_t q = fdiv((uint32_t)it, a.fdStrip);
+            const int r = it - (int)q * per_plane;
+            const uint32_t st = fdiv((uint32_t)r, a.fdQo);
+            const int ow = r - (int)st * a.Qo;
+            const int oh0 = (int)st * kSH;
+            const float* src = pl + q * HpWp + oh0 * a.Wp + ow;
+            const float* wt = wl + q * 9;
+            float wr[9];
+#pragma unroll
+            for (int t = 0; t < 9; ++t) wr[t] = wt[t];
+            float in[kSH + 2][3];
+#pragma unroll
+            for (int rr = 0; rr < kSH + 2; ++rr)
+#pragma unroll
+                for (int cc = 0; cc < 3; ++cc)
+                    in[rr][cc] = (oh0 + rr < a.Hp) ? src[rr * a.Wp + cc] : 0.f;
+            const float b = bl[q];
+            TOut* yo = ys + (size_t)q * PQo + (size_t)oh0 * a.Qo + ow;
+#pragma unroll
+            for (int i = 0; i < kSH; ++i) {
+                if (oh0 + i < a.P) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int rr = 0; rr < 3; ++rr)
+#pragma unroll
+                        for (int cc = 0; cc < 3; ++cc) acc = fmaf(in[i + rr][cc], wr[rr * 3 + cc], acc);
+                    const float v = acc + b;
+                    yo[i * a.Qo] = from_f32<TOut>(a.relu ? fmaxf(v, 0.f) : v);
+                }
+            }
+        }
+        return;
+    }
+    // outputs: consecutive elements of y on consecutive lanes
     for (int o = tid; o < np * PQo; o += kDThreads) {
         const uint32_t q = fdiv((uint32_t)o, a.fdPQo);
         const int r = o - (int)q * PQo;
@@ -153,6 +196,7 @@ bool dw_imp_plan(const Geom& g, const Epi& epi, int n_images, DwImpArgs& a, size
     a.fdW = make_fastdiv((uint32_t)g.W);
     a.fdPQo = make_fastdiv((uint32_t)(a.Po * a.Qo));
     a.fdQo = make_fastdiv((uint32_t)a.Qo);
+    a.fdStrip = make_fastdiv((uint32_t)(a.Qo * ((g.P + kSH - 1) / kSH)));
     lds = (size_t)per * plane_bytes;
     grid = (planes + per - 1) / per;
     return true;
@@ -165,9 +209,12 @@ hipError_t launch_dwi(const Geom& g, const void* x, const void* w, const void* b
     size_t lds = 0;
     int64_t grid = 0;
     if (!dw_imp_plan(g, epi, g.N, a, lds, grid)) return hipErrorInvalidValue;
+    const bool r3 = g.R == 3 && g.S == 3;
+    const bool strip = r3 && g.sh == 1 && g.sw == 1 && g.dh == 1 && g.dw == 1 && !epi.pool;
     void (*kfn)(const TIn*, const TIn*, const TIn*, TOut*, DwImpArgs) =
-        (g.R == 3 && g.S == 3) ? conv_dw_implicit_kernel<TIn, TOut, 3, 3>
-                               : conv_dw_implicit_kernel<TIn, TOut, 0, 0>;
+        strip ? conv_dw_implicit_kernel<TIn, TOut, 3, 3, true>
+              : r3 ? conv_dw_implicit_kernel<TIn, TOut, 3, 3, false>
+                   : conv_dw_implicit_kernel<TIn, TOut, 0, 0, false>;
     hipLaunchKernelGGL(kfn, dim3((uint32_t)grid), dim3(kDThreads), lds, st,
                        (const TIn*)x, (const TIn*)w, (const TIn*)bias, (TOut*)y, a);
     return hipGetLastError();
