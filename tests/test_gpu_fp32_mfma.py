@@ -99,3 +99,22 @@ def test_fp32_mfma_deterministic():
     y1 = ciw.conv2d(xd, wd, bd, 1, 1, flags=ciw.CIW_FLAG_FP32_MFMA)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("imgs", [1, 3])
+def test_fp32_mfma_batch_chunks(imgs):
+    """A 4-image fp32 layer whose plan takes the matrix cores, run in chunks
+    of 1 or 3 images through one workspace (the partial sums of every chunk
+    in the same buffer), against the oracle."""
+    L = workloads.Layer("f32chunk", N=4, C=96, H=14, W=14, K=128, R=3, S=3, stride=(1, 1),
+                        pad=(1, 1), x_dist=("uniform", -1.0, 1.0), seed=11)
+    x, w, b = workloads.make_inputs(L)
+    desc = ciw.make_desc(L.x_shape, L.w_shape, L.stride, L.pad, L.dil, 1)
+    ws = torch.empty(ciw.conv2d_workspace_bytes(desc, ciw.CIW_F32, imgs), dtype=torch.uint8,
+                     device="cuda")
+    y = ciw.conv2d(to_dev(x, "f32"), to_dev(w, "f32"), to_dev(b, "f32"), 1, 1, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.conv2d(x.astype(np.float64), w.astype(np.float64), b.astype(np.float64), 1, 1, 1, 1)
+    e = rel_err(to_host_f64(y), ref)
+    say(f"fp32 chunks of {imgs}: rel err {e:.3e}")
+    assert e <= TOL["f32"]
