@@ -8,8 +8,9 @@ ready window tensor).  Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line: TFLOP/s of the step (2*N*K*(C/G)*R*S*P*Q per second;
 with the fused pool, P and Q count only the pixels its 2x2 regions cover),
-the dominant kernel's roofline position (timed with HIP events on its launch
-stream), and the CPU oracle's throughput on the host cores.
+the dominant kernel's roofline position (its call timed with HIP events on
+its launch stream around back-to-back calls), and the CPU oracle's
+throughput on the host cores.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers]
                   [--epilogue none|relu|relu_pool]
@@ -204,31 +205,44 @@ def stored_traffic(workload: str):
     return None if entry is None else entry.get("bytes_per_call")
 
 
-def time_steps(step: Step, steps: int, warmup: int):
-    """K timed steps, each the two C-ABI calls on the step's stream,
-    bracketed by a device synchronisation on both sides; HIP events on that
-    stream time the two calls.  (Replaying the calls as HIP graphs was
-    measured slower here than launching them directly, so the step launches
-    them directly.)"""
+def loop_ms(stream, fn, steps: int, warmup: int):
+    """Mean time per iteration of `fn` over `steps` back-to-back iterations:
+    HIP events recorded on `stream` just before the first and just after
+    the last (the GPU's time), and the host's wall clock between two device
+    synchronisations (the figure throughput is quoted on).  Events between
+    iterations are left out on purpose: each one recorded on a stream costs
+    about 3-4 us of GPU time on this GPU, as much as a small kernel."""
     import torch
     for _ in range(warmup):
-        step.transform()
-        step.contract()
+        fn()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        e = ev[i]
-        e[0].record(step.stream)
-        step.transform()
-        e[1].record(step.stream)
-        step.contract()
-        e[2].record(step.stream)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    tr = [e[0].elapsed_time(e[1]) for e in ev]
-    co = [e[1].elapsed_time(e[2]) for e in ev]
-    return (t1 - t0) * 1e3 / steps, tr, co
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def time_steps(step: Step, steps: int, warmup: int):
+    """K timed steps, each the two C-ABI calls on the step's stream,
+    bracketed by a device synchronisation on both sides (wall clock) and by
+    one pair of HIP events on that stream.  Then the mean duration of each
+    call on its own: K transform calls back to back, and K contraction calls
+    back to back on the window tensor the last transform left (HIP events
+    around each loop).  (Replaying the calls as HIP graphs was measured
+    slower here than launching them directly, so the step launches them
+    directly.)"""
+    def one():
+        step.transform()
+        step.contract()
+    gpu_ms, wall_ms = loop_ms(step.stream, one, steps, warmup)
+    tr_ms, _ = loop_ms(step.stream, step.transform, steps, 2)
+    co_ms, _ = loop_ms(step.stream, step.contract, steps, 2)
+    return wall_ms, gpu_ms, tr_ms, co_ms
 
 
 def cpu_baseline(L: workloads.Layer, seconds: float) -> dict:
@@ -275,18 +289,9 @@ def time_unfused(L: workloads.Layer, epilogue: str, steps: int, warmup: int) -> 
                 y = F.max_pool2d(y, 2)
         return y
 
-    for _ in range(warmup):
-        step.transform()
-        run()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for e in ev:
-        step.transform()
-        e[0].record(step.stream)
-        run()
-        e[1].record(step.stream)
-    torch.cuda.synchronize()
-    return sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    step.transform()
+    ms, _ = loop_ms(step.stream, run, steps, warmup)
+    return ms
 
 
 def memory_report(L: workloads.Layer, steps: int = 5) -> dict:
@@ -380,9 +385,9 @@ def memory_report(L: workloads.Layer, steps: int = 5) -> dict:
 
 def time_implicit(step: Step, steps: int, warmup: int):
     """conv2d_fwd with CIW_FLAG_IMPLICIT (window rows built in LDS from x,
-    filter re-layout included) on the step's stream, K timed calls with HIP
-    events; None when the layer is not one that kernel runs."""
-    import statistics
+    filter re-layout included) on the step's stream, K calls back to back
+    (wall clock and HIP events around the loop); None when the layer is not
+    one that kernel runs."""
     import torch
     ciw = step.ciw
     flags = ciw.CIW_FLAG_IMPLICIT | step.epi_flags
@@ -399,18 +404,7 @@ def time_implicit(step: Step, steps: int, warmup: int):
         st = step.fn(*args)
         if st != 0:
             raise RuntimeError(f"conv2d_fwd (implicit): status {st}")
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record(step.stream)
-        call()
-        ev[i][1].record(step.stream)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
+    ms, wall = loop_ms(step.stream, call, steps, warmup)
     fl = step.flops()
     byt = step.bytes_x() + step.bytes_w() + step.bytes_b() + step.bytes_y()
     res = {
@@ -429,11 +423,10 @@ def time_implicit(step: Step, steps: int, warmup: int):
 
 def time_fp32_kernels(step: Step, steps: int, warmup: int):
     """The fp32 contraction (window ready) with each kernel forced: matrix
-    cores (CIW_FLAG_FP32_MFMA) and vector ALUs (CIW_FLAG_FP32_VALU), K timed
-    calls each with HIP events on the step's stream; the automatic choice is
+    cores (CIW_FLAG_FP32_MFMA) and vector ALUs (CIW_FLAG_FP32_VALU), K calls
+    back to back each, HIP events around the loop; the automatic choice is
     the step's own contraction.  None for layers the matrix-core kernel does
     not run."""
-    import statistics
     import torch
     ciw = step.ciw
     L = step.L
@@ -450,16 +443,7 @@ def time_fp32_kernels(step: Step, steps: int, warmup: int):
             st = step.fn(*args)
             if st != 0:
                 raise RuntimeError(f"conv2d_fwd ({name}): status {st}")
-        for _ in range(warmup):
-            call()
-        torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-        for i in range(steps):
-            ev[i][0].record(step.stream)
-            call()
-            ev[i][1].record(step.stream)
-        torch.cuda.synchronize()
-        ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
+        ms, _ = loop_ms(step.stream, call, steps, warmup)
         out[name] = {"contract_ms": round(ms, 5),
                      "contract_tflops": round(step.flops() / (ms * 1e-3) / 1e12, 3)}
     return out
@@ -467,17 +451,15 @@ def time_fp32_kernels(step: Step, steps: int, warmup: int):
 
 def measure_layer(L: workloads.Layer, steps: int, warmup: int, epilogue: str = "none",
                   unfused: bool = True) -> dict:
-    import statistics
     step = Step(L, epilogue)
-    ms, tr, co = time_steps(step, steps, warmup)
-    tr_ms, co_ms = statistics.mean(tr), statistics.mean(co)
+    ms, gpu_ms, tr_ms, co_ms = time_steps(step, steps, warmup)
     res = {
         "step_ms": round(ms, 5),
+        "step_gpu_ms": round(gpu_ms, 5),
         "tflops": round(step.flops() / (ms * 1e-3) / 1e12, 3),
         "transform_ms": round(tr_ms, 5),
         "transform_gbs": round(step.transform_bytes() / (tr_ms * 1e-3) / 1e9, 1),
         "contract_ms": round(co_ms, 5),
-        "contract_min_ms": round(min(co), 5),
         "contract_tflops": round(step.flops() / (co_ms * 1e-3) / 1e12, 3),
         "contract_gbs": round(step.contraction_bytes() / (co_ms * 1e-3) / 1e9, 1),
         "roofline": step.contraction_roofline(co_ms),

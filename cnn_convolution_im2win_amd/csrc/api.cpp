@@ -2,9 +2,13 @@
 // and workspace arithmetic, batch chunking and kernel dispatch.
 //
 // Every check runs before the first launch, so an error status means nothing
-// was enqueued.  The library holds no mutable state.
+// was enqueued.  The library's only state between calls is the record of
+// which kernels were allowed more than 64 KB of dynamic LDS (below).
 #include <cstdint>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "internal.hpp"
 
@@ -213,6 +217,19 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
 }
 
 }  // namespace
+
+hipError_t ciw::allow_dynamic_lds(const void* fn, size_t bytes) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, size_t> done;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    size_t& have = done[{dev, fn}];
+    if (have >= bytes) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) have = bytes;
+    return e;
+}
 
 extern "C" {
 

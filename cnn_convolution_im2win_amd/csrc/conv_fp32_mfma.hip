@@ -22,8 +22,6 @@
 // the bias and ReLU.  Every sum is in a fixed order: results are
 // deterministic.
 #include <algorithm>
-#include <map>
-#include <mutex>
 
 #include "internal.hpp"
 #include "device_common.hpp"
@@ -339,19 +337,6 @@ bool f32m_plan(const Geom& g, int n_images, F32MPlan& pl) {
     return pl.lds <= 160 * 1024;
 }
 
-hipError_t allow_lds_f32m(const void* fn, size_t bytes) {
-    static std::mutex mu;
-    static std::map<std::pair<int, const void*>, size_t> done;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    size_t& have = done[{dev, fn}];
-    if (have >= bytes) return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess) have = bytes;
-    return e;
-}
-
 }  // namespace
 
 int fp32_mfma_splits(const Geom& g, int n_images) {
@@ -368,7 +353,7 @@ hipError_t launch_conv_fp32_mfma(const Geom& g, const float* xw, const float* w,
     pl.a.relu = epi.relu;
     void (*kfn)(const float*, const float*, const float*, float*, F32MArgs) =
         g.R == 3 ? conv_fp32_mfma_kernel<3, 3> : conv_fp32_mfma_kernel<1, 1>;
-    if (pl.lds > 65536 && allow_lds_f32m(reinterpret_cast<const void*>(kfn), pl.lds) != hipSuccess)
+    if (pl.lds > 65536 && allow_dynamic_lds(reinterpret_cast<const void*>(kfn), pl.lds) != hipSuccess)
         return hipErrorInvalidValue;
     float* dst = pl.a.splits == 1 ? y : partials;
     hipLaunchKernelGGL(kfn, dim3((uint32_t)pl.a.ntask), dim3(kMThreads), pl.lds, st, xw, w, bias, dst, pl.a);

@@ -483,9 +483,7 @@ hipError_t launch_imp_one(const MfImpPlan& pl, const void* x, const void* aperm,
                           void* y, hipStream_t st) {
     void (*kfn)(const uint16_t*, const uint16_t*, const TIn*, TOut*, MfImpArgs) =
         conv_mfma_implicit_kernel<TIn, TOut, R, S, CB>;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    if (pl.lds_bytes > 65536 && allow_lds(reinterpret_cast<const void*>(kfn), dev, pl.lds_bytes) != hipSuccess)
+    if (pl.lds_bytes > 65536 && allow_dynamic_lds(reinterpret_cast<const void*>(kfn), pl.lds_bytes) != hipSuccess)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(kfn, dim3((uint32_t)pl.a.ntask), dim3(kThreads), pl.lds_bytes, st,
                        (const uint16_t*)x, (const uint16_t*)aperm, (const TIn*)bias, (TOut*)y, pl.a);

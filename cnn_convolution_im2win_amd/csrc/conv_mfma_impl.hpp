@@ -16,8 +16,6 @@
 #pragma once
 
 #include <algorithm>
-#include <map>
-#include <mutex>
 
 #include "internal.hpp"
 #include "device_common.hpp"
@@ -998,23 +996,10 @@ bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl, const Epi& epi = E
     return true;
 }
 
-// Raise a kernel's dynamic-LDS limit on this device once: the attribute
-// persists, so later launches (graph captures included) skip the call.
-hipError_t allow_lds(const void* fn, int dev, size_t bytes) {
-    static std::mutex mu;
-    static std::map<std::pair<int, const void*>, size_t> done;
-    std::lock_guard<std::mutex> lock(mu);
-    size_t& have = done[{dev, fn}];
-    if (have >= bytes) return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess) have = bytes;
-    return e;
-}
-
 // One compiled kernel: the tail-in-last-step form exists only for masked
 // plans (without masks it would be the same kernel).
 template <typename TIn, typename TOut, int NS, int M, bool MK, int PD, bool POOL>
-hipError_t launch_rows_one(const MfRowPlan& pl, int dev, int64_t grid, const void* xw,
+hipError_t launch_rows_one(const MfRowPlan& pl, int64_t grid, const void* xw,
                            const void* aperm, const void* bias, void* y, const MfRowArgs& a,
                            hipStream_t st) {
     void (*kfn)(const uint16_t*, const uint16_t*, const TIn*, TOut*, MfRowArgs) =
@@ -1023,7 +1008,7 @@ hipError_t launch_rows_one(const MfRowPlan& pl, int dev, int64_t grid, const voi
         if (pl.tail_last) kfn = conv_mfma_rows_kernel<TIn, TOut, NS, M, MK, PD, true, POOL>;
     }
     // more than 64 KB of dynamic LDS per workgroup must be allowed explicitly
-    if (pl.lds_bytes > 65536 && allow_lds(reinterpret_cast<const void*>(kfn), dev, pl.lds_bytes) != hipSuccess)
+    if (pl.lds_bytes > 65536 && allow_dynamic_lds(reinterpret_cast<const void*>(kfn), pl.lds_bytes) != hipSuccess)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(kfn, dim3((uint32_t)grid), dim3(kThreads), pl.lds_bytes, st,
                        (const uint16_t*)xw, (const uint16_t*)aperm, (const TIn*)bias, (TOut*)y, a);
@@ -1048,7 +1033,7 @@ hipError_t launch_rows(const Geom& g, MfRowPlan pl, const void* xw, const void* 
     if (grid > groups) grid = groups;
 #define CIW_MF_LAUNCH(NS, M, MK, PD)                                                           \
     do {                                                                                       \
-        const hipError_t e_ = launch_rows_one<TIn, TOut, NS, M, MK, PD, POOL>(pl, dev, grid, xw,   \
+        const hipError_t e_ = launch_rows_one<TIn, TOut, NS, M, MK, PD, POOL>(pl, grid, xw,        \
                                                                               aperm, bias, y,  \
                                                                               a, st);          \
         if (e_ != hipSuccess) return e_;                                                       \

@@ -64,6 +64,12 @@ inline int out_cols(const Geom& g, const Epi& e) { return e.pool ? g.Q / 2 : g.Q
 
 inline int elem_bytes(ciw_dtype t) { return t == CIW_F32 ? 4 : 2; }
 
+// Allow `fn` more than the default 64 KB of dynamic LDS per workgroup on the
+// current device.  The attribute persists for the process, so each
+// (device, kernel) pair is raised once and later launches, graph captures
+// included, skip the call: the only state the library keeps between calls.
+hipError_t allow_dynamic_lds(const void* fn, size_t bytes);
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the error of the launch.  Pointers are already
 // offset to the chunk; n_images is the chunk's image count.  y has

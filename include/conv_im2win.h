@@ -19,8 +19,10 @@
  * - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *   never allocates, frees or synchronises; work is enqueued on `stream`
  *   (a hipStream_t; NULL means the null stream) and completes
- *   asynchronously.  No mutable global state: calls on different streams may
- *   run concurrently if their buffers do not overlap.
+ *   asynchronously.  Calls on different streams may run concurrently if
+ *   their buffers do not overlap.  The only state kept between calls is,
+ *   per device, which kernels have already been allowed more than 64 KB of
+ *   dynamic LDS (set once, under a lock, on a kernel's first launch).
  * - Arguments are validated BEFORE anything is enqueued; on any error status
  *   nothing has been launched and no buffer has been touched.
  * - Tensors are dense and contiguous: x is NCHW [N][C][H][W]; the filters w
