@@ -68,9 +68,12 @@ struct MfImpArgs {
     int cg, wv;          // channel groups of 8, column vectors of 8
     int nblk, nkh;       // 32-pixel blocks per output row, 32-channel halves (1 or 2)
     int ostride;         // output tile row stride (elements of TOut)
-    int vec_store, nq, nsv;   // 16-byte stores?, stores per channel row, stores per thread
+    int se, nq, nsv;     // elements per store (a power of two, at most 16 bytes),
+                         // stores per channel row, stores per thread
     int band, nbands, ntask;  // output rows per workgroup, bands per image, workgroups
-    int relu;
+    int relu, pool;      // epilogue: ReLU; 2x2 max-pool (stride 2, floor)
+    int Pc;              // output rows computed: P, or 2 * (P / 2) with the pool
+    int qout, yplane;    // outputs per stored row and per channel plane of y
     uint32_t plane_bytes;     // H * W * 2: bytes between channel planes of x
     int off_stage, off_tile, off_bias;   // LDS regions (bytes)
 };
@@ -126,6 +129,97 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[
     }
 }
 
+// Output stores of E elements of T (E * sizeof(T) in {2, 4, 8, 16} bytes).
+template <int B> struct Word;
+template <> struct Word<2> { using type = uint16_t; };
+template <> struct Word<4> { using type = uint32_t; };
+template <> struct Word<8> { using type = uint2; };
+template <> struct Word<16> { using type = uint4; };
+
+// E adjacent tile elements to y.
+template <typename T, int E>
+__device__ __forceinline__ void copy_out(T* dst, const T* src) {
+    using U = typename Word<E * (int)sizeof(T)>::type;
+    *reinterpret_cast<U*>(dst) = *reinterpret_cast<const U*>(src);
+}
+
+// Horizontal half of the 2x2 pool: 2E adjacent tile elements (whose rows
+// already hold the vertical maximum) to E outputs, each the larger of a
+// pair.  Both values of a pair are T values, so the maximum is exact.
+template <typename T, int E>
+__device__ __forceinline__ void pool_out(T* dst, const T* src) {
+    if constexpr (sizeof(T) == 2) {
+        // a 32-bit word holds one horizontal pair
+        uint32_t w[E];
+        if constexpr (E == 8) {
+            const uint4 p = reinterpret_cast<const uint4*>(src)[0];
+            const uint4 q = reinterpret_cast<const uint4*>(src)[1];
+            w[0] = p.x; w[1] = p.y; w[2] = p.z; w[3] = p.w;
+            w[4] = q.x; w[5] = q.y; w[6] = q.z; w[7] = q.w;
+        } else if constexpr (E == 4) {
+            const uint4 p = *reinterpret_cast<const uint4*>(src);
+            w[0] = p.x; w[1] = p.y; w[2] = p.z; w[3] = p.w;
+        } else if constexpr (E == 2) {
+            const uint2 p = *reinterpret_cast<const uint2*>(src);
+            w[0] = p.x; w[1] = p.y;
+        } else {
+            w[0] = *reinterpret_cast<const uint32_t*>(src);
+        }
+        uint32_t o[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float lo = to_f32(__builtin_bit_cast(T, (uint16_t)(w[e] & 0xffffu)));
+            const float hi = to_f32(__builtin_bit_cast(T, (uint16_t)(w[e] >> 16)));
+            o[e] = f32_bits<T>(fmaxf(lo, hi));
+        }
+        if constexpr (E == 8) {
+            *reinterpret_cast<uint4*>(dst) = make_uint4(o[0] | (o[1] << 16), o[2] | (o[3] << 16),
+                                                        o[4] | (o[5] << 16), o[6] | (o[7] << 16));
+        } else if constexpr (E == 4) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+        } else if constexpr (E == 2) {
+            *reinterpret_cast<uint32_t*>(dst) = o[0] | (o[1] << 16);
+        } else {
+            *reinterpret_cast<uint16_t*>(dst) = (uint16_t)o[0];
+        }
+    } else {
+        float v[2 * E];
+        if constexpr (E == 4) {
+            const float4 p = reinterpret_cast<const float4*>(src)[0];
+            const float4 q = reinterpret_cast<const float4*>(src)[1];
+            v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+            v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
+        } else if constexpr (E == 2) {
+            const float4 p = *reinterpret_cast<const float4*>(src);
+            v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+        } else {
+            const float2 p = *reinterpret_cast<const float2*>(src);
+            v[0] = p.x; v[1] = p.y;
+        }
+        if constexpr (E == 4) {
+            *reinterpret_cast<float4*>(dst) = make_float4(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]),
+                                                          fmaxf(v[4], v[5]), fmaxf(v[6], v[7]));
+        } else if constexpr (E == 2) {
+            *reinterpret_cast<float2*>(dst) = make_float2(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+        } else {
+            *dst = fmaxf(v[0], v[1]);
+        }
+    }
+}
+
+// One output row's stores: nsv per thread at fixed tile / y offsets.
+template <typename T, int E, bool POOL>
+__device__ __forceinline__ void store_tile_row(T* yrow, const T* tl, const int* src, const int* dst,
+                                               int nsv) {
+#pragma unroll
+    for (int j = 0; j < kImpMaxStores; ++j) {
+        if (j < nsv) {
+            if constexpr (POOL) pool_out<T, E>(yrow + dst[j], tl + src[j]);
+            else copy_out<T, E>(yrow + dst[j], tl + src[j]);
+        }
+    }
+}
+
 template <typename TIn, typename TOut, int R, int S, int CB>
 __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ aperm,
@@ -151,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
         task = (int)(blockIdx.x & 7) * (a.ntask >> 3) + (int)(blockIdx.x >> 3);
     const int n = task / a.nbands;
     const int h0 = (task - n * a.nbands) * a.band;
-    const int rows = min(a.band, a.P - h0);
+    const int rows = min(a.band, a.Pc - h0);   // even with the pool
     const int J = rows + a.span - 1;                // input rows of the band
 
     // ---- filter fragments of channel half kh, kept for the whole kernel
@@ -240,36 +334,45 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
         }
     };
 
-    // ---- output stores: K rows of Q elements from the tile; exactly nsv
-    // per thread (surplus threads repeat the last one), positions fixed
-    constexpr int V = 16 / sizeof(TOut);
-    const int E = a.vec_store ? V : 1;
+    // ---- output stores: K rows of qout elements, se at a time, from the
+    // tile; exactly nsv per thread (surplus threads repeat the last one),
+    // positions fixed.  With the pool a stored row is the pair of output
+    // rows 2m, 2m + 1, already merged in one tile (their vertical maximum),
+    // and each stored element the larger of two adjacent tile elements.
     int st_src[kImpMaxStores], st_dst[kImpMaxStores];
 #pragma unroll
     for (int j = 0; j < kImpMaxStores; ++j) {
         const int idx = min(tid + kThreads * j, a.K * a.nq - 1);
         const int k = idx / a.nq, v = idx - (idx / a.nq) * a.nq;
-        st_src[j] = k * a.ostride + v * E;
-        st_dst[j] = k * a.P * a.Q + v * E;
+        st_src[j] = k * a.ostride + (v * a.se << a.pool);
+        st_dst[j] = k * a.yplane + v * a.se;
     }
     TOut* const tile0 = reinterpret_cast<TOut*>(lb + a.off_tile);
     const int tile_elems = a.K * a.ostride;
-    TOut* const yimg = y + (size_t)n * a.K * a.P * a.Q;
+    TOut* const yimg = y + (size_t)n * a.K * a.yplane;
+    // output row i's tile: alternate rows, or alternate row pairs with the pool
+    auto tile_of = [&](int i) { return tile0 + ((i >> a.pool) & 1) * tile_elems; };
+    constexpr int kW16 = 16 / (int)sizeof(TOut), kW8 = 8 / (int)sizeof(TOut);
+    constexpr int kW4 = 4 / (int)sizeof(TOut), kW2 = sizeof(TOut) == 2 ? 1 : kW4;
     auto store_row = [&](int i) {
-        const TOut* tl = tile0 + (i & 1) * tile_elems;
-        TOut* yrow = yimg + (size_t)(h0 + i) * a.Q;
-        if (a.vec_store) {
-#pragma unroll
-            for (int j = 0; j < kImpMaxStores; ++j)
-                if (j < a.nsv)
-                    *reinterpret_cast<uint4*>(yrow + st_dst[j]) =
-                        *reinterpret_cast<const uint4*>(tl + st_src[j]);
+        const TOut* tl = tile_of(i);
+        TOut* yrow = yimg + (size_t)((h0 + i) >> a.pool) * a.qout;
+        const int bytes = a.se * (int)sizeof(TOut);
+        if (a.pool) {
+            if (bytes == 16) store_tile_row<TOut, kW16, true>(yrow, tl, st_src, st_dst, a.nsv);
+            else if (bytes == 8) store_tile_row<TOut, kW8, true>(yrow, tl, st_src, st_dst, a.nsv);
+            else if (bytes == 4) store_tile_row<TOut, kW4, true>(yrow, tl, st_src, st_dst, a.nsv);
+            else store_tile_row<TOut, kW2, true>(yrow, tl, st_src, st_dst, a.nsv);
         } else {
-#pragma unroll
-            for (int j = 0; j < kImpMaxStores; ++j)
-                if (j < a.nsv) yrow[st_dst[j]] = tl[st_src[j]];
+            if (bytes == 16) store_tile_row<TOut, kW16, false>(yrow, tl, st_src, st_dst, a.nsv);
+            else if (bytes == 8) store_tile_row<TOut, kW8, false>(yrow, tl, st_src, st_dst, a.nsv);
+            else if (bytes == 4) store_tile_row<TOut, kW4, false>(yrow, tl, st_src, st_dst, a.nsv);
+            else store_tile_row<TOut, kW2, false>(yrow, tl, st_src, st_dst, a.nsv);
         }
     };
+    // row i - 1 is stored at the step of row i: every row, or with the pool
+    // the second row of each pair
+    auto stores_at = [&](int i) { return i >= 1 && (!a.pool || ((i - 1) & 1)); };
 
     // prologue: copies of input rows 0 .. pf; zero every window-row buffer
     // (padding columns stay zero: the transpose writes only columns
@@ -287,10 +390,10 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
     // Vector-memory operations this wave issues after the copy of row j:
     // copies of later rows and output stores, in issue order (the prologue
     // copies rows 0 .. pf; step v copies row v + pf + 1, then stores output
-    // row v - span).  Waiting for at most that many lets them stay in
-    // flight.
+    // row v - span, if that step stores).  Waiting for at most that many
+    // lets them stay in flight.
     auto dma_of = [&](int v) { return v + a.pf + 1 < J ? a.nd : 0; };
-    auto st_of = [&](int v) { return v >= a.span ? a.nsv : 0; };
+    auto st_of = [&](int v) { return stores_at(v - a.span + 1) ? a.nsv : 0; };
     auto later_ops = [&](int j) {
         int c = 0;
         if (j <= a.pf) {
@@ -328,14 +431,14 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
         wg_barrier();
         if (!CIW_ABLATE_NO_DOUBLE && u + a.pf + 1 < J) copy_row(u + a.pf + 1);
         const int i = u - a.span + 1;
-        if (i >= 1) store_row(i - 1);
+        if (stores_at(i)) store_row(i - 1);
         if (u + 1 < J) transpose_row(u + 1);
         if (i < 0) continue;
 
         int soff[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) soff[r] = ((i + r * a.dh) % a.nt) * a.row_bytes;
-        TOut* tile = tile0 + (i & 1) * tile_elems;
+        TOut* tile = tile_of(i);
         for (int b = pb0; b < a.nblk; b += npb) {
             // pixels past the row end read the last pixel (never stored)
             const int wr = min(32 * b + ml, a.Q - 1);
@@ -372,6 +475,19 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
             const int k = kh * 32 + ml;
             if (k < a.K) {
                 TOut* orow = tile + k * a.ostride + 32 * b + 4 * g;
+                // the second row of a pooled pair: this lane wrote the same
+                // tile elements for the first row in the previous step
+                // (LDS operations of one wave complete in order)
+                if (a.pool && (i & 1)) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 o = get4<TOut>(orow + 8 * q);
+                        acc[4 * q] = fmaxf(acc[4 * q], o.x);
+                        acc[4 * q + 1] = fmaxf(acc[4 * q + 1], o.y);
+                        acc[4 * q + 2] = fmaxf(acc[4 * q + 2], o.z);
+                        acc[4 * q + 3] = fmaxf(acc[4 * q + 3], o.w);
+                    }
+                }
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     put4<TOut>(orow + 8 * q, acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
@@ -402,9 +518,11 @@ inline bool imp_compiled(int R, int S, int CB) {
 // == 1 (checked by the caller), C a multiple of 16 (a step is 16 channels of
 // one tap), K <= 64 (the filter lives in registers), W a multiple of 8
 // (16-byte row copies), stride_h == 1 (one new input row per output row),
-// no 2x2 pool, and every LDS region within 160 KB.
+// at most 4 output stores per thread per row, and every LDS region within
+// 160 KB.
 inline bool mf_imp_plan(const Geom& g, int out_bytes, const Epi& epi, int cus, MfImpPlan& pl) {
-    if (g.C % 16 != 0 || g.K > 64 || g.W % 8 != 0 || g.sh != 1 || epi.pool) return false;
+    if (g.C % 16 != 0 || g.K > 64 || g.W % 8 != 0 || g.sh != 1) return false;
+    if (epi.pool && (g.P < 2 || g.Q < 2)) return false;
     const int CB = g.C / 16;
     if (!imp_compiled(g.R, g.S, CB)) return false;
     if ((int64_t)g.C * g.H * g.W * 2 >= ((int64_t)1 << 31)) return false;   // 32-bit copy offsets
@@ -429,11 +547,18 @@ inline bool mf_imp_plan(const Geom& g, int out_bytes, const Epi& epi, int cus, M
     int ostride = (32 * a.nblk + V - 1) / V * V;
     if (((ostride * out_bytes) / 16) % 2 == 0) ostride += V;   // odd 16-byte units per row
     a.ostride = ostride;
-    a.vec_store = g.Q % V == 0 ? 1 : 0;
-    a.nq = a.vec_store ? g.Q / V : g.Q;
+    a.pool = epi.pool ? 1 : 0;
+    a.relu = epi.relu ? 1 : 0;
+    a.Pc = a.pool ? 2 * (g.P / 2) : g.P;
+    a.qout = a.pool ? g.Q / 2 : g.Q;
+    const int64_t yplane = (int64_t)(a.pool ? g.P / 2 : g.P) * a.qout;
+    if ((int64_t)g.K * yplane >= ((int64_t)1 << 31)) return false;   // 32-bit store offsets
+    a.yplane = (int)yplane;
+    a.se = V;   // the widest store that divides a row
+    while (a.se > 1 && a.qout % a.se != 0) a.se >>= 1;
+    a.nq = a.qout / a.se;
     a.nsv = (g.K * a.nq + kThreads - 1) / kThreads;
     if (a.nsv > kImpMaxStores) return false;
-    a.relu = epi.relu ? 1 : 0;
     const size_t tile = 2 * (size_t)g.K * ostride * out_bytes;
     // two workgroups per CU with the deepest copy-ahead that fits, else one
     size_t lds = 0;
@@ -455,11 +580,13 @@ inline bool mf_imp_plan(const Geom& g, int out_bytes, const Epi& epi, int cus, M
     a.off_tile = a.off_stage + a.nstage * a.stage_bytes;
     a.off_bias = a.off_tile + (int)tile;
     // bands: about wgs_per_cu workgroups per CU in total, and at least 4
-    // output rows a band (fewer would re-read most input rows per row)
+    // output rows a band (fewer would re-read most input rows per row);
+    // whole row pairs with the pool
     const int64_t target = (int64_t)cus * wgs;
-    int nb = (int)std::min<int64_t>(g.P, std::max<int64_t>(1, (target + g.N / 2) / std::max(g.N, 1)));
-    a.band = std::max((g.P + nb - 1) / nb, std::min(g.P, 4));
-    a.nbands = (g.P + a.band - 1) / a.band;
+    int nb = (int)std::min<int64_t>(a.Pc, std::max<int64_t>(1, (target + g.N / 2) / std::max(g.N, 1)));
+    a.band = std::max((a.Pc + nb - 1) / nb, std::min(a.Pc, 4));
+    if (a.pool) a.band += a.band & 1;
+    a.nbands = (a.Pc + a.band - 1) / a.band;
     const int64_t ntask = (int64_t)g.N * a.nbands;
     if (ntask >= ((int64_t)1 << 31)) return false;
     a.ntask = (int)ntask;

@@ -169,10 +169,12 @@ ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
  * plane and its filter exceed 48 KB of LDS.  Dense: the re-laid-out filter;
  * CIW_ERR_UNSUPPORTED unless the input is fp16/bf16, groups == 1, C is a
  * multiple of 16, K <= 64, W a multiple of 8, stride_h == 1, the filter is
- * 3x3 with C <= 64 or 1x1 with C in {16, 32, 64}, an output row needs at
- * most 4 stores per thread (K*Q/V <= 1024 with V = 16 / output element
- * bytes when Q is a multiple of V, else K*Q <= 1024), no
- * CIW_FLAG_MAXPOOL2, and an image of x has fewer than 2^31 bytes. */
+ * 3x3 with C <= 64 or 1x1 with C in {16, 32, 64}, a stored output row
+ * needs at most 4 stores per thread (K*Qs/E <= 1024, where Qs is Q, or Q/2
+ * with CIW_FLAG_MAXPOOL2, and E the largest power of two that divides Qs
+ * with E * output element bytes <= 16), K times the output plane has
+ * fewer than 2^31 elements, and an image of x has fewer than 2^31 bytes.
+ * The fused ReLU and 2x2 max-pool are supported. */
 ciw_status conv2d_implicit_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
                                            ciw_dtype out_dtype, uint32_t flags, size_t* bytes);
 

@@ -126,6 +126,55 @@ def test_relu_and_no_bias(dtype):
     assert np.all(got >= 0)
 
 
+# the fused epilogue: 2x2 max-pool (stride 2, floor), with or without ReLU
+POOL_SHAPES = [s for s in SHAPES if s[2] >= 2] + [
+    (2, 32, 9, 16, 40, 3, 1, 1, 1),     # P = 9: the last output row has no pair
+    (1, 64, 7, 56, 64, 3, 1, 1, 1),     # pooled rows of 28: 4-element stores
+    (1, 16, 6, 40, 8, 1, 2, 0, 1),      # Q = 20, pooled 10: 2-element stores
+]
+
+
+@pytest.mark.parametrize("shape", POOL_SHAPES)
+@pytest.mark.parametrize("dtype,out,relu", [("f16", "f16", True), ("bf16", "bf16", False),
+                                            ("f16", "f32", False), ("bf16", "f32", True)])
+def test_pool_shapes_against_oracle(shape, dtype, out, relu):
+    N, C, H, W, K, R, sw, pad, dil = shape
+    L = workloads.Layer("imp", N=N, C=C, H=H, W=W, K=K, R=R, S=R, stride=(1, sw),
+                        pad=(pad, pad), dil=(dil, dil), dtype=dtype, out_dtype=out,
+                        x_dist=("normal", 0.0, 1.0), seed=sum(shape) + 3)
+    P, Q = oracle.out_dims(L.x_shape, L.w_shape, L.stride, L.pad, L.dil, 1)
+    if P < 2 or Q < 2:
+        pytest.skip("no 2x2 region")
+    say(f"implicit pool {shape} {dtype}->{out} relu={relu}")
+    x, w, b = workloads.make_inputs(L)
+    flags = IMP | ciw.CIW_FLAG_MAXPOOL2 | (ciw.CIW_FLAG_RELU if relu else 0)
+    got = to_host_f64(run(L, x, w, b, flags=flags))
+    conv = oracle.conv2d(f64(x, dtype), f64(w, dtype), f64(b, dtype), L.stride, L.pad, L.dil, 1)
+    ref = oracle.relu_pool(conv, relu=relu, pool=True)
+    check(got, ref, f"pool {shape} {dtype}->{out} relu={relu}")
+
+
+def test_resnet_layer_relu_pool_full_size():
+    """The full batch with ReLU and the 2x2 pool fused, in the launch
+    configuration the benchmark times: every output against the
+    materialised path's fused epilogue, and sampled outputs against the
+    oracle (each the maximum of its four convolution outputs)."""
+    L = RESNET
+    say("implicit resnet_3x3_fp16 full size, relu + pool")
+    x, w, b = workloads.make_inputs(L)
+    flags = ciw.CIW_FLAG_RELU | ciw.CIW_FLAG_MAXPOOL2
+    got_all = to_host_f64(run(L, x, w, b, flags=IMP | flags))
+    assert got_all.shape == (L.N, L.K, 28, 28)
+    explicit = to_host_f64(run(L, x, w, b, flags=flags))
+    check(got_all, explicit, "against the materialised path")
+    rng = np.random.default_rng(92)
+    idx = sample_indices(got_all.shape, 1000, rng)
+    quad = np.concatenate([idx * [1, 1, 2, 2] + [0, 0, dy, dx] for dy in (0, 1) for dx in (0, 1)])
+    pts = oracle.conv2d_points(f64(x, "f16"), f64(w, "f16"), None, quad, L.stride, L.pad, L.dil, 1)
+    ref = np.maximum(pts.reshape(4, -1).max(axis=0), 0)
+    check(got_all[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]], ref, "sampled")
+
+
 def test_empty_batch():
     L = RESNET.replace(N=0)
     xd = torch.empty(L.x_shape, dtype=torch.float16, device="cuda")
@@ -149,7 +198,7 @@ def test_errors():
         return fn(ctypes.byref(desc), code, code, x.data_ptr(), w.data_ptr(), None, y.data_ptr(),
                   ws.data_ptr(), ws.numel(), flags, None)
     assert st(IMP) == 0
-    assert st(IMP | ciw.CIW_FLAG_MAXPOOL2) == ciw._lib.CIW_ERR_UNSUPPORTED
+    assert st(IMP | ciw.CIW_FLAG_MAXPOOL2) == 0
     assert st(IMP, C=24) == ciw._lib.CIW_ERR_UNSUPPORTED
     assert st(IMP, W=52) == ciw._lib.CIW_ERR_UNSUPPORTED
     assert st(IMP, sh=2) == ciw._lib.CIW_ERR_UNSUPPORTED

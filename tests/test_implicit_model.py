@@ -12,6 +12,7 @@ the kernel ever runs on a GPU.  The plan is tied to the library through
 conv2d_implicit_workspace_bytes (eligibility and workspace size).
 """
 import ctypes
+import itertools
 
 import numpy as np
 import pytest
@@ -42,7 +43,9 @@ def compiled(R, S, CB):
 
 
 def plan(g, out_bytes, relu=False, pool=False, cus=256):
-    if g.C % 16 or g.K > 64 or g.W % 8 or g.sh != 1 or pool:
+    if g.C % 16 or g.K > 64 or g.W % 8 or g.sh != 1:
+        return None
+    if pool and (g.P < 2 or g.Q < 2):
         return None
     CB = g.C // 16
     if not compiled(g.R, g.S, CB):
@@ -68,8 +71,17 @@ def plan(g, out_bytes, relu=False, pool=False, cus=256):
     if (ost * out_bytes // 16) % 2 == 0:
         ost += V
     a["ostride"] = ost
-    a["vec"] = 1 if g.Q % V == 0 else 0
-    a["nq"] = g.Q // V if a["vec"] else g.Q
+    a["pool"] = int(pool)
+    a["Pc"] = 2 * (g.P // 2) if pool else g.P
+    a["qout"] = g.Q // 2 if pool else g.Q
+    a["yplane"] = (g.P // 2 if pool else g.P) * a["qout"]
+    if g.K * a["yplane"] >= 2 ** 31:
+        return None
+    se = V
+    while se > 1 and a["qout"] % se:
+        se //= 2
+    a["se"] = se
+    a["nq"] = a["qout"] // se
     a["nsv"] = -(-(g.K * a["nq"]) // THREADS)
     if a["nsv"] > MAX_STORES:
         return None
@@ -90,9 +102,12 @@ def plan(g, out_bytes, relu=False, pool=False, cus=256):
     a["off_tile"] = a["off_stage"] + a["nstage"] * a["stage_bytes"]
     a["off_bias"] = a["off_tile"] + tile
     target = cus * wgs
-    nb = min(g.P, max(1, (target + g.N // 2) // max(g.N, 1)))
-    a["band"] = max(-(-g.P // nb), min(g.P, 4))
-    a["nbands"] = -(-g.P // a["band"])
+    Pc = a["Pc"]
+    nb = min(Pc, max(1, (target + g.N // 2) // max(g.N, 1)))
+    a["band"] = max(-(-Pc // nb), min(Pc, 4))
+    if pool:
+        a["band"] += a["band"] & 1
+    a["nbands"] = -(-Pc // a["band"])
     a["ntask"] = g.N * a["nbands"]
     a["steps"] = g.R * g.S * CB
     a["CB"] = CB
@@ -116,13 +131,23 @@ def prep_filter(w16, g, a):
     return out
 
 
+def stores_at(i, a):
+    """The step of output row i stores row i - 1: every row, or with the
+    pool the second row of each pair."""
+    return i >= 1 and (not a["pool"] or (i - 1) % 2 == 1)
+
+
+def tile_of(i, a):
+    return (i >> a["pool"]) & 1
+
+
 def later_ops(j, a, J):
     """Vector-memory operations a wave issues after the copy of row j, up to
     the wait for it (prologue copies rows 0..pf; step v copies row
-    v + pf + 1, then stores output row v - span)."""
+    v + pf + 1, then stores output row v - span if that step stores)."""
     pf, nd, nsv, span = a["pf"], a["nd"], a["nsv"], a["span"]
     dma = lambda v: nd if v + pf + 1 < J else 0
-    st = lambda v: nsv if v >= span else 0
+    st = lambda v: nsv if stores_at(v - span + 1, a) else 0
     if j <= pf:
         c = nd * (min(pf + 1, J) - 1 - j)
         c += sum(dma(v) + st(v) for v in range(j - 1))
@@ -142,19 +167,25 @@ def issue_log(a, J):
         if v + a["pf"] + 1 < J:
             log += [("dma", v + a["pf"] + 1)] * 1
         i = v - a["span"] + 1
-        if i >= 1:
+        if stores_at(i, a):
             log += [("st", i - 1)]
     return log, waits
 
 
 def emulate(x16, w16, b, g, a, relu):
     """Replays the kernel on the CPU; returns y (fp64, before output rounding
-    is applied by the caller) and checks every access."""
+    is applied by the caller) and checks every access.  Outputs go through
+    the two tiles and the store plan, as in the kernel; `wrote` records
+    which output row each tile element last held."""
     N, C, H, W, K = g.N, g.C, g.H, g.W, g.K
+    pool = a["pool"]
+    Po, Qo = (g.P // 2, g.Q // 2) if pool else (g.P, g.Q)
     xbytes = x16.reshape(-1).view(np.uint8)
     img_bytes = C * H * W * 2
     aperm = prep_filter(w16, g, a)
-    y = np.full((N, K, g.P, g.Q), np.nan)
+    y = np.full((N, K, Po, Qo), np.nan)
+    yflat = y.reshape(-1)
+    stores = store_plan(g, a)
     seen = np.zeros(a["ntask"], dtype=bool)
     span, cg, CS, wv = a["span"], a["cg"], a["CS"], a["wv"]
     nd, nchunks = a["nd"], a["nchunks"]
@@ -168,7 +199,25 @@ def emulate(x16, w16, b, g, a, relu):
         seen[task] = True
         n, band = divmod(task, a["nbands"])
         h0 = band * a["band"]
-        rows = min(a["band"], g.P - h0)
+        rows = min(a["band"], a["Pc"] - h0)
+        assert rows >= 1 and (not pool or (h0 % 2 == 0 and rows % 2 == 0))
+        tile = np.full((2, K, a["ostride"]), np.nan)
+        wrote = np.full((2, K, a["ostride"]), -1)
+
+        def store_row(i):
+            t = tile_of(i, a)
+            yrow = n * K * a["yplane"] + ((h0 + i) >> pool) * a["qout"]
+            for (src, dst) in stores:
+                k, c0 = divmod(src, a["ostride"])
+                if pool:
+                    cols = list(range(c0, c0 + 2 * a["se"]))
+                else:
+                    cols = list(range(c0, c0 + a["se"]))
+                assert all(wrote[t, k, c] == i and c < g.Q for c in cols)
+                vals = tile[t, k, cols]
+                if pool:
+                    vals = np.maximum(vals[0::2], vals[1::2])
+                yflat[yrow + dst:yrow + dst + a["se"]] = vals
         J = rows + span - 1
         lds = np.zeros(a["lds"], dtype=np.uint8)
         # copy plan
@@ -227,6 +276,11 @@ def emulate(x16, w16, b, g, a, relu):
         transpose_row(0)
         done = {0}
         for u in range(J):
+            i = u - span + 1
+            if stores_at(i, a):
+                # the tile it reads is not the one this step's multiply writes
+                assert tile_of(i - 1, a) != tile_of(i, a)
+                store_row(i - 1)
             if u + a["pf"] + 1 < J:
                 # the staging buffer it overwrites held row u, transposed already
                 assert u in done
@@ -262,32 +316,54 @@ def emulate(x16, w16, b, g, a, relu):
                         acc += A @ Bm
                     if relu:
                         acc = np.maximum(acc, 0)
+                    t = tile_of(i, a)
                     for ml in range(32):
                         w_ = 32 * bb + ml
                         assert w_ < a["ostride"]
-                        if w_ < g.Q:
-                            for kk in range(32):
-                                k = kh * 32 + kk
-                                if k < K:
-                                    y[n, k, h0 + i, w_] = acc[ml, kk]
+                        for kk in range(32):
+                            k = kh * 32 + kk
+                            if k < K:
+                                v = acc[ml, kk]
+                                if pool and i % 2 == 1:
+                                    # the first row of the pair, same lane
+                                    assert wrote[t, k, w_] == i - 1
+                                    v = max(v, tile[t, k, w_])
+                                tile[t, k, w_] = v
+                                wrote[t, k, w_] = i
+        store_row(rows - 1)
     assert seen.all()
     return y
 
 
-def store_indices_ok(g, a):
-    """The store plan: every (k, vector) of an output row exactly covered,
-    reads inside the tile row, writes inside the output row block."""
-    E = (16 // a["out_bytes"]) if a["vec"] else 1
-    covered = set()
+def store_plan(g, a):
+    """(tile offset, y offset) of every store of one output row, over all
+    threads: idx = tid + 256 j, surplus threads repeating the last."""
+    out = []
     for tid in range(THREADS):
         for j in range(a["nsv"]):
             idx = min(tid + THREADS * j, g.K * a["nq"] - 1)
             k, v = divmod(idx, a["nq"])
-            src, dst = k * a["ostride"] + v * E, k * g.P * g.Q + v * E
-            assert src + E <= g.K * a["ostride"] and (src + E - 1) // a["ostride"] == k
-            assert v * E + E <= g.Q and dst + E <= g.K * g.P * g.Q
-            covered.add((k, v))
+            out.append((k * a["ostride"] + ((v * a["se"]) << a["pool"]),
+                        k * a["yplane"] + v * a["se"]))
+    return out
+
+
+def store_indices_ok(g, a):
+    """The store plan: every (k, vector) of an output row exactly covered,
+    reads inside the tile row, writes inside the output row block, and both
+    aligned to the store's width."""
+    E, eb = a["se"], a["out_bytes"]
+    span = E << a["pool"]          # tile elements one store reads
+    covered = set()
+    for src, dst in store_plan(g, a):
+        k = src // a["ostride"]
+        assert src + span <= g.K * a["ostride"] and (src + span - 1) // a["ostride"] == k
+        assert (src - k * a["ostride"]) + span <= g.Q
+        assert dst + E <= g.K * a["yplane"] and (dst - k * a["yplane"]) + E <= a["qout"]
+        assert (src * eb) % min(16, span * eb) == 0 and (dst * eb) % (E * eb) == 0
+        covered.add((k, dst - k * a["yplane"]))
     assert len(covered) == g.K * a["nq"]
+    assert E * eb in (2, 4, 8, 16) and a["qout"] % E == 0
 
 
 CASES = [
@@ -303,11 +379,12 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES)
-@pytest.mark.parametrize("out_bytes,cus", [(2, 256), (4, 256), (2, 1)])
-def test_emulated_kernel_matches_oracle(case, out_bytes, cus):
+@pytest.mark.parametrize("out_bytes,cus,pool", [(2, 256, False), (4, 256, False), (2, 1, False),
+                                                (2, 256, True), (4, 1, True)])
+def test_emulated_kernel_matches_oracle(case, out_bytes, cus, pool):
     N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw = case
     g = G(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw)
-    a = plan(g, out_bytes, cus=cus)
+    a = plan(g, out_bytes, pool=pool, cus=cus)
     assert a is not None
     rng = np.random.default_rng(7)
     x = rng.standard_normal((N, C, H, W)).astype(np.float16)
@@ -317,8 +394,7 @@ def test_emulated_kernel_matches_oracle(case, out_bytes, cus):
     got = emulate(x, w, b, g, a, relu)
     ref = oracle.conv2d(x.astype(np.float64), w.astype(np.float64), b.astype(np.float64),
                         (sh, sw), (ph, pw), (dh, dw), 1)
-    if relu:
-        ref = np.maximum(ref, 0)
+    ref = oracle.relu_pool(ref, relu=relu, pool=pool)
     assert not np.isnan(got).any()
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-9 * max(1.0, np.abs(ref).max()))
     store_indices_ok(g, a)
@@ -371,13 +447,17 @@ def test_plan_agrees_with_library():
         if g.P < 1 or g.Q < 1:
             continue
         desc = ciw.make_desc((N, C, H, W), (K, C, R, S), (sh, sw), (ph, pw), (dh, dw), 1)
-        for dt, ob in ((ciw.CIW_F16, 2), (ciw.CIW_BF16, 2), (ciw.CIW_F16, 4)):
+        for (dt, ob), pool in itertools.product(((ciw.CIW_F16, 2), (ciw.CIW_BF16, 2),
+                                                  (ciw.CIW_F16, 4)), (False, True)):
             out_dt = dt if ob == 2 else ciw.CIW_F32
-            a = plan(g, ob)
+            a = plan(g, ob, pool=pool)
             out = ctypes.c_size_t()
-            st = _lib.load().conv2d_implicit_workspace_bytes(ctypes.byref(desc), dt, out_dt, 0,
+            flags = _lib.CIW_FLAG_MAXPOOL2 if pool else 0
+            st = _lib.load().conv2d_implicit_workspace_bytes(ctypes.byref(desc), dt, out_dt, flags,
                                                              ctypes.byref(out))
-            if a is None:
+            if pool and (g.P < 2 or g.Q < 2):
+                assert st == _lib.CIW_ERR_INVALID_ARG, s
+            elif a is None:
                 assert st == _lib.CIW_ERR_UNSUPPORTED, s
             else:
                 assert st == 0, s
