@@ -80,17 +80,19 @@ def test_graph_replays_match_eager(name):
         assert np.array_equal(got, ref), f"{name}: replay {rep} differs from the eager result"
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_graph_replays_match_eager_implicit(dtype):
+@pytest.mark.parametrize("dtype,pool", [("f16", False), ("bf16", False), ("f16", True)])
+def test_graph_replays_match_eager_implicit(dtype, pool):
     """conv2d_fwd with the window rows built in LDS (filter re-layout, then
-    the contraction) captured and replayed the same way."""
+    the contraction), with ReLU and optionally the 2x2 pool, captured and
+    replayed the same way."""
     L = workloads.LAYERS["resnet_3x3_fp16"].replace(N=4, dtype=dtype, out_dtype=dtype)
-    say(f"graph replay implicit {dtype} N={L.N}")
+    say(f"graph replay implicit {dtype} N={L.N} pool={pool}")
     lib = _lib.load()
     x, w, _ = (to_dev(a, L.dtype) for a in workloads.make_inputs(L))
     desc = ciw.make_desc(L.x_shape, L.w_shape, L.stride, L.pad, L.dil, 1)
-    y = torch.empty((L.N, L.K, 56, 56), dtype=torch_dtype(dtype), device="cuda")
-    flags = ciw.CIW_FLAG_IMPLICIT | ciw.CIW_FLAG_RELU
+    side = 28 if pool else 56
+    y = torch.empty((L.N, L.K, side, side), dtype=torch_dtype(dtype), device="cuda")
+    flags = ciw.CIW_FLAG_IMPLICIT | ciw.CIW_FLAG_RELU | (ciw.CIW_FLAG_MAXPOOL2 if pool else 0)
     ws_bytes = ciw.conv2d_implicit_workspace_bytes(desc, CODE[dtype], CODE[dtype], flags)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
@@ -115,4 +117,4 @@ def test_graph_replays_match_eager_implicit(dtype):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert np.array_equal(to_host_bits(y), ref), f"implicit {dtype}: replay {rep} differs"
+        assert np.array_equal(to_host_bits(y), ref), f"implicit {dtype} pool={pool}: replay {rep} differs"
