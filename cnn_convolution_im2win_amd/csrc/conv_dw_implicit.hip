@@ -32,6 +32,7 @@ struct DwImpArgs {
     int per;             // planes per workgroup
     int Po, Qo;          // output extent (pooled or not)
     int relu, pool;
+    int strip;           // 3x3 strip form (planes padded to whole strips)
     FastDiv fdHW, fdW, fdPQo, fdQo;
     FastDiv fdStrip;     // Qo * ceil(P / kSH): strip items per plane
 };
@@ -102,7 +103,8 @@ __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
     if (STRIP) {
         // 3x3, stride 1, dilation 1, no pool: a lane computes kSH outputs
         // down one column (consecutive lanes: consecutive columns), reading
-        // the (kSH + 2) x 3 inputs and the 9 taps once
+        // the (kSH + 2) x 3 inputs and the 9 taps once (the plane's zero
+        // rows reach the last strip's end)
         const int nstrip = (a.P + kSH - 1) / kSH;
         const int per_plane = a.Qo * nstrip;
         for (int it = tid; it < np * per_plane; it += kDThreads) {
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
             for (int rr = 0; rr < kSH + 2; ++rr)
 #pragma unroll
                 for (int cc = 0; cc < 3; ++cc)
-                    in[rr][cc] = (oh0 + rr < a.Hp) ? src[rr * a.Wp + cc] : 0.f;
+                    in[rr][cc] = src[rr * a.Wp + cc];
             const float b = bl[q];
             TOut* yo = ys + (size_t)q * PQo + (size_t)oh0 * a.Qo + ow;
 #pragma unroll
@@ -174,12 +176,25 @@ __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
 bool dw_imp_plan(const Geom& g, const Epi& epi, int n_images, DwImpArgs& a, size_t& lds, int64_t& grid) {
     a.C = g.C; a.H = g.H; a.W = g.W; a.P = g.P; a.Q = g.Q; a.R = g.R; a.S = g.S;
     a.sh = g.sh; a.sw = g.sw; a.ph = g.ph; a.pw = g.pw; a.dh = g.dh; a.dw = g.dw;
-    a.Hp = g.H + 2 * g.ph;
     a.Wp = g.W + 2 * g.pw;
     // LDS plane area a multiple of 4 words (the zeroing writes 16 bytes)
-    while ((a.Hp * a.Wp) % 4) ++a.Hp;
-    const int64_t plane_bytes = ((int64_t)a.Hp * a.Wp + (int64_t)g.R * g.S + 1) * 4;
-    if (plane_bytes > kDwLdsBytes) return false;
+    auto plane_of = [&](int hp) {
+        while (((int64_t)hp * a.Wp) % 4) ++hp;
+        return hp;
+    };
+    auto bytes_of = [&](int hp) { return ((int64_t)hp * a.Wp + (int64_t)g.R * g.S + 1) * 4; };
+    a.Hp = plane_of(g.H + 2 * g.ph);
+    if (bytes_of(a.Hp) > kDwLdsBytes) return false;
+    // the strip form reads kSH + 2 rows from each strip's first row: pad the
+    // plane with zero rows to the last strip's end, when that still fits
+    const int nstrip = (g.P + kSH - 1) / kSH;
+    a.strip = g.R == 3 && g.S == 3 && g.sh == 1 && g.sw == 1 && g.dh == 1 && g.dw == 1 && !epi.pool;
+    if (a.strip) {
+        const int hs = plane_of(std::max(a.Hp, nstrip * kSH + 2));
+        if (bytes_of(hs) <= kDwLdsBytes) a.Hp = hs;
+        else a.strip = 0;
+    }
+    const int64_t plane_bytes = bytes_of(a.Hp);
     const int64_t planes = (int64_t)n_images * g.C;
     if (planes * std::max<int64_t>((int64_t)g.H * g.W, (int64_t)g.P * g.Q) >= ((int64_t)1 << 31)) return false;
     a.planes = (int)planes;
@@ -187,6 +202,15 @@ bool dw_imp_plan(const Geom& g, const Epi& epi, int n_images, DwImpArgs& a, size
     // at least about 1024 workgroups
     int per = (int)std::min<int64_t>(kDwLdsBytes / plane_bytes, std::max<int64_t>(1, 16 * kDThreads / ((int64_t)g.H * g.W)));
     per = std::max(1, std::min<int>(per, (int)std::max<int64_t>(1, planes / 1024)));
+    if (a.strip) {
+        // every thread the same number of strips where that costs less
+        // time per plane: 20 planes of 28 strips take 3 passes of 256
+        // threads (2.2 on average), 18 planes take 2
+        const int spp = g.Q * nstrip;
+        const int it = (per * spp + kDThreads - 1) / kDThreads;
+        const int per2 = (it - 1) * kDThreads / spp;
+        if (it > 1 && per2 >= 1 && (int64_t)(it - 1) * per < (int64_t)it * per2) per = per2;
+    }
     a.per = per;
     a.relu = epi.relu;
     a.pool = epi.pool;
@@ -210,9 +234,8 @@ hipError_t launch_dwi(const Geom& g, const void* x, const void* w, const void* b
     int64_t grid = 0;
     if (!dw_imp_plan(g, epi, g.N, a, lds, grid)) return hipErrorInvalidValue;
     const bool r3 = g.R == 3 && g.S == 3;
-    const bool strip = r3 && g.sh == 1 && g.sw == 1 && g.dh == 1 && g.dw == 1 && !epi.pool;
     void (*kfn)(const TIn*, const TIn*, const TIn*, TOut*, DwImpArgs) =
-        strip ? conv_dw_implicit_kernel<TIn, TOut, 3, 3, true>
+        a.strip ? conv_dw_implicit_kernel<TIn, TOut, 3, 3, true>
               : r3 ? conv_dw_implicit_kernel<TIn, TOut, 3, 3, false>
                    : conv_dw_implicit_kernel<TIn, TOut, 0, 0, false>;
     hipLaunchKernelGGL(kfn, dim3((uint32_t)grid), dim3(kDThreads), lds, st,
