@@ -33,6 +33,7 @@ struct DwImpArgs {
     int Po, Qo;          // output extent (pooled or not)
     int relu, pool;
     int strip;           // 3x3 strip form (planes padded to whole strips)
+    int dQ, dH, dW;      // 256 input elements as planes, rows and columns (dH < H, dW < W)
     FastDiv fdHW, fdW, fdPQo, fdQo;
     FastDiv fdStrip;     // Qo * ceil(P / kSH): strip items per plane
 };
@@ -81,18 +82,31 @@ __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
     }
     for (int e = tid; e < np; e += kDThreads) bl[e] = bias ? to_f32(bias[(p0 + e) % a.C]) : 0.f;
     __syncthreads();
-    // the planes' interiors
+    // the planes' interiors: a thread's elements are kDThreads apart, so
+    // its LDS position is split into (plane, row, column) once and then
+    // stepped by (dQ, dH, dW) with the carries
+    const int step = a.dQ * HpWp + a.dH * a.Wp + a.dW;
     for (int e0 = tid; e0 < total; e0 += kU * kDThreads) {
         if (e0 != tid) load(e0);
+        const uint32_t q0 = fdiv((uint32_t)e0, a.fdHW);
+        const int r0 = e0 - (int)q0 * HW;
+        int hh = (int)fdiv((uint32_t)r0, a.fdW);
+        int ww = r0 - hh * a.W;
+        int off = (int)q0 * HpWp + (hh + a.ph) * a.Wp + ww + a.pw;
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int e = e0 + u * kDThreads;
-            if (e < total) {
-                const uint32_t q = fdiv((uint32_t)e, a.fdHW);
-                const int r = e - (int)q * HW;
-                const uint32_t hh = fdiv((uint32_t)r, a.fdW);
-                const int ww = r - (int)hh * a.W;
-                pl[q * HpWp + (hh + a.ph) * a.Wp + ww + a.pw] = v[u];
+            if (e0 + u * kDThreads < total) pl[off] = v[u];
+            ww += a.dW;
+            hh += a.dH;
+            off += step;
+            if (ww >= a.W) {            // next row
+                ww -= a.W;
+                ++hh;
+                off += a.Wp - a.W;
+            }
+            if (hh >= a.H) {            // next plane
+                hh -= a.H;
+                off += HpWp - a.H * a.Wp;
             }
         }
     }
@@ -216,6 +230,12 @@ bool dw_imp_plan(const Geom& g, const Epi& epi, int n_images, DwImpArgs& a, size
     a.pool = epi.pool;
     a.Po = out_rows(g, epi);
     a.Qo = out_cols(g, epi);
+    {
+        const int HW = g.H * g.W;
+        a.dQ = kDThreads / HW;
+        a.dH = (kDThreads % HW) / g.W;
+        a.dW = (kDThreads % HW) % g.W;
+    }
     a.fdHW = make_fastdiv((uint32_t)(g.H * g.W));
     a.fdW = make_fastdiv((uint32_t)g.W);
     a.fdPQo = make_fastdiv((uint32_t)(a.Po * a.Qo));
