@@ -34,6 +34,7 @@ struct DwImpArgs {
     int relu, pool;
     int strip;           // 3x3 strip form (planes padded to whole strips)
     int dQ, dH, dW;      // 256 input elements as planes, rows and columns (dH < H, dW < W)
+    int vec4;            // H * W a multiple of 4 and W >= 4: fp32 input staged with 16-byte loads
     FastDiv fdHW, fdW, fdPQo, fdQo;
     FastDiv fdStrip;     // Qo * ceil(P / kSH): strip items per plane
 };
@@ -65,7 +66,24 @@ __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
     const int total = np * HW;
     constexpr int kU = 16;
     float v[kU];
+    // fp32 planes whose area is a multiple of 4 come in 16-byte loads:
+    // e0 then counts float4s, and float4 e0 + u * kDThreads lands in
+    // v[4u .. 4u + 3]
+    const bool vec4 = sizeof(TIn) == 4 && a.vec4;
     auto load = [&](int e0) {
+        if (vec4) {
+            const float4* xs4 = reinterpret_cast<const float4*>(xs);
+#pragma unroll
+            for (int u = 0; u < kU / 4; ++u) {
+                const int e4 = e0 + u * kDThreads;
+                const float4 t = 4 * e4 < total ? xs4[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
+                v[4 * u] = t.x;
+                v[4 * u + 1] = t.y;
+                v[4 * u + 2] = t.z;
+                v[4 * u + 3] = t.w;
+            }
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int e = e0 + u * kDThreads;
@@ -82,11 +100,36 @@ __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
     }
     for (int e = tid; e < np; e += kDThreads) bl[e] = bias ? to_f32(bias[(p0 + e) % a.C]) : 0.f;
     __syncthreads();
+    if (vec4) {
+        // four elements of one plane a float4 (the area is a multiple of 4),
+        // the last ones on the next row when the row ends inside it
+        const int total4 = total / 4;
+        for (int e0 = tid; e0 < total4; e0 += (kU / 4) * kDThreads) {
+            if (e0 != tid) load(e0);
+#pragma unroll
+            for (int u = 0; u < kU / 4; ++u) {
+                const int e4 = e0 + u * kDThreads;
+                if (e4 < total4) {
+                    const int el = 4 * e4;
+                    const uint32_t q = fdiv((uint32_t)el, a.fdHW);
+                    const int r = el - (int)q * HW;
+                    const int hh = (int)fdiv((uint32_t)r, a.fdW);
+                    const int ww = r - hh * a.W;
+                    float* row = pl + q * HpWp + (hh + a.ph) * a.Wp + a.pw;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int c = ww + j;
+                        row[c < a.W ? c : c - a.W + a.Wp] = v[4 * u + j];
+                    }
+                }
+            }
+        }
+    }
     // the planes' interiors: a thread's elements are kDThreads apart, so
     // its LDS position is split into (plane, row, column) once and then
     // stepped by (dQ, dH, dW) with the carries
     const int step = a.dQ * HpWp + a.dH * a.Wp + a.dW;
-    for (int e0 = tid; e0 < total; e0 += kU * kDThreads) {
+    for (int e0 = tid; !vec4 && e0 < total; e0 += kU * kDThreads) {
         if (e0 != tid) load(e0);
         const uint32_t q0 = fdiv((uint32_t)e0, a.fdHW);
         const int r0 = e0 - (int)q0 * HW;
@@ -235,6 +278,7 @@ bool dw_imp_plan(const Geom& g, const Epi& epi, int n_images, DwImpArgs& a, size
         a.dQ = kDThreads / HW;
         a.dH = (kDThreads % HW) / g.W;
         a.dW = (kDThreads % HW) % g.W;
+        a.vec4 = (HW % 4 == 0 && g.W >= 4) ? 1 : 0;
     }
     a.fdHW = make_fastdiv((uint32_t)(g.H * g.W));
     a.fdW = make_fastdiv((uint32_t)g.W);

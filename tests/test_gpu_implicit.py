@@ -251,6 +251,8 @@ DW_SHAPES = [
     (2, 6, 12, 10, 3, 1, 0, 1, "f16", "f32"),
     (1, 3, 64, 64, 3, 1, 1, 1, "bf16", "f32"),
     (4, 33, 1, 1, 1, 1, 0, 1, "f32", "f32"),
+    (1, 4, 70, 70, 3, 1, 1, 1, "f32", "f32"),    # 16-byte staging, a plane over two load rounds
+    (2, 10, 6, 6, 5, 2, 2, 1, "f32", "f32"),     # 16-byte staging, float4s across row ends
 ]
 
 
