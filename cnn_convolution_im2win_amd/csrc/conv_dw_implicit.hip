@@ -36,7 +36,7 @@ struct DwImpArgs {
     int dQ, dH, dW;      // 256 input elements as planes, rows and columns (dH < H, dW < W)
     int vec4;            // H * W a multiple of 4 and W >= 4: fp32 input staged with 16-byte loads
     FastDiv fdHW, fdW, fdPQo, fdQo;
-    FastDiv fdStrip;     // Qo * ceil(P / kSH): strip items per plane
+    FastDiv fdStrip;     // strip items per plane: Qo * ceil(P / kSH), or Qo * ceil(Po / kPS) with the pool
 };
 
 // KR x KS: the filter extent when fixed at compile time (0: run time).
@@ -45,6 +45,7 @@ struct DwImpArgs {
 // is copied element by element (consecutive lanes, consecutive elements:
 // coalesced), and lane i of a pass computes output o0 + i.
 constexpr int kSH = 7;   // outputs per lane down a column (strip form)
+constexpr int kPS = 4;   // pooled outputs per lane down a column (strip form with the pool)
 
 template <typename TIn, typename TOut, int KR, int KS, bool STRIP>
 __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
@@ -157,6 +158,54 @@ __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
 
     const int PQo = a.Po * a.Qo;
     TOut* ys = y + (size_t)p0 * PQo;
+    if (STRIP && a.pool) {
+        // 3x3, stride 1, dilation 1 with the 2x2 pool: a lane computes kPS
+        // pooled outputs down one pooled column, the 2 kPS x 2 convolution
+        // outputs under them from the (2 kPS + 2) x 4 inputs and the 9 taps
+        // read once (the plane's zero rows reach the last strip's end)
+        const int nps = (a.Po + kPS - 1) / kPS;
+        const int per_plane = a.Qo * nps;
+        for (int it = tid; it < np * per_plane; it += kDThreads) {
+            const uint32_t q = fdiv((uint32_t)it, a.fdStrip);
+            const int r = it - (int)q * per_plane;
+            const uint32_t st = fdiv((uint32_t)r, a.fdQo);
+            const int ow = r - (int)st * a.Qo;
+            const int oi0 = (int)st * kPS;
+            const float* src = pl + q * HpWp + 2 * oi0 * a.Wp + 2 * ow;
+            const float* wt = wl + q * 9;
+            float wr[9];
+#pragma unroll
+            for (int t = 0; t < 9; ++t) wr[t] = wt[t];
+            float in[2 * kPS + 2][4];
+#pragma unroll
+            for (int rr = 0; rr < 2 * kPS + 2; ++rr)
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) in[rr][cc] = src[rr * a.Wp + cc];
+            const float b = bl[q];
+            TOut* yo = ys + (size_t)q * PQo + (size_t)oi0 * a.Qo + ow;
+#pragma unroll
+            for (int i = 0; i < kPS; ++i) {
+                if (oi0 + i < a.Po) {
+                    float m = 0.f;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const int dr = 2 * i + (d >> 1), dc = d & 1;
+                        float acc = 0.f;
+#pragma unroll
+                        for (int rr = 0; rr < 3; ++rr)
+#pragma unroll
+                            for (int cc = 0; cc < 3; ++cc)
+                                acc = fmaf(in[dr + rr][dc + cc], wr[rr * 3 + cc], acc);
+                        float v = acc + b;
+                        if (a.relu) v = fmaxf(v, 0.f);
+                        m = d == 0 ? v : fmaxf(m, v);
+                    }
+                    yo[i * a.Qo] = from_f32<TOut>(m);
+                }
+            }
+        }
+        return;
+    }
     if (STRIP) {
         // 3x3, stride 1, dilation 1, no pool: a lane computes kSH outputs
         // down one column (consecutive lanes: consecutive columns), reading
@@ -244,10 +293,12 @@ bool dw_imp_plan(const Geom& g, const Epi& epi, int n_images, DwImpArgs& a, size
     if (bytes_of(a.Hp) > kDwLdsBytes) return false;
     // the strip form reads kSH + 2 rows from each strip's first row: pad the
     // plane with zero rows to the last strip's end, when that still fits
-    const int nstrip = (g.P + kSH - 1) / kSH;
-    a.strip = g.R == 3 && g.S == 3 && g.sh == 1 && g.sw == 1 && g.dh == 1 && g.dw == 1 && !epi.pool;
+    // (with the pool: 2 kPS + 2 rows from each pooled strip's first row)
+    const int nstrip = epi.pool ? (g.P / 2 + kPS - 1) / kPS : (g.P + kSH - 1) / kSH;
+    const int strip_rows = epi.pool ? 2 * kPS : kSH;
+    a.strip = g.R == 3 && g.S == 3 && g.sh == 1 && g.sw == 1 && g.dh == 1 && g.dw == 1;
     if (a.strip) {
-        const int hs = plane_of(std::max(a.Hp, nstrip * kSH + 2));
+        const int hs = plane_of(std::max(a.Hp, nstrip * strip_rows + 2));
         if (bytes_of(hs) <= kDwLdsBytes) a.Hp = hs;
         else a.strip = 0;
     }
@@ -263,7 +314,7 @@ bool dw_imp_plan(const Geom& g, const Epi& epi, int n_images, DwImpArgs& a, size
         // every thread the same number of strips where that costs less
         // time per plane: 20 planes of 28 strips take 3 passes of 256
         // threads (2.2 on average), 18 planes take 2
-        const int spp = g.Q * nstrip;
+        const int spp = (epi.pool ? g.Q / 2 : g.Q) * nstrip;
         const int it = (per * spp + kDThreads - 1) / kDThreads;
         const int per2 = (it - 1) * kDThreads / spp;
         if (it > 1 && per2 >= 1 && (int64_t)(it - 1) * per < (int64_t)it * per2) per = per2;
@@ -284,7 +335,7 @@ bool dw_imp_plan(const Geom& g, const Epi& epi, int n_images, DwImpArgs& a, size
     a.fdW = make_fastdiv((uint32_t)g.W);
     a.fdPQo = make_fastdiv((uint32_t)(a.Po * a.Qo));
     a.fdQo = make_fastdiv((uint32_t)a.Qo);
-    a.fdStrip = make_fastdiv((uint32_t)(a.Qo * ((g.P + kSH - 1) / kSH)));
+    a.fdStrip = make_fastdiv((uint32_t)(a.Qo * nstrip));
     lds = (size_t)per * plane_bytes;
     grid = (planes + per - 1) / per;
     return true;
