@@ -15,8 +15,9 @@ Usage, from the repository root:
 
 Each variant is a full copy of the library with the switch set; --run
 checks every variant's output on the 128x64x56x56 fp16 layer against the
-CPU oracle at sampled points before timing it (HIP events, 50 calls after
-10 warm-ups), each in its own process, and prints one JSON line.
+CPU oracle at sampled points before timing it (five runs of 50 calls back
+to back after 10 warm-ups, HIP events around each run; the median run),
+each in its own process, and prints one JSON line.
 """
 from __future__ import annotations
 
@@ -117,13 +118,18 @@ def time_variant(name: str) -> dict:
     for _ in range(10):
         call()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
-    for a, b in ev:
+    # events only around runs of calls: one recorded between calls costs
+    # GPU time of its own
+    ms = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        call()
+        for _ in range(50):
+            call()
         b.record()
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in ev)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b) / 50)
+    ms.sort()
     flops = 2 * L.N * L.K * L.C * L.R * L.S * 56 * 56
     med = ms[len(ms) // 2]
     return {"variant": name, "median_us": round(med * 1e3, 2), "best_us": round(ms[0] * 1e3, 2),

@@ -297,8 +297,14 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_implicit_kernel(
                                               16 * (pos_base[jj] + tid)) = v;
                 } else {
                     const uint32_t dst = __builtin_amdgcn_readfirstlane(dst0 + 16u * (uint32_t)pos_base[jj]);
+                    // the row's address is uniform; readfirstlane keeps it in
+                    // scalar registers, which the instruction's operand needs
+                    // whatever the register allocation around it
+                    const uint64_t sp = reinterpret_cast<uint64_t>(src);
+                    const uint64_t su = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(sp >> 32)) << 32) |
+                                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sp);
                     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
-                                 :: "v"(src_off[jj]), "s"(dst), "s"(src) : "memory");
+                                 :: "v"(src_off[jj]), "s"(dst), "s"(su) : "memory");
                 }
             }
         }
