@@ -490,6 +490,70 @@ def measure_layer(L: workloads.Layer, steps: int, warmup: int, epilogue: str = "
     return res, step
 
 
+def ablation_report(runs: int = 5, calls: int = 50) -> dict:
+    """The ablation variants (copies of the library with one kernel's
+    optimizations switched off, built by cnn_convolution_im2win_amd.build)
+    timed on the 128x64x56x56 fp16 layer through their C ABI: 10 warm-up
+    calls, then `runs` runs of `calls` calls back to back, HIP events around
+    each run; median, best and spread of the per-call means.  Parity of every
+    variant is checked by tests/test_gpu_ablation.py, not here."""
+    import torch
+    from cnn_convolution_im2win_amd import _lib, build
+    L = workloads.LAYERS["resnet_3x3_fp16"]
+    x, w, _ = workloads.make_inputs(L)
+    xd = torch.from_numpy(x).to("cuda")
+    wd = torch.from_numpy(w).to("cuda")
+    desc = _lib.ConvDesc(L.N, L.C, L.H, L.W, L.K, L.R, L.S, 1, 1, 1, 1, 1, 1, 1)
+    y = torch.empty((L.N, L.K, L.H, L.W), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.Stream()
+    out = {}
+    for name, (_, _, what) in build.VARIANTS.items():
+        lib = _lib.open_library(build.variant_path(name))
+        nb = ctypes.c_size_t()
+        implicit = name.startswith("implicit")
+        flags = _lib.CIW_FLAG_IMPLICIT if implicit else 0
+        if implicit:
+            st = lib.conv2d_implicit_workspace_bytes(ctypes.byref(desc), 1, 1, flags, ctypes.byref(nb))
+        else:
+            st = lib.conv2d_workspace_bytes(ctypes.byref(desc), 1, L.N, ctypes.byref(nb))
+        if st != 0:
+            raise RuntimeError(f"{name}: workspace query status {st}")
+        ws = torch.empty(max(nb.value, 16), dtype=torch.uint8, device="cuda")
+        args = (ctypes.byref(desc), 1, 1, xd.data_ptr(), wd.data_ptr(), None, y.data_ptr(),
+                ws.data_ptr(), nb.value, flags, stream.cuda_stream)
+
+        def call():
+            st = lib.conv2d_fwd(*args)
+            if st != 0:
+                raise RuntimeError(f"{name}: conv2d_fwd status {st}")
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(runs):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(calls):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1) / calls)
+        ms.sort()
+        med = ms[len(ms) // 2]
+        out[name] = {"what": what, "median_us": round(med * 1e3, 2), "best_us": round(ms[0] * 1e3, 2),
+                     "worst_us": round(ms[-1] * 1e3, 2)}
+        print(f"# ablation {name}: {json.dumps(out[name])}", file=sys.stderr, flush=True)
+    for name, r in out.items():
+        base = out[name.split("_", 1)[0] + "_baseline"]
+        r["vs_baseline"] = round(r["median_us"] / base["median_us"], 3)
+        # a difference counts only beyond both runs' spreads (worst - best)
+        noise = (r["worst_us"] - r["best_us"]) + (base["worst_us"] - base["best_us"])
+        r["beyond_noise"] = abs(r["median_us"] - base["median_us"]) > noise
+    return {"layer": describe(L), "scope": "one conv2d_fwd call (materialised: repack + contraction "
+            "+ filter re-layout; in-LDS: filter re-layout + contraction)", "runs": runs,
+            "calls_per_run": calls, "variants": out}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -505,6 +569,8 @@ def main():
                     help="with --epilogue, skip the unfused comparison (e.g. under a profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ablation", action="store_true",
+                    help="time the ablation variant libraries instead (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -521,6 +587,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+
+    if args.ablation:
+        print(json.dumps(ablation_report()), flush=True)
+        return
 
     L = workloads.LAYERS[args.workload]
     print(f"# measuring {describe(L)} (epilogue {args.epilogue}): {args.warmup} warmup + "

@@ -66,16 +66,15 @@ class Im2winError(RuntimeError):
 _lib = None
 
 
-def load():
-    """Open the HIP library (once).  Raises if it has not been built."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
+def open_library(path: str):
+    """Open a build of the library at `path` with the ctypes signatures of
+    the C ABI set (the package's own library, or an ablation variant built
+    by ``build.build_variants``)."""
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m cnn_convolution_im2win_amd.build` "
+            f"{path} is missing: build it with `python -m cnn_convolution_im2win_amd.build` "
             "(or __graft_entry__.build()); there is no CPU fallback")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     D = ctypes.POINTER(ConvDesc)
     i32, u32, i64 = ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64
@@ -98,8 +97,15 @@ def load():
         fn.restype = ctypes.c_int
     lib.conv_im2win_status_string.argtypes = [ctypes.c_int]
     lib.conv_im2win_status_string.restype = ctypes.c_char_p
-    _lib = lib
     return lib
+
+
+def load():
+    """Open the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        _lib = open_library(LIB_PATH)
+    return _lib
 
 
 def status_string(status: int) -> str:

@@ -3,6 +3,14 @@
 Usage: ``python -m cnn_convolution_im2win_amd.build`` (or ``build()``).
 Every source compiles to an object in ``_build/`` in parallel, then the
 objects link into ``cnn_convolution_im2win_amd/libconv_im2win.so``.
+
+``build_variants()`` also links the ablation variants: copies of the library
+in which one kernel is compiled with some of its optimizations switched off
+(the im2win paper, §IV-E, ablates its tensor-core kernel the same way).
+Each lands in ``variants/<name>/libconv_im2win.so`` next to this file; only
+the switched kernel's sources are recompiled, the other objects are the main
+build's (every kernel lives in an anonymous namespace, so objects built with
+different switches link together).
 """
 from __future__ import annotations
 
@@ -47,6 +55,67 @@ def _compile(src: str) -> str:
     return obj
 
 
+# name -> (compile definitions, sources recompiled with them, what it measures)
+VARIANTS = {
+    # the materialised-window row kernel (conv_mfma_rows_kernel), fp16 inputs
+    "rows_baseline": ([], ["conv_mfma.hip", "conv_mfma_f16.hip"],
+                      "row kernel as in the library"),
+    # the window-row buffers of the in-LDS kernel (conv_mfma_implicit_kernel)
+    "implicit_baseline": ([], ["conv_implicit.hip", "conv_implicit_f16.hip"],
+                          "in-LDS window kernel as in the library"),
+    "implicit_no_double": (["-DCIW_ABLATE_NO_DOUBLE=1"], ["conv_implicit.hip", "conv_implicit_f16.hip"],
+                           "input row copied at the step that needs it, then waited for"),
+    "implicit_no_async": (["-DCIW_ABLATE_NO_ASYNC=1"], ["conv_implicit.hip", "conv_implicit_f16.hip"],
+                          "rows copied global -> registers -> LDS"),
+    "implicit_no_xcd": (["-DCIW_ABLATE_NO_XCD=1"], ["conv_implicit.hip", "conv_implicit_f16.hip"],
+                        "bands in dispatch order"),
+}
+VARIANT_DIR = os.path.join(PKG, "variants")
+
+
+def variant_path(name: str) -> str:
+    return os.path.join(VARIANT_DIR, name, "libconv_im2win.so")
+
+
+def build_variants(verbose: bool = False) -> None:
+    """Link every ablation variant (needs the main build's objects)."""
+    main_objs = {s: os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES}
+    missing = [o for o in main_objs.values() if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"build the library first (missing {missing[0]})")
+    jobs = []
+    for name, (defs, srcs, _) in VARIANTS.items():
+        for src in srcs:
+            jobs.append((name, defs, src))
+
+    def one(job):
+        name, defs, src = job
+        bdir = os.path.join(BUILD_DIR, "variants", name)
+        os.makedirs(bdir, exist_ok=True)
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC] + CFLAGS + defs + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"{name}: hipcc failed for {src}:\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        list(ex.map(one, jobs))
+    for name, (defs, srcs, _) in VARIANTS.items():
+        bdir = os.path.join(BUILD_DIR, "variants", name)
+        objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") if s in srcs else main_objs[s]
+                for s in SOURCES]
+        out = variant_path(name)
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out + ".tmp"] + objs
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"{name}: link failed:\n{r.stderr}")
+        os.replace(out + ".tmp", out)
+        if verbose:
+            print(f"built {out}")
+
+
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link the shared library; returns its path."""
     if not shutil.which(HIPCC) and not os.path.exists(HIPCC):
@@ -67,3 +136,5 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    if "--variants" in sys.argv:
+        build_variants(verbose=True)

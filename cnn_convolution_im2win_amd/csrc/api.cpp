@@ -6,6 +6,7 @@
 // which kernels were allowed more than 64 KB of dynamic LDS (below).
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -29,9 +30,32 @@ int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d) {
 
 bool dtype_ok(int t) { return t == CIW_F32 || t == CIW_F16 || t == CIW_BF16; }
 
+// Product of non-negative extents, false if it reaches 2^62 (then the
+// tensor is far past int32 indexing whatever the other factors are).  Every
+// partial product is checked, so no multiplication can overflow int64.
+bool mul_ok(std::initializer_list<int64_t> factors, int64_t* out) {
+    const int64_t cap = (int64_t)1 << 62;
+    int64_t p = 1;
+    for (int64_t f : factors) {
+        if (f < 0) return false;
+        if (f != 0 && p > cap / f) return false;
+        p *= f;
+    }
+    *out = p;
+    return true;
+}
+
+// True when the product of the extents is below 2^31 (int32 indexing).
+bool below_2_31(std::initializer_list<int64_t> factors) {
+    int64_t p = 0;
+    return mul_ok(factors, &p) && p < kMaxElems;
+}
+
 // a1: validate a descriptor and resolve the geometry.  Problems whose
 // tensors exceed int32 indexing, or whose dilated filter is taller than the
 // repack's LDS tile can hold (more than 4096 input rows), are unsupported.
+// Extents come from the caller and may be as large as 2^31 - 1 each, so
+// every product below is formed with overflow checks.
 ciw_status resolve(const ciw_conv_desc* d, ciw_dtype dt, Geom* g) {
     if (!d || !dtype_ok(dt)) return CIW_ERR_INVALID_ARG;
     if (d->N < 0 || d->C < 1 || d->H < 1 || d->W < 1 || d->K < 1 || d->R < 1 || d->S < 1)
@@ -49,17 +73,20 @@ ciw_status resolve(const ciw_conv_desc* d, ciw_dtype dt, Geom* g) {
     if (P < 1 || Q < 1) return CIW_ERR_INVALID_ARG;
     if ((int64_t)d->dil_h * (d->R - 1) + 1 > 4096) return CIW_ERR_UNSUPPORTED;
     const int64_t eb = elem_bytes(dt);
+    // (Q - 1) * stride_w <= W + 2 pad_w < 2^33 and dil_w * (S - 1) < 2^62:
+    // no overflow here
     const int64_t wwin = (Q - 1) * d->stride_w + (int64_t)d->dil_w * (d->S - 1) + 1;
-    const int64_t lenA = wwin * d->R;
+    if (wwin >= kMaxElems) return CIW_ERR_UNSUPPORTED;
+    // every tensor the kernels index must stay below 2^31 elements
+    const int64_t N = d->N > 0 ? d->N : 1;
+    if (!below_2_31({N, d->C, d->H, d->W}) || !below_2_31({d->K, d->C / d->groups, d->R, d->S}) ||
+        !below_2_31({N, d->K, P, Q}) || !below_2_31({N, wwin, d->R, d->C}))
+        return CIW_ERR_UNSUPPORTED;
+    const int64_t lenA = wwin * d->R;   // < 2^31 by the check above
     const int64_t lenB = lenA * d->C;
     const int64_t pitchA = round_up(lenA, 16 / eb);
     const int64_t pitchB = round_up(lenB, 16 / eb);
-    // every tensor the kernels index must stay below 2^31 elements
-    const int64_t N = d->N > 0 ? d->N : 1;
-    if (N * d->C * d->H * d->W >= kMaxElems || d->K * (d->C / d->groups) * d->R * d->S >= kMaxElems ||
-        N * d->K * P * Q >= kMaxElems || N * d->C * P * pitchA >= kMaxElems ||
-        N * P * pitchB >= kMaxElems || wwin >= kMaxElems)
-        return CIW_ERR_UNSUPPORTED;
+    if (!below_2_31({N, d->C, P, pitchA}) || !below_2_31({N, P, pitchB})) return CIW_ERR_UNSUPPORTED;
     g->N = (int)d->N; g->C = (int)d->C; g->H = (int)d->H; g->W = (int)d->W;
     g->K = (int)d->K; g->R = (int)d->R; g->S = (int)d->S; g->P = (int)P; g->Q = (int)Q;
     g->sh = d->stride_h; g->sw = d->stride_w; g->ph = d->pad_h; g->pw = d->pad_w;
@@ -275,7 +302,9 @@ ciw_status conv_im2win_window_bytes(const ciw_conv_desc* desc, ciw_dtype dtype,
     Geom g;
     ciw_status s = resolve(desc, dtype, &g);
     if (s != CIW_OK) return s;
-    *bytes = (size_t)(window_bytes_per_image(g, layout) * n_images);
+    int64_t total = 0;
+    if (!mul_ok({window_bytes_per_image(g, layout), n_images}, &total)) return CIW_ERR_UNSUPPORTED;
+    *bytes = (size_t)total;
     return CIW_OK;
 }
 
@@ -300,6 +329,9 @@ ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
     if (s != CIW_OK) return s;
     bool dw = g.G > 1;
     if (dw && !(g.G == g.C && g.K == g.C)) return CIW_ERR_UNSUPPORTED;
+    // a chunk never holds more than the batch (a larger n_images describes
+    // the same single chunk); this also keeps the products below in range
+    if (n_images > g.N && g.N > 0) n_images = g.N;
     *bytes = (size_t)chunk_workspace(g, path_of(g, in_dtype, dw), n_images);
     return CIW_OK;
 }

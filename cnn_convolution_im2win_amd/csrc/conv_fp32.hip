@@ -15,8 +15,7 @@
 // operand; the lane's own R*S filter taps sit in vector registers.  Per
 // input channel a lane therefore issues TN*R*S multiply-adds against R*S
 // vector loads -- the reuse of overlapping windows that the paper credits
-// to the cache ("elements loaded in a previous window remain in cache",
-// §III-C) happens here in registers.
+// to the cache (§III-C) happens here in registers.
 //
 // The channel sum is split two ways so that small layers (one 13x13 image)
 // still fill 256 compute units: the four waves of a workgroup take

@@ -360,7 +360,10 @@ hipError_t launch_conv_fp32_mfma(const Geom& g, const float* xw, const float* w,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || pl.a.splits == 1) return e;
     const int64_t per_split = (int64_t)n_images * g.K * g.P * g.Q;
-    const bool vec = per_split % 4 == 0;
+    // float4 form: every slice starts 16-byte aligned (per_split % 4 == 0,
+    // partials is) and so must y, which is offset by the chunk's first
+    // image and need not be
+    const bool vec = per_split % 4 == 0 && ((uintptr_t)y & 15u) == 0;
     const int64_t threads = vec ? per_split / 4 : per_split;
     hipLaunchKernelGGL(vec ? split_reduce_nkp_kernel<true> : split_reduce_nkp_kernel<false>,
                        dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0,

@@ -19,8 +19,8 @@
 //     channels at column w*stride_w + q*dil_w of buffer h + r*dil_h: the
 //     window row of the paper with its (column, filter row) pairs kept in
 //     R separate buffers.  One buffer serves the R output rows that read it,
-//     so each input element crosses HBM once per band ("elements loaded in
-//     a previous window remain in cache", §III-C);
+//     so each input element crosses HBM once per band (the paper's point
+//     that overlapping windows reuse inputs already in cache, §III-C);
 //   - the reduction is ordered t = (r*S + q)*C + c, a reordering of the
 //     paper's window order, so one 16-entry MFMA step is 16 channels of one
 //     tap and a lane's 8 entries are one 16-byte LDS read.
@@ -30,8 +30,8 @@
 // accumulation, bias seeding the accumulators, one rounding at the store.
 //
 // Ablation switches (the im2win paper §IV-E ablates double buffering,
-// asynchronous copies and its zig-zag order; cnn_convolution_im2win_amd/
-// ablation.py builds and times each), all 0 in the library:
+// asynchronous copies and its zig-zag order; build.py builds a copy of the
+// library per switch), all 0 in the library:
 //   CIW_ABLATE_NO_DOUBLE: input row u + 1 is copied at the step that needs
 //     it and waited for at once (no copy ahead);
 //   CIW_ABLATE_NO_ASYNC: rows go global memory -> registers -> LDS instead

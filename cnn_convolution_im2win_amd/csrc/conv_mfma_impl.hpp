@@ -10,8 +10,8 @@
 // (n, h, w) is, for each filter column q, the R*C contiguous elements at
 // column w*stride_w + q*dil_w of row (n, h); with dil_w = 1 the whole window
 // (S*R*C elements) is one contiguous run.  The reduction index is
-// t = (q*R + r)*C + c and the filter operand is F[k][c][r][q] ("height before
-// width", §III-C).  Products are exact in fp32 and accumulate in fp32
+// t = (q*R + r)*C + c and the filter operand is F[k][c][r][q] (the filter
+// height index varies before the width, §III-C).  Products are exact in fp32 and accumulate in fp32
 // (§III-F); the bias is added in fp32 and the result rounded once.
 #pragma once
 
@@ -176,8 +176,8 @@ __global__ __launch_bounds__(kThreads) void conv_mfma_generic_kernel(
 //     multiplied (load/compute overlap, §III-D/§III-E);
 //   - the window of pixel w is the run of LDS chunks starting at w*D, D =
 //     stride_w*R*C, so consecutive pixels read overlapping runs and each
-//     window element crosses HBM once per output row ("elements loaded in
-//     a previous window remain in cache", §III-C);
+//     window element crosses HBM once per output row (overlapping windows
+//     reuse inputs already in cache, the im2win paper §III-C);
 //   - the window fragment is the MFMA's first operand, so a lane ends up
 //     holding 16 pixels of one output channel, four of them adjacent; they
 //     go through an LDS tile so each output row leaves with whole-vector

@@ -8,8 +8,9 @@
  *   1. the input is repacked once into a window tensor in which the inputs
  *      of every output row sit in one contiguous row (§III-B, §III-C);
  *   2. a windowed dot product contracts each output's contiguous window with
- *      the filter (§III-C), on the vector ALUs in fp32 and on the matrix
- *      cores in fp16/bf16 with fp32 accumulation (§III-D, §III-F).
+ *      the filter (§III-C), in fp32 on the vector ALUs or the fp32 matrix
+ *      cores and in fp16/bf16 on the matrix cores with fp32 accumulation
+ *      (§III-D, §III-F).
  * The problem statement (N, C, H, W, K, R, S, stride, padding, dilation,
  * bias; zero padding; cross-correlation; bias added after the sum) is the one
  * of the OpenCL-Benchmarks page's direct "conv2d" kernel ("Setting: normal").
@@ -68,8 +69,8 @@ typedef enum { CIW_F32 = 0, CIW_F16 = 1, CIW_BF16 = 2 } ciw_dtype;
  * dil_w*(S-1) + 1.  Rows are padded with zeros to a pitch that is a multiple
  * of 16 bytes.  The window of output (h, w) is, for each filter column q, the
  * R (CHW) or R*C (HWC) contiguous elements at column w*stride_w + q*dil_w;
- * with dil_w = 1 the whole window is one contiguous run ("height before
- * width", §III-C). */
+ * with dil_w = 1 the whole window is one contiguous run (the filter height
+ * index varies before the width, §III-C). */
 typedef enum { CIW_WIN_CHW = 0, CIW_WIN_HWC = 1 } ciw_win_layout;
 
 /* Convolution descriptor.  groups must divide C and K; the library runs
@@ -128,23 +129,35 @@ typedef struct {
 #define CIW_FLAG_FP32_VALU    0x80u
 
 /* Output extent: P = floor((H + 2 pad_h - dil_h (R-1) - 1) / stride_h) + 1,
- * Q likewise.  Returns CIW_ERR_INVALID_ARG if the descriptor is invalid or
- * the window does not fit the padded input. */
+ * Q likewise.  The OpenCL-Benchmarks page's conv2d kernel takes out_h and
+ * out_w as arguments without saying how they are formed; its layer table
+ * ("Convolution Ops Analysis": 13x13 in, 3x3, stride 1, padding 1, 13x13
+ * out) fits this floor formula, the reading taken here.  Returns
+ * CIW_ERR_INVALID_ARG if the descriptor is invalid or the window does not
+ * fit the padded input, CIW_ERR_UNSUPPORTED if a tensor of the layer has
+ * 2^31 or more elements. */
 ciw_status conv_im2win_output_dims(const ciw_conv_desc* desc, int64_t* P, int64_t* Q);
 
 /* Extent of the output conv2d_fwd / conv2d_dw_fwd write with these flags:
- * (P, Q) as above, or (P/2, Q/2) with CIW_FLAG_MAXPOOL2 (CIW_ERR_INVALID_ARG
- * if P or Q < 2).  Other flag bits are ignored here. */
+ * (P, Q) as above, or (P/2, Q/2) with CIW_FLAG_MAXPOOL2, the max over each
+ * 2x2 region ("CS149 L9", slide 23; the pool fused after the conv as in
+ * "Fusion: keep intermediates out of memory"); CIW_ERR_INVALID_ARG if P or
+ * Q < 2.  Other flag bits are ignored here. */
 ciw_status conv2d_output_dims(const ciw_conv_desc* desc, uint32_t flags, int64_t* P, int64_t* Q);
 
-/* Geometry of the window tensor of ONE image: number of rows (C*P for CHW,
+/* Geometry of the window tensor of ONE image (the im2win paper, §III-B:
+ * one row per output row holding the input columns its windows cover;
+ * §III-D for the channel-innermost variant): number of rows (C*P for CHW,
  * P for HWC), elements per row before padding, and the row pitch in
  * elements.  Any output pointer may be NULL. */
 ciw_status conv_im2win_window_geometry(const ciw_conv_desc* desc, ciw_dtype dtype,
                                        ciw_win_layout layout, int64_t* rows_per_image,
                                        int64_t* row_elems, int64_t* row_pitch);
 
-/* Bytes of the window tensor of n_images images (pitch included). */
+/* Bytes of the window tensor of n_images images, pitch included: the
+ * memory cost of the repack that the im2win paper weighs against the
+ * im2col matrix (§III-B).  CIW_ERR_UNSUPPORTED if the size does not fit in
+ * 62 bits. */
 ciw_status conv_im2win_window_bytes(const ciw_conv_desc* desc, ciw_dtype dtype,
                                     ciw_win_layout layout, int64_t n_images, size_t* bytes);
 
@@ -157,8 +170,10 @@ ciw_status conv_im2win_transform(const ciw_conv_desc* desc, ciw_dtype dtype,
                                  void* stream);
 
 /* Workspace conv2d_fwd / conv2d_dw_fwd need to process n_images images per
- * chunk (the window tensor of the chunk plus any partial sums).  Passing
- * n_images = N gives the single-chunk (full-batch) size; the minimum usable
+ * chunk (the window tensor of the chunk plus any partial sums): the
+ * single-batch / mini-batch / full-batch processing strategies of the im2win
+ * paper (§IV-D1) are n_images = 1, 1 < n_images < N and n_images = N (a
+ * larger n_images gives the n_images = N size).  The minimum usable
  * workspace is the n_images = 1 size. */
 ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
                                   int64_t n_images, size_t* bytes);
@@ -180,9 +195,11 @@ ciw_status conv2d_implicit_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype 
 
 /* Dense forward convolution (groups == 1), im2win method: for each batch
  * chunk, the repack into `workspace` followed by the windowed contraction
- * (the im2win paper §III-C..§III-F).  fp32 uses the CHW window layout and
- * the vector ALUs; fp16/bf16 use the HWC layout and the matrix cores with
- * fp32 accumulation.  The chunk size is the largest number of images whose
+ * (the im2win paper §III-C..§III-F; the problem statement is that of the
+ * OpenCL-Benchmarks page's conv2d kernel).  fp32 uses the CHW window layout
+ * and the fp32 matrix cores or the vector ALUs (see CIW_FLAG_FP32_MFMA);
+ * fp16/bf16 use the HWC layout and the matrix cores with fp32
+ * accumulation.  The chunk size is the largest number of images whose
  * workspace (conv2d_workspace_bytes) fits in workspace_bytes, capped at N;
  * CIW_ERR_WORKSPACE if not even one image fits.  With
  * CIW_FLAG_WINDOW_READY the workspace must hold the full-batch window
@@ -194,16 +211,20 @@ ciw_status conv2d_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype o
                       void* workspace, size_t workspace_bytes, uint32_t flags,
                       void* stream);
 
-/* Depthwise forward convolution (groups == C == K, one filter per channel):
- * the CHW window tensor, then a per-channel windowed dot product
- * (bandwidth-bound).  Same arguments, workspace and flag rules as
+/* Depthwise forward convolution (groups == C == K, one filter per channel;
+ * "Diagonalwise Refactorization: An Efficient Training Method for Depthwise
+ * Convolutions", abstract: each input channel is convolved with its own
+ * filter, which equals a dense convolution whose filter is zero off the
+ * channel diagonal): the CHW window tensor, then a per-channel windowed dot
+ * product (bandwidth-bound).  Same arguments, workspace and flag rules as
  * conv2d_fwd; w is [C][1][R][S]. */
 ciw_status conv2d_dw_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype out_dtype,
                          const void* x, const void* w, const void* bias, void* y,
                          void* workspace, size_t workspace_bytes, uint32_t flags,
                          void* stream);
 
-/* Static description of a status code (never NULL). */
+/* Static description of a status code (never NULL).  A convenience of
+ * this library: no passage of the pages defines error statuses. */
 const char* conv_im2win_status_string(ciw_status status);
 
 #ifdef __cplusplus

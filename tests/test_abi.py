@@ -215,6 +215,45 @@ def test_int32_overflow_is_unsupported():
     assert call_fwd(d) == _lib.CIW_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("fields", [
+    # 2^20 * 2^20 * 2^20 * 16 = 2^64: wraps to 0 in an unchecked int64 product
+    dict(N=1 << 20, C=1 << 20, H=1 << 20, W=16, K=1 << 20, R=1, S=1, pad_h=0, pad_w=0),
+    # 2^21 * 2^21 * 2^21 * 2^1 = 2^64 through the output tensor
+    dict(N=1 << 21, C=1, H=1 << 21, W=2, K=1 << 21, R=1, S=1, pad_h=0, pad_w=0),
+    # filter tensor K * C * R * S = 2^31 * ... past int64
+    dict(N=1, C=1 << 30, H=1, W=1, K=(1 << 31) - 1, R=1, S=1, pad_h=0, pad_w=0),
+    # window row length: Wwin * R * C with a huge dilation
+    dict(N=1, C=1 << 16, H=8, W=8, K=1, R=3, S=1 << 16, pad_h=1, pad_w=1 << 30, dil_w=1 << 14),
+    # largest legal extents in every field
+    dict(N=(1 << 31) - 1, C=(1 << 31) - 1, H=(1 << 31) - 1, W=(1 << 31) - 1, K=(1 << 31) - 1,
+         R=1, S=1, pad_h=0, pad_w=0),
+])
+def test_wrapping_descriptors_are_unsupported(fields):
+    """Extents whose products wrap a 64-bit integer must be rejected, not
+    accepted with a wrapped size (the host checks every partial product)."""
+    d = valid_desc(**fields)
+    assert call_fwd(d) == _lib.CIW_ERR_UNSUPPORTED
+    P, Q = ctypes.c_int64(), ctypes.c_int64()
+    assert lib().conv_im2win_output_dims(ctypes.byref(d), ctypes.byref(P), ctypes.byref(Q)) == \
+        _lib.CIW_ERR_UNSUPPORTED
+    out = ctypes.c_size_t()
+    for lay in (m.CIW_WIN_CHW, m.CIW_WIN_HWC):
+        assert lib().conv_im2win_window_bytes(ctypes.byref(d), 0, lay, 1, ctypes.byref(out)) == \
+            _lib.CIW_ERR_UNSUPPORTED
+    assert lib().conv2d_workspace_bytes(ctypes.byref(d), 0, 1, ctypes.byref(out)) == \
+        _lib.CIW_ERR_UNSUPPORTED
+
+
+def test_window_bytes_of_huge_image_counts_do_not_wrap():
+    d = valid_desc()
+    out = ctypes.c_size_t()
+    assert lib().conv_im2win_window_bytes(ctypes.byref(d), 0, 0, 1 << 62, ctypes.byref(out)) == \
+        _lib.CIW_ERR_UNSUPPORTED
+    # a workspace query for more images than the batch is the full-batch size
+    assert lib().conv2d_workspace_bytes(ctypes.byref(d), 0, 1 << 62, ctypes.byref(out)) == _lib.CIW_OK
+    assert out.value == m.conv2d_workspace_bytes(d, 0, d.N)
+
+
 def test_empty_batch_is_a_no_op():
     d = valid_desc(N=0)
     assert call_fwd(d, x=None, w=None, y=None, ws=None) == _lib.CIW_OK

@@ -58,7 +58,7 @@ def test_fp32_mfma_against_oracle(shape, relu):
     ref = oracle.conv2d(x.astype(np.float64), w.astype(np.float64), b.astype(np.float64),
                         L.stride, L.pad, L.dil, 1)
     if relu:
-        ref = np.maximum(ref, 0)
+        ref = oracle.relu_pool(ref, relu=True, pool=False)
     e = rel_err(got, ref)
     say(f"  rel err {e:.3e}")
     assert got.shape == ref.shape and np.all(np.isfinite(got))
@@ -117,4 +117,25 @@ def test_fp32_mfma_batch_chunks(imgs):
     ref = oracle.conv2d(x.astype(np.float64), w.astype(np.float64), b.astype(np.float64), 1, 1, 1, 1)
     e = rel_err(to_host_f64(y), ref)
     say(f"fp32 chunks of {imgs}: rel err {e:.3e}")
+    assert e <= TOL["f32"]
+
+
+@pytest.mark.parametrize("forced", [ciw.CIW_FLAG_FP32_MFMA, ciw.CIW_FLAG_FP32_VALU])
+def test_fp32_uneven_chunks_odd_plane(forced):
+    """K * P * Q odd and a workspace for 5 of 9 images: the second chunk's
+    output starts at a byte offset that is not a multiple of 16 (4 images x
+    3 x 13 x 13 floats), which the slice reduction must handle (no 16-byte
+    stores to it)."""
+    L = workloads.Layer("f32odd", N=9, C=64, H=13, W=13, K=3, R=3, S=3, stride=(1, 1),
+                        pad=(1, 1), x_dist=("uniform", -1.0, 1.0), seed=23)
+    x, w, b = workloads.make_inputs(L)
+    desc = ciw.make_desc(L.x_shape, L.w_shape, L.stride, L.pad, L.dil, 1)
+    ws = torch.empty(ciw.conv2d_workspace_bytes(desc, ciw.CIW_F32, 5), dtype=torch.uint8,
+                     device="cuda")
+    y = ciw.conv2d(to_dev(x, "f32"), to_dev(w, "f32"), to_dev(b, "f32"), 1, 1, workspace=ws,
+                   flags=forced)
+    torch.cuda.synchronize()
+    ref = oracle.conv2d(x.astype(np.float64), w.astype(np.float64), b.astype(np.float64), 1, 1, 1, 1)
+    e = rel_err(to_host_f64(y), ref)
+    say(f"fp32 odd plane, chunks of 5 ({forced:#x}): rel err {e:.3e}")
     assert e <= TOL["f32"]

@@ -121,7 +121,8 @@ def test_relu_and_no_bias(dtype):
                         b_dist=None, seed=5)
     x, w, _ = workloads.make_inputs(L)
     got = to_host_f64(run(L, x, w, None, flags=IMP | ciw.CIW_FLAG_RELU))
-    ref = np.maximum(oracle.conv2d(f64(x, dtype), f64(w, dtype), None, L.stride, L.pad, L.dil, 1), 0)
+    ref = oracle.relu_pool(oracle.conv2d(f64(x, dtype), f64(w, dtype), None, L.stride, L.pad,
+                                         L.dil, 1), relu=True, pool=False)
     check(got, ref, f"relu {dtype}")
     assert np.all(got >= 0)
 
@@ -171,7 +172,9 @@ def test_resnet_layer_relu_pool_full_size():
     idx = sample_indices(got_all.shape, 1000, rng)
     quad = np.concatenate([idx * [1, 1, 2, 2] + [0, 0, dy, dx] for dy in (0, 1) for dx in (0, 1)])
     pts = oracle.conv2d_points(f64(x, "f16"), f64(w, "f16"), None, quad, L.stride, L.pad, L.dil, 1)
-    ref = np.maximum(pts.reshape(4, -1).max(axis=0), 0)
+    # each sampled output's four convolution outputs as one 2x2 plane, through O5
+    quads = pts.reshape(2, 2, -1).transpose(2, 0, 1)[None]
+    ref = oracle.relu_pool(quads, relu=True, pool=True).reshape(-1)
     check(got_all[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]], ref, "sampled")
 
 

@@ -248,7 +248,7 @@ def test_points_match_full():
 def test_repack_worked_example_chw():
     # 4x4 ramp, 3x3 filter, stride 1, no padding: the window tensor row of
     # output row h holds input columns 0..3 in order, each as the 3 values of
-    # rows h..h+2 ("height before width").  The window of output (0,0) is the
+    # rows h..h+2 (filter height index before width).  The window of output (0,0) is the
     # first 9 entries: columns 0..2 of rows 0..2.
     xw = oracle.im2win(ramp16(), 3, 3)
     assert xw.shape == (2, 12)              # W_win = 4 columns * 3 rows, pitch 12 (fp64: even)
