@@ -19,6 +19,7 @@ from typing import Optional, Sequence, Tuple, Union
 
 from . import _lib
 from ._lib import (CIW_BF16, CIW_F16, CIW_F32, CIW_FLAG_FP32_MFMA, CIW_FLAG_FP32_VALU,
+                   CIW_NOALLOC_SCRATCH_BYTES,
                    CIW_FLAG_GENERIC,
                    CIW_FLAG_IMPLICIT, CIW_FLAG_MAXPOOL2,
                    CIW_FLAG_NO_SPLIT, CIW_FLAG_RELU, CIW_FLAG_WINDOW_READY, CIW_WIN_CHW,
@@ -27,13 +28,14 @@ from ._lib import (CIW_BF16, CIW_F16, CIW_F32, CIW_FLAG_FP32_MFMA, CIW_FLAG_FP32
 IntPair = Union[int, Sequence[int]]
 
 __all__ = [
-    "conv2d", "conv2d_fwd", "conv2d_dw_fwd", "conv_im2win_transform",
+    "conv2d", "conv2d_fwd", "conv2d_fwd_noalloc", "conv2d_dw_fwd", "conv_im2win_transform",
     "conv_im2win_output_dims", "conv2d_output_dims", "conv_im2win_window_geometry",
     "conv_im2win_window_bytes",
     "conv2d_workspace_bytes", "conv2d_implicit_workspace_bytes", "make_desc", "Im2winError", "status_string", "LIB_PATH",
     "CIW_F32", "CIW_F16", "CIW_BF16", "CIW_WIN_CHW", "CIW_WIN_HWC",
     "CIW_FLAG_WINDOW_READY", "CIW_FLAG_NO_SPLIT", "CIW_FLAG_GENERIC", "CIW_FLAG_RELU",
     "CIW_FLAG_MAXPOOL2", "CIW_FLAG_IMPLICIT", "CIW_FLAG_FP32_MFMA", "CIW_FLAG_FP32_VALU",
+    "CIW_NOALLOC_SCRATCH_BYTES",
 ]
 
 
@@ -192,6 +194,22 @@ def conv2d_fwd(x, w, bias, y, workspace, stride: IntPair = 1, padding: IntPair =
     x may be None with CIW_FLAG_WINDOW_READY (then pass x_shape)."""
     return _conv_call("conv2d_fwd", x, w, bias, y, workspace, stride, padding, dilation, 1,
                       flags, stream, x_shape)
+
+
+def conv2d_fwd_noalloc(x, w, bias, y, stride: IntPair = 1, padding: IntPair = 0,
+                       dilation: IntPair = 1, flags: int = 0, stream=None):
+    """Dense (groups = 1) im2win convolution into the preallocated y with no
+    workspace argument: the library's own device array
+    (CIW_NOALLOC_SCRATCH_BYTES per GPU) serves as the workspace, so nothing
+    is allocated on this path.  Calls that overlap on one GPU race on it."""
+    desc = make_desc(x.shape, w.shape, stride, padding, dilation, 1)
+    _need_device(x, w, bias, y)
+    _check_shapes(desc, x, w, bias, y, flags)
+    st = _lib.load().conv2d_fwd_noalloc(
+        ctypes.byref(desc), _dtype_code(w.dtype), _dtype_code(y.dtype), _ptr(x), _ptr(w),
+        _ptr(bias), _ptr(y), int(flags), _stream(stream))
+    _lib.check(st, "conv2d_fwd_noalloc")
+    return y
 
 
 def conv2d_dw_fwd(x, w, bias, y, workspace, stride: IntPair = 1, padding: IntPair = 0,

@@ -39,9 +39,13 @@ ENTRY_POINTS = (
     "conv2d_workspace_bytes",
     "conv2d_implicit_workspace_bytes",
     "conv2d_fwd",
+    "conv2d_fwd_noalloc",
     "conv2d_dw_fwd",
     "conv_im2win_status_string",
 )
+
+# bytes of the device array conv2d_fwd_noalloc uses as its workspace
+CIW_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class ConvDesc(ctypes.Structure):
@@ -89,6 +93,7 @@ def open_library(path: str):
         "conv2d_workspace_bytes": [D, i32, i64, psz],
         "conv2d_implicit_workspace_bytes": [D, i32, i32, u32, psz],
         "conv2d_fwd": [D, i32, i32, P, P, P, P, P, ctypes.c_size_t, u32, P],
+        "conv2d_fwd_noalloc": [D, i32, i32, P, P, P, P, u32, P],
         "conv2d_dw_fwd": [D, i32, i32, P, P, P, P, P, ctypes.c_size_t, u32, P],
     }
     for name, args in sig.items():

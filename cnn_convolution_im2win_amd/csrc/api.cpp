@@ -2,8 +2,9 @@
 // and workspace arithmetic, batch chunking and kernel dispatch.
 //
 // Every check runs before the first launch, so an error status means nothing
-// was enqueued.  The library's only state between calls is the record of
-// which kernels were allowed more than 64 KB of dynamic LDS (below).
+// was enqueued.  State kept between calls: the record of which kernels were
+// allowed more than 64 KB of dynamic LDS (below), and the per-device
+// addresses of the allocation-free entry point's workspace array.
 #include <cstdint>
 #include <cstring>
 #include <initializer_list>
@@ -128,9 +129,50 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 ciw_status from_hip(hipError_t e) { return e == hipSuccess ? CIW_OK : CIW_ERR_HIP; }
 
+// ---- the allocation-free entry point's workspace.
+// A file-scope device array: each GPU the library runs on holds its own copy
+// (CIW_NOALLOC_SCRATCH_BYTES) from the first use until the process ends.  In
+// host code the name `scratch` is only a stand-in for the symbol, never a
+// device address: the address of a device's copy comes from
+// hipGetSymbolAddress, looked up once per device with that device current,
+// and only that pointer reaches kernels.  Every conv2d_fwd_noalloc call on
+// a GPU uses the same array, so calls that overlap on one GPU (other
+// streams, other threads) race on it.  Nothing in it needs clearing between
+// calls: each call's repack writes every byte of the window tensor it
+// reads, and every other workspace region a kernel reads is fully written
+// earlier in the same call.
+static __device__ __align__(256) unsigned char scratch[CIW_NOALLOC_SCRATCH_BYTES];
+
+// The current device's copy of `scratch` (CIW_ERR_HIP if the runtime cannot
+// give its address).
+ciw_status scratch_of_current_device(void** out) {
+    static std::mutex mu;
+    static std::map<int, void*> ptrs;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CIW_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = ptrs.find(dev);
+    if (it == ptrs.end()) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) return CIW_ERR_HIP;
+        it = ptrs.emplace(dev, p).first;
+    }
+    *out = it->second;
+    return CIW_OK;
+}
+
+// noalloc: the workspace is this device's copy of `scratch` (ws and
+// ws_bytes are ignored), fetched after every check, before the first launch.
 ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, const void* x,
                     const void* w, const void* bias, void* y, void* ws, size_t ws_bytes,
-                    uint32_t flags, void* stream, bool depthwise) {
+                    uint32_t flags, void* stream, bool depthwise, bool noalloc = false) {
+    if (noalloc) {
+        // a window tensor prepared by the caller cannot be in the library's array
+        if (flags & CIW_FLAG_WINDOW_READY) return CIW_ERR_INVALID_ARG;
+        ws = nullptr;
+        ws_bytes = CIW_NOALLOC_SCRATCH_BYTES;
+    }
     Geom g;
     ciw_status s = resolve(desc, in, &g);
     if (s != CIW_OK) return s;
@@ -164,7 +206,7 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
     }
     if (g.N == 0) return CIW_OK;   // empty batch: nothing to do
     const bool ready = (flags & CIW_FLAG_WINDOW_READY) != 0;
-    if ((!ready && !x) || !w || !y || !ws) return CIW_ERR_INVALID_ARG;
+    if ((!ready && !x) || !w || !y || (!ws && !noalloc)) return CIW_ERR_INVALID_ARG;
     if ((x && !aligned(x, 16)) || !aligned(w, 16) || !aligned(y, 16) || !aligned(ws, 16) ||
         (bias && !aligned(bias, elem_bytes(in))))
         return CIW_ERR_INVALID_ARG;
@@ -176,6 +218,7 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
         const size_t need = implicit_workspace_bytes(g, out, epi);
         if (need == 0) return CIW_ERR_UNSUPPORTED;
         if (ws_bytes < need) return CIW_ERR_WORKSPACE;
+        if (noalloc && (s = scratch_of_current_device(&ws)) != CIW_OK) return s;
         (void)hipGetLastError();
         return from_hip(launch_conv_implicit(g, in, out, x, w, bias, y, ws, epi, (hipStream_t)stream));
     }
@@ -204,6 +247,7 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
         if (nc == 0) return CIW_ERR_WORKSPACE;
     }
 
+    if (noalloc && (s = scratch_of_current_device(&ws)) != CIW_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     (void)hipGetLastError();   // clear a stale error so launch checks report our own
     // the matrix-core kernel's filter copy sits after the window tensor of
@@ -365,6 +409,13 @@ ciw_status conv2d_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype o
                       size_t workspace_bytes, uint32_t flags, void* stream) {
     return run_conv(desc, in_dtype, out_dtype, x, w, bias, y, workspace, workspace_bytes, flags,
                     stream, false);
+}
+
+ciw_status conv2d_fwd_noalloc(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype out_dtype,
+                              const void* x, const void* w, const void* bias, void* y,
+                              uint32_t flags, void* stream) {
+    return run_conv(desc, in_dtype, out_dtype, x, w, bias, y, nullptr, 0, flags, stream, false,
+                    true);
 }
 
 ciw_status conv2d_dw_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype out_dtype,

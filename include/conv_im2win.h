@@ -211,6 +211,29 @@ ciw_status conv2d_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype o
                       void* workspace, size_t workspace_bytes, uint32_t flags,
                       void* stream);
 
+/* Size of the device array conv2d_fwd_noalloc uses as its workspace. */
+#define CIW_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* conv2d_fwd without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The workspace is
+ * a file-scope device array of the library, CIW_NOALLOC_SCRATCH_BYTES bytes
+ * per GPU, held from the first call on that GPU until the process ends; the
+ * batch is processed in chunks of as many images as fit in it (see
+ * conv2d_workspace_bytes), with CIW_FLAG_IMPLICIT the array holds the
+ * re-laid-out filter.  Same arguments, flags and results as conv2d_fwd
+ * otherwise.  Errors (before anything is enqueued): CIW_ERR_WORKSPACE if
+ * one image's workspace (or the CIW_FLAG_IMPLICIT workspace) exceeds the
+ * array; CIW_ERR_INVALID_ARG with CIW_FLAG_WINDOW_READY (the array cannot
+ * hold a window tensor the caller prepared); CIW_ERR_HIP if the runtime
+ * cannot give the array's address.  The library calls no allocating routine
+ * on this path.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams or threads) race and must be ordered by
+ * the caller. */
+ciw_status conv2d_fwd_noalloc(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype out_dtype,
+                              const void* x, const void* w, const void* bias, void* y,
+                              uint32_t flags, void* stream);
+
 /* Depthwise forward convolution (groups == C == K, one filter per channel;
  * "Diagonalwise Refactorization: An Efficient Training Method for Depthwise
  * Convolutions", abstract: each input channel is convolved with its own

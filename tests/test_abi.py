@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_and_binding_agree():
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     assert tuple(names) == _lib.ENTRY_POINTS
 
 
@@ -267,3 +267,34 @@ def test_transform_validation():
     assert L.conv_im2win_transform(ctypes.byref(d), 0, 0, None, FAKE, None) == _lib.CIW_ERR_INVALID_ARG
     assert L.conv_im2win_transform(ctypes.byref(d), 0, 0, FAKE, FAKE + 8, None) == _lib.CIW_ERR_INVALID_ARG
     assert L.conv_im2win_transform(ctypes.byref(d), 5, 0, FAKE, FAKE, None) == _lib.CIW_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------- allocation-free entry point
+def call_noalloc(d, in_dt=0, out_dt=0, x=FAKE, w=FAKE, b=None, y=FAKE, flags=0):
+    return lib().conv2d_fwd_noalloc(ctypes.byref(d) if d is not None else None, in_dt, out_dt,
+                                    x, w, b, y, flags, None)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    assert re.search(r"#define CIW_NOALLOC_SCRATCH_BYTES \(32u << 20\)", text)
+    assert _lib.CIW_NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
+def test_noalloc_validation_before_any_launch():
+    """Every rejection happens before the library touches the runtime (these
+    run without a GPU)."""
+    assert call_noalloc(None) == _lib.CIW_ERR_INVALID_ARG
+    d = valid_desc()
+    # a prepared window tensor cannot live in the library's array
+    assert call_noalloc(d, x=None, flags=m.CIW_FLAG_WINDOW_READY) == _lib.CIW_ERR_INVALID_ARG
+    assert call_noalloc(d, x=None) == _lib.CIW_ERR_INVALID_ARG
+    assert call_noalloc(d, y=FAKE + 8) == _lib.CIW_ERR_INVALID_ARG
+    assert call_noalloc(d, flags=0x10000) == _lib.CIW_ERR_INVALID_ARG
+    assert call_noalloc(d, in_dt=0, out_dt=1) == _lib.CIW_ERR_INVALID_ARG
+    assert call_noalloc(valid_desc(C=4, K=4, groups=4)) == _lib.CIW_ERR_UNSUPPORTED
+    # one image's window tensor larger than the array: 224 x (226*3*512) x 2 B
+    big = valid_desc(N=2, C=512, H=224, W=224, K=64)
+    assert m.conv2d_workspace_bytes(big, 1, 1) > _lib.CIW_NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(big, in_dt=1, out_dt=1) == _lib.CIW_ERR_WORKSPACE
+    assert call_noalloc(valid_desc(N=0), x=None, w=None, y=None) == _lib.CIW_OK
