@@ -30,7 +30,7 @@ ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "transform.hip", "conv_fp32.hip", "conv_fp32_mfma.hip", "conv_mfma.hip", "conv_mfma_f16.hip",
            "conv_mfma_bf16.hip", "conv_dw.hip", "conv_dw_implicit.hip", "conv_implicit.hip", "conv_implicit_f16.hip",
-           "conv_implicit_bf16.hip"]
+           "conv_implicit_bf16.hip", "conv_band_f16.hip", "conv_band_bf16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
@@ -61,13 +61,17 @@ VARIANTS = {
     "rows_baseline": ([], ["conv_mfma.hip", "conv_mfma_f16.hip"],
                       "row kernel as in the library"),
     # the window-row buffers of the in-LDS kernel (conv_mfma_implicit_kernel)
-    "implicit_baseline": ([], ["conv_implicit.hip", "conv_implicit_f16.hip"],
-                          "in-LDS window kernel as in the library"),
-    "implicit_no_double": (["-DCIW_ABLATE_NO_DOUBLE=1"], ["conv_implicit.hip", "conv_implicit_f16.hip"],
+    # (CIW_BAND_OFF keeps these on that kernel where the band kernel would run)
+    "implicit_baseline": (["-DCIW_BAND_OFF=1"], ["conv_implicit.hip", "conv_implicit_f16.hip"],
+                          "row-band in-LDS window kernel as in the library"),
+    "implicit_no_double": (["-DCIW_BAND_OFF=1", "-DCIW_ABLATE_NO_DOUBLE=1"],
+                           ["conv_implicit.hip", "conv_implicit_f16.hip"],
                            "input row copied at the step that needs it, then waited for"),
-    "implicit_no_async": (["-DCIW_ABLATE_NO_ASYNC=1"], ["conv_implicit.hip", "conv_implicit_f16.hip"],
+    "implicit_no_async": (["-DCIW_BAND_OFF=1", "-DCIW_ABLATE_NO_ASYNC=1"],
+                          ["conv_implicit.hip", "conv_implicit_f16.hip"],
                           "rows copied global -> registers -> LDS"),
-    "implicit_no_xcd": (["-DCIW_ABLATE_NO_XCD=1"], ["conv_implicit.hip", "conv_implicit_f16.hip"],
+    "implicit_no_xcd": (["-DCIW_BAND_OFF=1", "-DCIW_ABLATE_NO_XCD=1"],
+                        ["conv_implicit.hip", "conv_implicit_f16.hip"],
                         "bands in dispatch order"),
 }
 VARIANT_DIR = os.path.join(PKG, "variants")

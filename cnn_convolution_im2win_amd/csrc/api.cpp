@@ -206,19 +206,21 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
     }
     if (g.N == 0) return CIW_OK;   // empty batch: nothing to do
     const bool ready = (flags & CIW_FLAG_WINDOW_READY) != 0;
-    if ((!ready && !x) || !w || !y || (!ws && !noalloc)) return CIW_ERR_INVALID_ARG;
+    size_t imp_need = 0;   // workspace of the in-LDS kernels (may be 0: then ws may be NULL)
+    if (implicit) {
+        if (in == CIW_F32 || !implicit_workspace(g, out, epi, &imp_need)) return CIW_ERR_UNSUPPORTED;
+    }
+    const bool ws_needed = !noalloc && !(implicit && imp_need == 0);
+    if ((!ready && !x) || !w || !y || (!ws && ws_needed)) return CIW_ERR_INVALID_ARG;
     if ((x && !aligned(x, 16)) || !aligned(w, 16) || !aligned(y, 16) || !aligned(ws, 16) ||
         (bias && !aligned(bias, elem_bytes(in))))
         return CIW_ERR_INVALID_ARG;
 
     if (implicit) {
         // window rows built in LDS from x: no chunks, the workspace holds
-        // only the re-laid-out filter
-        if (in == CIW_F32) return CIW_ERR_UNSUPPORTED;
-        const size_t need = implicit_workspace_bytes(g, out, epi);
-        if (need == 0) return CIW_ERR_UNSUPPORTED;
-        if (ws_bytes < need) return CIW_ERR_WORKSPACE;
-        if (noalloc && (s = scratch_of_current_device(&ws)) != CIW_OK) return s;
+        // at most the re-laid-out filter
+        if (ws_bytes < imp_need) return CIW_ERR_WORKSPACE;
+        if (noalloc && imp_need > 0 && (s = scratch_of_current_device(&ws)) != CIW_OK) return s;
         (void)hipGetLastError();
         return from_hip(launch_conv_implicit(g, in, out, x, w, bias, y, ws, epi, (hipStream_t)stream));
     }
@@ -397,9 +399,8 @@ ciw_status conv2d_implicit_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype 
         *bytes = 0;
         return CIW_OK;
     }
-    if (in_dtype == CIW_F32) return CIW_ERR_UNSUPPORTED;
-    const size_t need = implicit_workspace_bytes(g, out_dtype, epi);
-    if (need == 0) return CIW_ERR_UNSUPPORTED;
+    size_t need = 0;
+    if (in_dtype == CIW_F32 || !implicit_workspace(g, out_dtype, epi, &need)) return CIW_ERR_UNSUPPORTED;
     *bytes = need;
     return CIW_OK;
 }

@@ -112,10 +112,11 @@ hipError_t launch_conv_mfma(const Geom& g, ciw_dtype in, ciw_dtype out, const vo
                             int n_images, bool generic, const Epi& epi, hipStream_t st);
 
 // fp16/bf16 dense contraction that builds its window rows in LDS from x
-// (no window tensor in memory).  implicit_workspace_bytes is 0 for layers
-// the kernel does not run; otherwise the workspace holds the re-laid-out
-// filter, which launch_conv_implicit writes before the contraction.
-size_t implicit_workspace_bytes(const Geom& g, ciw_dtype out, const Epi& epi);
+// (no window tensor in memory).  implicit_workspace is false for layers no
+// such kernel runs; otherwise *bytes is the workspace: 0 for the band
+// kernel (3x3, no pool), else the re-laid-out filter, which
+// launch_conv_implicit writes before the contraction.
+bool implicit_workspace(const Geom& g, ciw_dtype out, const Epi& epi, size_t* bytes);
 hipError_t launch_conv_implicit(const Geom& g, ciw_dtype in, ciw_dtype out, const void* x,
                                 const void* w, const void* bias, void* y, void* ws,
                                 const Epi& epi, hipStream_t st);

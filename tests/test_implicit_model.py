@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
+from tests.test_band_model import band_plan
 
 THREADS = 256
 MAX_COPIES = 4
@@ -455,8 +456,13 @@ def test_plan_agrees_with_library():
             flags = _lib.CIW_FLAG_MAXPOOL2 if pool else 0
             st = _lib.load().conv2d_implicit_workspace_bytes(ctypes.byref(desc), dt, out_dt, flags,
                                                              ctypes.byref(out))
+            # the band kernel (3x3, no pool; no workspace) takes the layers it
+            # runs before this kernel
+            band = band_plan(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, pool=pool)
             if pool and (g.P < 2 or g.Q < 2):
                 assert st == _lib.CIW_ERR_INVALID_ARG, s
+            elif band is not None:
+                assert st == 0 and out.value == 0, s
             elif a is None:
                 assert st == _lib.CIW_ERR_UNSUPPORTED, s
             else:
