@@ -9,18 +9,19 @@
 // xw[n][c][h][(w*stride_w + q*dil_w)*R + r] (§III-C: the R values of a
 // column adjacent, columns in order).
 //
-// A workgroup (8 waves) owns 64 output channels, a block of up to 192
-// output pixels (whole output rows of one image) and a slice of TC input
-// channels, which it streams through LDS in chunks of 8 channels (filter
-// rows and window rows, double-buffered).  Waves 0-3 reduce the first half
-// of each chunk, waves 4-7 the second; within a half, wave t owns channel tile t & 1 (32
-// channels) and pixel tiles 3 (t >> 1) .. 3 (t >> 1) + 2.  One MFMA step
-// takes two reduction entries (lane / 32 picks one): a channel pair at one
-// filter tap.  The two halves' sums are added through LDS, first half
-// first; with several slices the slice sums go to a partial
-// buffer [slice][n][K][P*Q] that a second kernel adds in slice order, then
-// the bias and ReLU.  Every sum is in a fixed order: results are
-// deterministic.
+// A workgroup (8 waves) owns 32 output channels, a block of up to 192
+// output pixels (whole output rows of one image) and a slice of up to 64
+// input channels, which it streams through LDS in chunks of 16 channels
+// (filter rows and window rows, double-buffered).  Wave t owns pixel tiles
+// 3 (t & 1) .. 3 (t & 1) + 2 and reduces quarter t >> 1 of each chunk's
+// channels.  One MFMA step takes two reduction entries (lane / 32 picks
+// one): a channel pair at one filter tap.  The four quarters' sums are added
+// through LDS in quarter order; with several slices the slice sums go to a
+// partial buffer [slice][n][K][P*Q] that a second kernel adds in slice
+// order, then the bias and ReLU.  Every sum is in a fixed order: results
+// are deterministic.  (32 channels per workgroup rather than 64 keeps the
+// filter read once while halving the slices, and with them the partial
+// sums written and read back.)
 #include <algorithm>
 
 #include "internal.hpp"
@@ -31,9 +32,10 @@ namespace {
 
 constexpr int kMThreads = 512;   // 8 waves
 constexpr int kMaxPix = 192;     // pixels per block: 6 tiles of 32
-constexpr int kTC = 32;          // input channels per slice (at most)
-constexpr int kCh = 8;           // channels per LDS chunk (two pairs per half)
-constexpr int kMaxB = 3;         // window float4 loads per thread per chunk
+constexpr int kMT = 32;          // output channels per workgroup
+constexpr int kTC = 64;          // input channels per slice (at most)
+constexpr int kCh = 16;          // channels per LDS chunk (two pairs per quarter)
+constexpr int kMaxB = 6;         // window float4 loads per thread per chunk
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -41,7 +43,7 @@ struct F32MArgs {
     int C, K, P, Q, pitch, sw, dw;
     int HB;          // output rows per pixel block
     int pblocks;     // pixel blocks per image
-    int mblocks;     // 64-channel blocks
+    int mblocks;     // 32-channel blocks
     int splits, TC;  // channel slices, channels per slice (even)
     int AS;          // LDS row stride of the staged filter (floats)
     int BS;          // LDS stride between staged channels of the window (floats)
@@ -58,9 +60,8 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int half = wave >> 2;
-    const int ct = wave & 1;          // channel tile
-    const int pg = (wave >> 1) & 1;   // pixel tiles 3 pg .. 3 pg + 2
+    const int qt = wave >> 1;         // quarter of each chunk's channels
+    const int pg = wave & 1;          // pixel tiles 3 pg .. 3 pg + 2
     const int j = lane & 31;          // A row (channel) / B column (pixel) of the lane
     const int kk = lane >> 5;         // reduction entry of the pair
 
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
     rest /= a.pblocks;
     const int n_img = rest % a.nimg;
     const int sl = rest / a.nimg;
-    const int k0 = mb * 64;
+    const int k0 = mb * kMT;
     const int h0 = pb * a.HB;
     const int rows = min(a.HB, a.P - h0);
     const int npx = rows * a.Q;
@@ -86,15 +87,15 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
     // ---- the slice in chunks of kCh channels, double-buffered in LDS: the
     // global loads of chunk ch + 1 are in flight (in registers) while chunk
     // ch multiplies, then land in the other buffer.  A chunk holds the
-    // filter rows k0 .. k0 + 63 over its channels cc .. cc + kCh - 1,
-    // entries (c - cc) * RS + r * S + q of the KCRS filter ([64][AS], zero
+    // filter rows k0 .. k0 + 31 over its channels cc .. cc + kCh - 1,
+    // entries (c - cc) * RS + r * S + q of the KCRS filter ([32][AS], zero
     // past K and C), and the window rows h0 .. h0 + rows - 1 of its
     // channels ([kCh][BS]).  Consecutive lanes load consecutive floats of
     // a filter row and write consecutive LDS banks.
-    const int chunk_floats = 64 * a.AS + kCh * a.BS;
+    const int chunk_floats = kMT * a.AS + kCh * a.BS;
     const int nch = (tc + kCh - 1) / kCh;
     constexpr int T = kCh * RS;                  // filter entries per chunk row
-    constexpr int kAL = (64 * T + kMThreads - 1) / kMThreads;   // filter loads per thread
+    constexpr int kAL = (kMT * T + kMThreads - 1) / kMThreads;  // filter loads per thread
     const int run4 = rows * a.pitch / 4;         // float4 per channel (pitch is a multiple of 4)
     const int nB4 = kCh * run4;
     const int kBL = (nB4 + kMThreads - 1) / kMThreads;          // window loads per thread (<= kMaxB)
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
             const int e = tid + u * kMThreads;
             const int row = e / T, t = e - row * T;
             ra[u] = 0.f;
-            if (e < 64 * T && k0 + row < a.K && t < nc * RS)
+            if (e < kMT * T && k0 + row < a.K && t < nc * RS)
                 ra[u] = w[((size_t)(k0 + row) * a.C + cc) * RS + t];
         }
 #pragma unroll
@@ -129,12 +130,12 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
         const float (&ra)[kAL] = f.ra;
         const float4 (&rb)[kMaxB] = f.rb;
         float* As = smem + buf * chunk_floats;
-        float* Bs = As + 64 * a.AS;
+        float* Bs = As + kMT * a.AS;
 #pragma unroll
         for (int u = 0; u < kAL; ++u) {
             const int e = tid + u * kMThreads;
             const int row = e / T, t = e - row * T;
-            if (e < 64 * T) As[row * a.AS + t] = ra[u];
+            if (e < kMT * T) As[row * a.AS + t] = ra[u];
         }
 #pragma unroll
         for (int u = 0; u < kMaxB; ++u) {
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[t3][v] = 0.f;
 
-    // One chunk: the half's channel pairs (kCh / 4 of them), each the
+    // One chunk: the quarter's channel pairs (kCh / 8 of them), each the
     // lane's filter taps and, per pixel tile, its window taps; the second
     // pair's operands are read while the first pair multiplies.
     struct Ops {
@@ -172,11 +173,11 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
     };
     auto multiply = [&](int buf) {
         const float* As = smem + buf * chunk_floats;
-        const float* Bs = As + 64 * a.AS;
-        const float* arow = As + (ct * 32 + j) * a.AS + kk * RS;
+        const float* Bs = As + kMT * a.AS;
+        const float* arow = As + j * a.AS + kk * RS;
         const float* bch = Bs + kk * a.BS;
         auto load = [&](Ops& o, int cp) {
-            const int cl = half * (kCh / 2) + 2 * cp;   // lane's channel: cl + kk
+            const int cl = qt * (kCh / 4) + 2 * cp;     // lane's channel: cl + kk
             const float* ap = arow + cl * RS;
             const float* bp = bch + cl * a.BS;
 #pragma unroll
@@ -212,21 +213,23 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
         __syncthreads();
     }
 
-    // ---- the two halves' sums (through LDS; the chunk buffers are no
-    // longer read after the loop's last barrier).
-    // Each half finishes 8 of a lane's 16 entries per tile (half h the
-    // entries 8 h .. 8 h + 7): it hands the other 8 to the wave of the
-    // other half with the same tiles, which adds them after its own (first
-    // half first, the sum's fixed order).
-    float* red = smem;                           // [2 halves][4 waves][3][8][64]
-    const int tg = wave & 3;
-    const int mine = half * 8, theirs = 8 - half * 8;
-    float* to_other = red + ((1 - half) * 4 + tg) * 3 * 8 * 64;
-    const float* from_other = red + (half * 4 + tg) * 3 * 8 * 64;
+    // ---- the four quarters' sums (through LDS; the chunk buffers are no
+    // longer read after the loop's last barrier).  Wave (pg, qt) finishes
+    // entries 4 qt .. 4 qt + 3 of each of its tiles' 16: it hands the other
+    // 12 to the waves of the other quarters with the same tiles, and adds
+    // the four quarters' values of its own entries in quarter order.
+    // red[dst quarter][pg][src quarter][t3][4][64]
+    float* red = smem;
+    auto slot = [&](int dq, int sq) { return red + (((dq * 2 + pg) * 4 + sq) * 3) * 4 * 64; };
 #pragma unroll
-    for (int t3 = 0; t3 < 3; ++t3)
+    for (int dq = 0; dq < 4; ++dq) {
+        if (dq == qt) continue;
+        float* to = slot(dq, qt);
 #pragma unroll
-        for (int v = 0; v < 8; ++v) to_other[(t3 * 8 + v) * 64 + lane] = acc[t3][theirs + v];
+        for (int t3 = 0; t3 < 3; ++t3)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) to[(t3 * 4 + e) * 64 + lane] = acc[t3][4 * dq + e];
+    }
     __syncthreads();
     // lane holds D[i][j] for channel i = 8 (v / 4) + 4 kk + v % 4 of the
     // tile, pixel j of the tile
@@ -237,11 +240,16 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
     for (int t3 = 0; t3 < 3; ++t3) {
         const int px = (3 * pg + t3) * 32 + j;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const int vv = mine + v;
-            const int k = k0 + ct * 32 + 8 * (vv >> 2) + 4 * kk + (vv & 3);
-            const float o = from_other[(t3 * 8 + v) * 64 + lane];
-            float s = half == 0 ? acc[t3][vv] + o : o + acc[t3][vv];
+        for (int e = 0; e < 4; ++e) {
+            const int k = k0 + 8 * qt + 4 * kk + e;
+            // the wave's own value of entry vv (qt is uniform: a branch, no
+            // indexed register access)
+            const float mine = qt == 0 ? acc[t3][e] : qt == 1 ? acc[t3][4 + e]
+                             : qt == 2 ? acc[t3][8 + e] : acc[t3][12 + e];
+            float s = 0.f;
+#pragma unroll
+            for (int sq = 0; sq < 4; ++sq)
+                s += sq == qt ? mine : slot(qt, sq)[(t3 * 4 + e) * 64 + lane];
             if (px < npx && k < a.K) {
                 if (final_out) {
                     s += bias ? bias[k] : 0.f;
@@ -254,48 +262,28 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
 }
 
 // y[i] = bias[k] + sum over slices s (in order) of part[s][i], i = (n*K + k)*PQ + pix.
-// VEC (a slice holds a multiple of 4 outputs, so every slice starts 16-byte
-// aligned): four consecutive outputs per thread with 16-byte loads and
-// stores, every slice's loads issued before the sums, which then run in
-// slice order.  Otherwise one output per thread.
-constexpr int kRedMax = 32;   // slices a thread holds in registers at once
-template <bool VEC>
+// One output per thread (consecutive threads, consecutive outputs: every
+// slice's loads are coalesced), the slices' loads issued kRedMax at a time
+// before their in-order sum.
+constexpr int kRedMax = 16;
 __global__ __launch_bounds__(256) void split_reduce_nkp_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, float* __restrict__ y,
     uint32_t per_split, int splits, int PQ, int K, int relu) {
     const uint32_t t = blockIdx.x * 256 + threadIdx.x;
-    if (!VEC) {
-        if (t >= per_split) return;
-        float v = 0.f;
-        for (int s = 0; s < splits; ++s) v += part[(size_t)s * per_split + t];
-        const int k = (int)((t / (uint32_t)PQ) % (uint32_t)K);
-        v += bias ? bias[k] : 0.f;
-        y[t] = relu ? fmaxf(v, 0.f) : v;
-        return;
-    }
-    if (4 * t >= per_split) return;
-    const float4* p4 = reinterpret_cast<const float4*>(part) + t;
-    const uint32_t stride4 = per_split / 4;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t >= per_split) return;
+    float acc = 0.f;
     for (int s0 = 0; s0 < splits; s0 += kRedMax) {
-        float4 v[kRedMax];
+        float v[kRedMax];
 #pragma unroll
         for (int s = 0; s < kRedMax; ++s)
-            if (s0 + s < splits) v[s] = p4[(size_t)(s0 + s) * stride4];
+            if (s0 + s < splits) v[s] = part[(size_t)(s0 + s) * per_split + t];
 #pragma unroll
         for (int s = 0; s < kRedMax; ++s)
-            if (s0 + s < splits) {
-                acc.x += v[s].x; acc.y += v[s].y; acc.z += v[s].z; acc.w += v[s].w;
-            }
+            if (s0 + s < splits) acc += v[s];
     }
-    float* a = &acc.x;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int k = (int)(((4 * t + e) / (uint32_t)PQ) % (uint32_t)K);
-        const float v = a[e] + (bias ? bias[k] : 0.f);
-        a[e] = relu ? fmaxf(v, 0.f) : v;
-    }
-    reinterpret_cast<float4*>(y)[t] = acc;
+    const int k = (int)((t / (uint32_t)PQ) % (uint32_t)K);
+    const float v = acc + (bias ? bias[k] : 0.f);
+    y[t] = relu ? fmaxf(v, 0.f) : v;
 }
 
 struct F32MPlan {
@@ -312,10 +300,10 @@ bool f32m_plan(const Geom& g, int n_images, F32MPlan& pl) {
     a.C = g.C; a.K = g.K; a.P = g.P; a.Q = g.Q; a.pitch = g.pitchA; a.sw = g.sw; a.dw = g.dw;
     a.HB = std::min(g.P, kMaxPix / g.Q);
     a.pblocks = (g.P + a.HB - 1) / a.HB;
-    a.mblocks = (g.K + 63) / 64;
+    a.mblocks = (g.K + kMT - 1) / kMT;
     const int RS = g.R * g.S;
-    // slices: about one workgroup per CU in total, each slice an even
-    // channel count of at most kTC (a multiple of 4: two halves of pairs)
+    // slices: about one workgroup per CU in total, each slice whole chunks
+    // of kCh channels, at most kTC
     const int64_t others = (int64_t)n_images * a.pblocks * a.mblocks;
     int want = (int)std::max<int64_t>(1, (256 + others - 1) / others);
     int tc = (g.C + want - 1) / want;
@@ -331,8 +319,8 @@ bool f32m_plan(const Geom& g, int n_images, F32MPlan& pl) {
     if (ntask >= (1ll << 31)) return false;
     a.ntask = (int)ntask;
     a.nimg = n_images;
-    const size_t staged = (size_t)2 * ((size_t)64 * a.AS + (size_t)kCh * a.BS) * 4;
-    const size_t red = (size_t)2 * 4 * 3 * 8 * 64 * 4;
+    const size_t staged = (size_t)2 * ((size_t)kMT * a.AS + (size_t)kCh * a.BS) * 4;
+    const size_t red = (size_t)4 * 2 * 4 * 3 * 4 * 64 * 4;   // [4][2][4][3][4][64] floats
     pl.lds = std::max(staged, red);
     return pl.lds <= 160 * 1024;
 }
@@ -360,13 +348,7 @@ hipError_t launch_conv_fp32_mfma(const Geom& g, const float* xw, const float* w,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || pl.a.splits == 1) return e;
     const int64_t per_split = (int64_t)n_images * g.K * g.P * g.Q;
-    // float4 form: every slice starts 16-byte aligned (per_split % 4 == 0,
-    // partials is) and so must y, which is offset by the chunk's first
-    // image and need not be
-    const bool vec = per_split % 4 == 0 && ((uintptr_t)y & 15u) == 0;
-    const int64_t threads = vec ? per_split / 4 : per_split;
-    hipLaunchKernelGGL(vec ? split_reduce_nkp_kernel<true> : split_reduce_nkp_kernel<false>,
-                       dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL(split_reduce_nkp_kernel, dim3((uint32_t)((per_split + 255) / 256)), dim3(256), 0,
                        st, partials, bias, y, (uint32_t)per_split, pl.a.splits, g.P * g.Q, g.K,
                        (int)epi.relu);
     return hipGetLastError();
