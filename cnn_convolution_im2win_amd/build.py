@@ -55,11 +55,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-# name -> (compile definitions, sources recompiled with them, what it measures)
+# name -> (compile definitions, sources recompiled with them, what it measures).
+# The row-kernel variants are built for the fp16 3x3 64 -> 64 layer they are
+# timed and checked on (CIW_ROWS_ABLATION_ONLY: other row-kernel plans are
+# turned down with an error), which keeps their builds short.
 VARIANTS = {
     # the materialised-window row kernel (conv_mfma_rows_kernel), fp16 inputs
-    "rows_baseline": ([], ["conv_mfma.hip", "conv_mfma_f16.hip"],
+    "rows_baseline": (["-DCIW_ROWS_ABLATION_ONLY=1"], ["conv_mfma.hip", "conv_mfma_f16.hip"],
                       "row kernel as in the library"),
+    "rows_no_double": (["-DCIW_ROWS_ABLATION_ONLY=1", "-DCIW_ABLATE_ROWS_NO_DOUBLE=1"], ["conv_mfma.hip", "conv_mfma_f16.hip"],
+                       "one row buffer: each row copied when it is multiplied, then waited for"),
+    "rows_no_async": (["-DCIW_ROWS_ABLATION_ONLY=1", "-DCIW_ABLATE_ROWS_NO_ASYNC=1"], ["conv_mfma.hip", "conv_mfma_f16.hip"],
+                      "rows copied global -> registers -> LDS"),
+    "rows_no_pad": (["-DCIW_ROWS_ABLATION_ONLY=1", "-DCIW_ABLATE_ROWS_NO_PAD=1"], ["conv_mfma.hip", "conv_mfma_f16.hip"],
+                    "no LDS pad chunks: a fragment's lanes read the same banks"),
+    "rows_no_index": (["-DCIW_ROWS_ABLATION_ONLY=1", "-DCIW_ABLATE_ROWS_NO_INDEX=1"], ["conv_mfma.hip", "conv_mfma_f16.hip"],
+                      "plain divisions and no filter re-layout: fragments gathered in the kernel"),
     # the window-row buffers of the in-LDS kernel (conv_mfma_implicit_kernel)
     # (CIW_BAND_OFF keeps these on that kernel where the band kernel would run)
     "implicit_baseline": (["-DCIW_BAND_OFF=1"], ["conv_implicit.hip", "conv_implicit_f16.hip"],

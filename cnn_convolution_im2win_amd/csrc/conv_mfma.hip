@@ -23,6 +23,7 @@ hipError_t launch_mfma_prep(const Geom& g, ciw_dtype out, const void* w, void* a
                             hipStream_t st) {
     MfRowPlan pl;
     if (!mf_row_plan(g, elem_bytes(out), pl)) return hipSuccess;   // generic kernel: no prep
+    if (CIW_ABLATE_ROWS_NO_INDEX) return hipSuccess;                // the kernel gathers itself
     PermArgs p;
     p.C = g.C; p.K = g.K; p.R = g.R; p.S = g.S;
     p.D = pl.a.D; p.T = pl.a.T; p.steps = pl.steps;

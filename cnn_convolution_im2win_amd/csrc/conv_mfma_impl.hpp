@@ -196,6 +196,41 @@ __global__ __launch_bounds__(kThreads) void conv_mfma_generic_kernel(
 // chunks (PAD the largest power of two dividing G, at most 8), which makes
 // the lane stride G + G/PAD odd; every run starts on the pad grid, so the
 // offset of each reduction step is a compile-time constant.
+// Ablation switches of the row kernel (compile definitions; the library is
+// built with all of them 0, the ablation variants each set one).  Each
+// changes when or how data moves, never the order of a sum:
+//   CIW_ABLATE_ROWS_NO_DOUBLE: one row buffer; each row is copied at the
+//     iteration that multiplies it and waited for (no copy-ahead).
+//   CIW_ABLATE_ROWS_NO_ASYNC: rows go global memory -> registers -> LDS
+//     instead of the direct global-to-LDS copy.
+//   CIW_ABLATE_ROWS_NO_PAD: no pad chunks in the LDS rows, so with one
+//     pixel phase the lanes of a fragment read the same banks (the
+//     bank-conflict avoidance that the im2win paper's zig-zag order serves).
+//   CIW_ABLATE_ROWS_NO_INDEX: no precomputed indices: plain divisions
+//     instead of the multiply-shift ones, and no filter re-layout kernel --
+//     each lane gathers its filter fragments from the KCRS filter itself,
+//     computing every element's (channel, filter row, filter column).
+#ifndef CIW_ABLATE_ROWS_NO_DOUBLE
+#define CIW_ABLATE_ROWS_NO_DOUBLE 0
+#endif
+#ifndef CIW_ABLATE_ROWS_NO_ASYNC
+#define CIW_ABLATE_ROWS_NO_ASYNC 0
+#endif
+#ifndef CIW_ABLATE_ROWS_NO_PAD
+#define CIW_ABLATE_ROWS_NO_PAD 0
+#endif
+#ifndef CIW_ABLATE_ROWS_NO_INDEX
+#define CIW_ABLATE_ROWS_NO_INDEX 0
+#endif
+// The ablation variants are timed and checked on one layer (fp16 in and
+// out, 3x3, 64 -> 64 channels, stride 1, no pool); CIW_ROWS_ABLATION_ONLY
+// builds only the row-kernel forms that layer uses (one pixel phase, 36
+// steps, no masks) and turns every other plan down with
+// hipErrorNotSupported, which keeps the variant builds short.
+#ifndef CIW_ROWS_ABLATION_ONLY
+#define CIW_ROWS_ABLATION_ONLY 0
+#endif
+
 struct MfRowArgs {
     int C, K, R, S, P, Q, pitch;   // pitch: window row pitch (elements)
     int D, T;                      // window start stride, window length
@@ -454,6 +489,33 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
 #pragma unroll
     for (int j = 0; j < NSET; ++j) {
         const int pb = min(pb0 * NSET + j, npb - 1);   // set j serves phase pb % nph
+        if (CIW_ABLATE_ROWS_NO_INDEX) {
+            // aperm is the KCRS filter: entry t of the fragment is filter
+            // (k, c, r, q) with t - delta = (q R + r) C + c, by division
+            const int dl = ((pb & (a.nph - 1)) * a.D) & 7;
+            const int k = kh * 32 + ml;
+#pragma clang loop unroll(full)
+            for (int s2 = 0; s2 < STEPS; ++s2) {
+                uint32_t d[4];
+#pragma clang loop unroll(full)
+                for (int e = 0; e < 8; ++e) {
+                    const int t = 16 * s2 + 8 * g + e - dl;
+                    uint32_t v = 0;
+                    if (k < a.K && t >= 0 && t < a.T) {
+                        const int qr = t / a.C, c = t % a.C;
+                        const int q = qr / a.R, r = qr % a.R;
+                        v = aperm[(((size_t)k * a.C + c) * a.R + r) * a.S + q];
+                    }
+                    if (e & 1) d[e >> 1] |= v << 16;
+                    else d[e >> 1] = v;
+                }
+                // opaque from here on: kept in registers like the loaded
+                // fragments, not recomputed where they are used
+                asm volatile("" : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]));
+                F[j][s2] = make_uint4(d[0], d[1], d[2], d[3]);
+            }
+            continue;
+        }
         const uint16_t* fp = aperm + ((size_t)((pb & (a.nph - 1)) * 2 + kh) * STEPS * 64 + lane) * 8;
 #pragma unroll
         for (int s2 = 0; s2 < STEPS; ++s2)
@@ -497,7 +559,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
     auto window_row = [&](int u) -> int {
         if (!POOL) return u;
         const uint32_t pr = (uint32_t)u >> 1;
-        const uint32_t n = fdiv(pr, a.fdPo);
+        const uint32_t n = CIW_ABLATE_ROWS_NO_INDEX ? pr / (uint32_t)a.Po : fdiv(pr, a.fdPo);
         return (int)(n * a.P + 2 * (pr - n * a.Po)) + (u & 1);
     };
     auto copy_row = [&](int u, int buf) {
@@ -506,6 +568,13 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
 #pragma unroll
         for (int j = 0; j < kMfMaxChunks; ++j) {
             if (j < a.nd) {
+                if (CIW_ABLATE_ROWS_NO_ASYNC) {
+                    // through registers, to the position the direct copy writes
+                    const uint4 v = *reinterpret_cast<const uint4*>(
+                        reinterpret_cast<const char*>(src) + src_off[j]);
+                    *reinterpret_cast<uint4*>(ring + buf * a.buf_elems + 8 * (pos_base[j] + tid)) = v;
+                    continue;
+                }
                 const uint32_t dst = __builtin_amdgcn_readfirstlane(dst0 + 16u * (uint32_t)pos_base[j]);
                 asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
                              :: "v"(src_off[j]), "s"(dst), "s"(src) : "memory");
@@ -569,7 +638,8 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
     // each tile read is issued one store ahead of its use.
     const int PQo = a.Po * a.Qo;
     auto store_row = [&](int orow_idx, const TOut* tl) {
-        const uint32_t n = fdiv(orow_idx, a.fdPo);
+        const uint32_t n = CIW_ABLATE_ROWS_NO_INDEX ? (uint32_t)orow_idx / (uint32_t)a.Po
+                                                    : fdiv(orow_idx, a.fdPo);
         const int h = orow_idx - n * a.Po;
         TOut* yrow = y + (size_t)n * a.K * PQo + (size_t)h * a.Qo;
         int k = sk0, v = sv0;
@@ -648,9 +718,18 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
             const int lo2 = max(lo, 2);
             later_stores = it - 1 >= lo2 ? (it - 1) / 2 - (lo2 - 1) / 2 : 0;
         }
-        wait_vm_lgkm(a.nd * later_rows + a.ns * later_stores);
+        if (CIW_ABLATE_ROWS_NO_DOUBLE) {
+            // one buffer: once every wave is done with row it - 1, copy row
+            // it into it and wait for the copy
+            if (it > 0) wg_barrier();
+            copy_row(first + it, 0);
+            wait_vm_lgkm(0);
+        } else {
+            wait_vm_lgkm(a.nd * later_rows + a.ns * later_stores);
+        }
         wg_barrier();                // row it landed; the tile to store is complete and free
-        if (it + a.nbuf - 1 < my_rows) copy_row(first + it + a.nbuf - 1, (it + a.nbuf - 1) % a.nbuf);
+        if (!CIW_ABLATE_ROWS_NO_DOUBLE && it + a.nbuf - 1 < my_rows)
+            copy_row(first + it + a.nbuf - 1, (it + a.nbuf - 1) % a.nbuf);
         if (!POOL) {
             if (it > 0) store_row(first + it - 1, otile0 + ((it - 1) & 1) * tile_elems);
         } else if (it >= 2 && (it & 1) == 0) {
@@ -909,7 +988,7 @@ bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl, const Epi& epi = E
     // power-of-two part of G, at most 8) makes the stride G + G / PAD odd
     const int G = nph == 1 ? D / 8 : 0;
     int pad = 1;
-    if (nph == 1)
+    if (nph == 1 && !CIW_ABLATE_ROWS_NO_PAD)
         while (pad < 8 && G % (2 * pad) == 0) pad *= 2;
     const int stride = pad == 1 ? D * nph / 8 : G + G / pad;   // chunks between lane starts
     const int copy_chunks = pad == 1 ? nchunks : (nchunks + pad - 1) / pad * (pad + 1);
@@ -939,7 +1018,7 @@ bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl, const Epi& epi = E
     // waits at a barrier or stores) beat one with a deeper ring
     int nbuf = 0, wgs = 0;
     for (int w = 2; w >= 1 && nbuf == 0; --w)
-        for (int nb = 6; nb >= 2; --nb)
+        for (int nb = CIW_ABLATE_ROWS_NO_DOUBLE ? 1 : 6; nb >= (CIW_ABLATE_ROWS_NO_DOUBLE ? 1 : 2); --nb)
             if (((size_t)nb * buf * 2 + tile) * w <= 160 * 1024) {
                 nbuf = nb;
                 wgs = w;
@@ -1053,6 +1132,12 @@ hipError_t launch_rows(const Geom& g, MfRowPlan pl, const void* xw, const void* 
         else if (pl.pad == 4) CIW_MF_STEPS(MK, 4);                                             \
         else CIW_MF_STEPS(MK, 8);                                                              \
     } while (0)
+#if CIW_ROWS_ABLATION_ONLY
+    if (POOL || pl.nset != 1 || pl.mask || pl.steps != 36 || (pl.pad != 1 && pl.pad != 8))
+        return hipErrorNotSupported;
+    if (pl.pad == 8) CIW_MF_LAUNCH(1, 36, false, 8);
+    else CIW_MF_LAUNCH(1, 36, false, 1);
+#else
     if (pl.nset == 1) {
         if (pl.mask) CIW_MF_PAD(true);
         else CIW_MF_PAD(false);
@@ -1062,6 +1147,7 @@ hipError_t launch_rows(const Geom& g, MfRowPlan pl, const void* xw, const void* 
     } else {
         CIW_MF_LAUNCH(4, 10, true, 1);
     }
+#endif
 #undef CIW_MF_PAD
 #undef CIW_MF_STEPS
 #undef CIW_MF_LAUNCH
@@ -1074,9 +1160,20 @@ hipError_t launch_t(const Geom& g, const void* xw, const void* w, const void* ap
                     hipStream_t st) {
     if (n_images == 0) return hipSuccess;
     MfRowPlan pl;
-    if (!generic && aperm && mf_row_plan(g, (int)sizeof(TOut), pl, epi))
-        return epi.pool ? launch_rows<TIn, TOut, true>(g, pl, xw, aperm, bias, y, n_images, st)
-                        : launch_rows<TIn, TOut, false>(g, pl, xw, aperm, bias, y, n_images, st);
+    if (!generic && aperm && mf_row_plan(g, (int)sizeof(TOut), pl, epi)) {
+        // without the re-layout the kernel gathers from the filter itself
+        const void* fsrc = CIW_ABLATE_ROWS_NO_INDEX ? w : aperm;
+#if CIW_ROWS_ABLATION_ONLY
+        if (epi.pool) return hipErrorNotSupported;
+        return launch_rows<TIn, TOut, false>(g, pl, xw, fsrc, bias, y, n_images, st);
+#else
+        return epi.pool ? launch_rows<TIn, TOut, true>(g, pl, xw, fsrc, bias, y, n_images, st)
+                        : launch_rows<TIn, TOut, false>(g, pl, xw, fsrc, bias, y, n_images, st);
+#endif
+    }
+#if CIW_ROWS_ABLATION_ONLY
+    return hipErrorNotSupported;
+#else
     MfmaArgs a;
     a.C = g.C; a.K = g.K; a.R = g.R; a.S = g.S; a.P = g.P; a.Q = g.Q;
     a.sw = g.sw; a.dw = g.dw; a.pitch = g.pitchB;
@@ -1097,6 +1194,7 @@ hipError_t launch_t(const Geom& g, const void* xw, const void* w, const void* ap
     hipLaunchKernelGGL((conv_mfma_generic_kernel<TIn, TOut>), grid, dim3(kThreads), 0, st,
                        (const uint16_t*)xw, (const uint16_t*)w, (const TIn*)bias, (TOut*)y, a);
     return hipGetLastError();
+#endif
 }
 
 }  // namespace
