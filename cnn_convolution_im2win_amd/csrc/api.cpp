@@ -31,6 +31,19 @@ int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d) {
 
 bool dtype_ok(int t) { return t == CIW_F32 || t == CIW_F16 || t == CIW_BF16; }
 
+// The integer a caller passed for an enum parameter, read from its bytes: a
+// C caller may pass any int, and loading an enum object that holds a value
+// outside the enumeration's range is undefined in C++.  Every entry point
+// checks its enum arguments this way before using them.
+template <typename E>
+int raw(const E& e) {
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+bool layout_ok(int l) { return l == CIW_WIN_CHW || l == CIW_WIN_HWC; }
+
 // Product of non-negative extents, false if it reaches 2^62 (then the
 // tensor is far past int32 indexing whatever the other factors are).  Every
 // partial product is checked, so no multiplication can overflow int64.
@@ -330,7 +343,7 @@ ciw_status conv2d_output_dims(const ciw_conv_desc* desc, uint32_t flags, int64_t
 ciw_status conv_im2win_window_geometry(const ciw_conv_desc* desc, ciw_dtype dtype,
                                        ciw_win_layout layout, int64_t* rows_per_image,
                                        int64_t* row_elems, int64_t* row_pitch) {
-    if (layout != CIW_WIN_CHW && layout != CIW_WIN_HWC) return CIW_ERR_INVALID_ARG;
+    if (!layout_ok(raw(layout)) || !dtype_ok(raw(dtype))) return CIW_ERR_INVALID_ARG;
     Geom g;
     ciw_status s = resolve(desc, dtype, &g);
     if (s != CIW_OK) return s;
@@ -343,7 +356,7 @@ ciw_status conv_im2win_window_geometry(const ciw_conv_desc* desc, ciw_dtype dtyp
 
 ciw_status conv_im2win_window_bytes(const ciw_conv_desc* desc, ciw_dtype dtype,
                                     ciw_win_layout layout, int64_t n_images, size_t* bytes) {
-    if (layout != CIW_WIN_CHW && layout != CIW_WIN_HWC) return CIW_ERR_INVALID_ARG;
+    if (!layout_ok(raw(layout)) || !dtype_ok(raw(dtype))) return CIW_ERR_INVALID_ARG;
     if (!bytes || n_images < 0) return CIW_ERR_INVALID_ARG;
     Geom g;
     ciw_status s = resolve(desc, dtype, &g);
@@ -357,7 +370,7 @@ ciw_status conv_im2win_window_bytes(const ciw_conv_desc* desc, ciw_dtype dtype,
 ciw_status conv_im2win_transform(const ciw_conv_desc* desc, ciw_dtype dtype,
                                  ciw_win_layout layout, const void* x, void* x_win,
                                  void* stream) {
-    if (layout != CIW_WIN_CHW && layout != CIW_WIN_HWC) return CIW_ERR_INVALID_ARG;
+    if (!layout_ok(raw(layout)) || !dtype_ok(raw(dtype))) return CIW_ERR_INVALID_ARG;
     Geom g;
     ciw_status s = resolve(desc, dtype, &g);
     if (s != CIW_OK) return s;
@@ -369,7 +382,7 @@ ciw_status conv_im2win_transform(const ciw_conv_desc* desc, ciw_dtype dtype,
 
 ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
                                   int64_t n_images, size_t* bytes) {
-    if (!bytes || n_images < 1) return CIW_ERR_INVALID_ARG;
+    if (!bytes || n_images < 1 || !dtype_ok(raw(in_dtype))) return CIW_ERR_INVALID_ARG;
     Geom g;
     ciw_status s = resolve(desc, in_dtype, &g);
     if (s != CIW_OK) return s;
@@ -384,7 +397,7 @@ ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
 
 ciw_status conv2d_implicit_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
                                            ciw_dtype out_dtype, uint32_t flags, size_t* bytes) {
-    if (!bytes || !dtype_ok(out_dtype)) return CIW_ERR_INVALID_ARG;
+    if (!bytes || !dtype_ok(raw(in_dtype)) || !dtype_ok(raw(out_dtype))) return CIW_ERR_INVALID_ARG;
     Geom g;
     ciw_status s = resolve(desc, in_dtype, &g);
     if (s != CIW_OK) return s;
@@ -408,6 +421,7 @@ ciw_status conv2d_implicit_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype 
 ciw_status conv2d_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype out_dtype,
                       const void* x, const void* w, const void* bias, void* y, void* workspace,
                       size_t workspace_bytes, uint32_t flags, void* stream) {
+    if (!dtype_ok(raw(in_dtype)) || !dtype_ok(raw(out_dtype))) return CIW_ERR_INVALID_ARG;
     return run_conv(desc, in_dtype, out_dtype, x, w, bias, y, workspace, workspace_bytes, flags,
                     stream, false);
 }
@@ -415,6 +429,7 @@ ciw_status conv2d_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype o
 ciw_status conv2d_fwd_noalloc(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype out_dtype,
                               const void* x, const void* w, const void* bias, void* y,
                               uint32_t flags, void* stream) {
+    if (!dtype_ok(raw(in_dtype)) || !dtype_ok(raw(out_dtype))) return CIW_ERR_INVALID_ARG;
     return run_conv(desc, in_dtype, out_dtype, x, w, bias, y, nullptr, 0, flags, stream, false,
                     true);
 }
@@ -423,12 +438,13 @@ ciw_status conv2d_dw_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtyp
                          const void* x, const void* w, const void* bias, void* y,
                          void* workspace, size_t workspace_bytes, uint32_t flags,
                          void* stream) {
+    if (!dtype_ok(raw(in_dtype)) || !dtype_ok(raw(out_dtype))) return CIW_ERR_INVALID_ARG;
     return run_conv(desc, in_dtype, out_dtype, x, w, bias, y, workspace, workspace_bytes, flags,
                     stream, true);
 }
 
 const char* conv_im2win_status_string(ciw_status status) {
-    switch (status) {
+    switch (raw(status)) {
         case CIW_OK: return "success";
         case CIW_ERR_INVALID_ARG: return "invalid argument";
         case CIW_ERR_UNSUPPORTED: return "unsupported convolution";

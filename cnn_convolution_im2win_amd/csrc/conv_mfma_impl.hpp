@@ -958,8 +958,12 @@ int gcd_int(int x, int y) {
 bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl, const Epi& epi = Epi{}) {
     if (g.K > 64 || g.dw != 1) return false;
     MfRowArgs& a = pl.a;
-    const int D = g.sw * g.R * g.C;
-    const int T = g.S * g.R * g.C;
+    // window start stride and length in elements, in 64 bits (a huge
+    // horizontal stride is legal); a window row must fit LDS anyway
+    const int64_t D64 = (int64_t)g.sw * g.R * g.C, T64 = (int64_t)g.S * g.R * g.C;
+    if (D64 > (1 << 20) || T64 > (1 << 20)) return false;
+    const int D = (int)D64;
+    const int T = (int)T64;
     const int nph = 8 / gcd_int(D, 8);
     int maxdelta = 0;
     for (int ph = 0; ph < nph; ++ph) maxdelta = std::max(maxdelta, (ph * D) & 7);

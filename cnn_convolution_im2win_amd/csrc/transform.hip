@@ -285,9 +285,12 @@ bool launch_chw_planes(const Geom& g, const void* x, void* xw, int n_images, hip
     PlaneArgs a;
     a.H = g.H; a.W = g.W; a.P = g.P; a.sh = g.sh; a.ph = g.ph; a.pw = g.pw; a.dh = g.dh; a.R = g.R;
     a.Wwin = g.Wwin; a.len = g.lenA; a.pitch = g.pitchA;
-    a.Hp = (g.P - 1) * g.sh + (g.R - 1) * g.dh + 1;
-    const int64_t tile_bytes = (int64_t)a.Hp * a.Wwin * sizeof(T);
-    if (tile_bytes > kPlaneLds) return false;
+    // input rows a plane's windows span, in 64 bits (a huge vertical stride
+    // is legal); the plane must fit LDS
+    const int64_t hp = (int64_t)(g.P - 1) * g.sh + (int64_t)(g.R - 1) * g.dh + 1;
+    const int64_t tile_bytes = hp * a.Wwin * (int64_t)sizeof(T);
+    if (hp > kPlaneLds || tile_bytes > kPlaneLds) return false;
+    a.Hp = (int)hp;
     const int64_t planes = (int64_t)n_images * g.C;
     if (planes >= (1ll << 31) || planes * g.H * g.W >= (1ll << 31)) return false;
     a.planes = (int)planes;
