@@ -33,10 +33,13 @@ struct DwImpArgs {
     int Po, Qo;          // output extent (pooled or not)
     int relu, pool;
     int strip;           // 3x3 strip form (planes padded to whole strips)
+    int pairs;           // strip form, no pool: a lane takes two adjacent columns (Qo even)
     int dQ, dH, dW;      // 256 input elements as planes, rows and columns (dH < H, dW < W)
     int vec4;            // H * W a multiple of 4 and W >= 4: fp32 input staged with 16-byte loads
     FastDiv fdHW, fdW, fdPQo, fdQo;
-    FastDiv fdStrip;     // strip items per plane: Qo * ceil(P / kSH), or Qo * ceil(Po / kPS) with the pool
+    FastDiv fdStrip;     // strip items per plane: Qo * ceil(P / kSH), Qo / 2 * ceil(P / kSH) with
+                         // pairs, or Qo * ceil(Po / kPS) with the pool
+    FastDiv fdQh;        // Qo / 2
 };
 
 // KR x KS: the filter extent when fixed at compile time (0: run time).
@@ -44,6 +47,18 @@ struct DwImpArgs {
 // conflicts): the planes are zeroed with consecutive 16-byte stores, then x
 // is copied element by element (consecutive lanes, consecutive elements:
 // coalesced), and lane i of a pass computes output o0 + i.
+// Two adjacent outputs, each rounded once to the output type, as one store
+// (p is aligned to two elements).
+template <typename T>
+__device__ __forceinline__ void store_pair(T* p, float a, float b) {
+    *reinterpret_cast<uint32_t*>(p) = (uint32_t)f32_bits<T>(a) | ((uint32_t)f32_bits<T>(b) << 16);
+}
+
+template <>
+__device__ __forceinline__ void store_pair<float>(float* p, float a, float b) {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+
 constexpr int kSH = 7;   // outputs per lane down a column (strip form)
 constexpr int kPS = 4;   // pooled outputs per lane down a column (strip form with the pool)
 
@@ -206,6 +221,58 @@ __global__ __launch_bounds__(kDThreads) void conv_dw_implicit_kernel(
         }
         return;
     }
+    if (STRIP && a.pairs) {
+        // 3x3, stride 1, dilation 1, no pool, Qo even: a lane computes kSH
+        // outputs down two adjacent columns 2 cp, 2 cp + 1.  Their inputs are
+        // the plane's columns 2 cp .. 2 cp + 3 (LDS columns; the interior
+        // starts at pad_w), an 8-byte-aligned run (Wp and the plane area are
+        // even): two 8-byte reads a row, and each output row leaves as one
+        // 2-element store (Qo and P * Qo even).
+        const int nstrip = (a.P + kSH - 1) / kSH;
+        const int qh = a.Qo >> 1;
+        const int per_plane = qh * nstrip;
+        for (int it = tid; it < np * per_plane; it += kDThreads) {
+            const uint32_t q = fdiv((uint32_t)it, a.fdStrip);
+            const int r = it - (int)q * per_plane;
+            const uint32_t st = fdiv((uint32_t)r, a.fdQh);
+            const int cp = r - (int)st * qh;
+            const int oh0 = (int)st * kSH;
+            const float* src = pl + q * HpWp + oh0 * a.Wp + 2 * cp;
+            const float* wt = wl + q * 9;
+            float wr[9];
+#pragma unroll
+            for (int t = 0; t < 9; ++t) wr[t] = wt[t];
+            const float b = bl[q];
+            float in[kSH + 2][4];
+#pragma unroll
+            for (int rr = 0; rr < kSH + 2; ++rr) {
+                const float2 lo = *reinterpret_cast<const float2*>(src + rr * a.Wp);
+                const float2 hi = *reinterpret_cast<const float2*>(src + rr * a.Wp + 2);
+                in[rr][0] = lo.x; in[rr][1] = lo.y; in[rr][2] = hi.x; in[rr][3] = hi.y;
+            }
+            TOut* yo = ys + (size_t)q * PQo + (size_t)oh0 * a.Qo + 2 * cp;
+#pragma unroll
+            for (int i = 0; i < kSH; ++i) {
+                if (oh0 + i < a.P) {
+                    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+                    for (int rr = 0; rr < 3; ++rr)
+#pragma unroll
+                        for (int cc = 0; cc < 3; ++cc) {
+                            acc0 = fmaf(in[i + rr][cc], wr[rr * 3 + cc], acc0);
+                            acc1 = fmaf(in[i + rr][cc + 1], wr[rr * 3 + cc], acc1);
+                        }
+                    float v0 = acc0 + b, v1 = acc1 + b;   // bias, then ReLU (maxNum against 0)
+                    if (a.relu) {
+                        v0 = fmaxf(v0, 0.f);
+                        v1 = fmaxf(v1, 0.f);
+                    }
+                    store_pair(yo + i * a.Qo, v0, v1);
+                }
+            }
+        }
+        return;
+    }
     if (STRIP) {
         // 3x3, stride 1, dilation 1, no pool: a lane computes kSH outputs
         // down one column (consecutive lanes: consecutive columns), reading
@@ -302,6 +369,8 @@ bool dw_imp_plan(const Geom& g, const Epi& epi, int n_images, DwImpArgs& a, size
         if (bytes_of(hs) <= kDwLdsBytes) a.Hp = hs;
         else a.strip = 0;
     }
+    // two columns a lane: Qo even (then Wp = Qo + 2 and P * Qo are even too)
+    a.pairs = a.strip && !epi.pool && g.Q % 2 == 0 && a.Wp % 2 == 0 ? 1 : 0;
     const int64_t plane_bytes = bytes_of(a.Hp);
     const int64_t planes = (int64_t)n_images * g.C;
     if (planes * std::max<int64_t>((int64_t)g.H * g.W, (int64_t)g.P * g.Q) >= ((int64_t)1 << 31)) return false;
@@ -314,7 +383,7 @@ bool dw_imp_plan(const Geom& g, const Epi& epi, int n_images, DwImpArgs& a, size
         // every thread the same number of strips where that costs less
         // time per plane: 20 planes of 28 strips take 3 passes of 256
         // threads (2.2 on average), 18 planes take 2
-        const int spp = (epi.pool ? g.Q / 2 : g.Q) * nstrip;
+        const int spp = (epi.pool || a.pairs ? g.Q / 2 : g.Q) * nstrip;
         const int it = (per * spp + kDThreads - 1) / kDThreads;
         const int per2 = (it - 1) * kDThreads / spp;
         if (it > 1 && per2 >= 1 && (int64_t)(it - 1) * per < (int64_t)it * per2) per = per2;
@@ -335,7 +404,8 @@ bool dw_imp_plan(const Geom& g, const Epi& epi, int n_images, DwImpArgs& a, size
     a.fdW = make_fastdiv((uint32_t)g.W);
     a.fdPQo = make_fastdiv((uint32_t)(a.Po * a.Qo));
     a.fdQo = make_fastdiv((uint32_t)a.Qo);
-    a.fdStrip = make_fastdiv((uint32_t)(a.Qo * nstrip));
+    a.fdStrip = make_fastdiv((uint32_t)((a.pairs ? a.Qo / 2 : a.Qo) * nstrip));
+    a.fdQh = make_fastdiv((uint32_t)std::max(a.Qo / 2, 1));
     lds = (size_t)per * plane_bytes;
     grid = (planes + per - 1) / per;
     return true;
@@ -348,6 +418,12 @@ hipError_t launch_dwi(const Geom& g, const void* x, const void* w, const void* b
     size_t lds = 0;
     int64_t grid = 0;
     if (!dw_imp_plan(g, epi, g.N, a, lds, grid)) return hipErrorInvalidValue;
+    if ((uintptr_t)y % (2 * sizeof(TOut)) != 0) {   // pair stores need y aligned to two elements
+        if (a.pairs) {
+            a.pairs = 0;
+            a.fdStrip = make_fastdiv((uint32_t)(a.Qo * ((a.P + kSH - 1) / kSH)));
+        }
+    }
     const bool r3 = g.R == 3 && g.S == 3;
     void (*kfn)(const TIn*, const TIn*, const TIn*, TOut*, DwImpArgs) =
         a.strip ? conv_dw_implicit_kernel<TIn, TOut, 3, 3, true>

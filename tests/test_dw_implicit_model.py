@@ -44,11 +44,13 @@ def plan(N, C, H, W, R, S, sh, sw, ph, pw, dh, dw, pool):
             a["Hp"] = hs
         else:
             a["strip"] = False
+    # two columns a lane (no pool, Qo even)
+    a["pairs"] = a["strip"] and not pool and Q % 2 == 0 and a["Wp"] % 2 == 0
     planes = N * C
     per = min(LDS_BYTES // bytes_of(a["Hp"]), max(1, 16 * THREADS // (H * W)))
     per = max(1, min(per, max(1, planes // 1024)))
     if a["strip"]:
-        spp = (Q // 2 if pool else Q) * nstrip
+        spp = (Q // 2 if pool or a["pairs"] else Q) * nstrip
         it = -(-per * spp // THREADS)
         per2 = (it - 1) * THREADS // spp
         if it > 1 and per2 >= 1 and (it - 1) * per < it * per2:
@@ -115,7 +117,9 @@ def stage(xp, a, np_, fp32):
 
 
 def strip_outputs(lds, wts, bias, a, np_, relu):
-    """Both strip forms over one workgroup's planes; every read bounds-checked."""
+    """The strip forms over one workgroup's planes (pooled, two columns a
+    lane, one column a lane); every read bounds-checked, the pair form's
+    8-byte reads and two-element stores checked for alignment."""
     Hp, Wp, P, Q, Po, Qo = a["Hp"], a["Wp"], a["P"], a["Q"], a["Po"], a["Qo"]
     HpWp = Hp * Wp
     y = np.full((np_, Po, Qo), np.nan)
@@ -125,6 +129,26 @@ def strip_outputs(lds, wts, bias, a, np_, relu):
         return lds[q * HpWp + r * Wp + c]
 
     rows = 2 * KPS if a["pool"] else KSH
+    if a["pairs"]:
+        qh = Qo // 2
+        assert Wp % 2 == 0 and HpWp % 2 == 0 and Qo % 2 == 0 and (P * Qo) % 2 == 0
+        for it in range(np_ * qh * a["nstrip"]):
+            q, r = divmod(it, qh * a["nstrip"])
+            st, cp = divmod(r, qh)
+            oh0 = st * KSH
+            w = wts[q].reshape(3, 3)
+            base = q * HpWp + oh0 * Wp + 2 * cp
+            assert base % 2 == 0                       # 8-byte aligned float2 reads
+            patch = np.array([[rd(q, oh0 + rr, 2 * cp + cc) for cc in range(4)]
+                              for rr in range(rows + 2)])
+            for i in range(KSH):
+                if oh0 + i < P:
+                    assert ((oh0 + i) * Qo + 2 * cp) % 2 == 0   # two-element store aligned
+                    for j in range(2):
+                        v = float(np.sum(patch[i:i + 3, j:j + 3] * w)) + bias[q]
+                        assert np.isnan(y[q, oh0 + i, 2 * cp + j])
+                        y[q, oh0 + i, 2 * cp + j] = max(v, 0.0) if relu else v
+        return y
     per_plane = Qo * a["nstrip"]
     for it in range(np_ * per_plane):
         q, r = divmod(it, per_plane)
@@ -164,6 +188,8 @@ CASES = [
     (1, 2, 6, 6, 0, True, True),        # float4s across row ends, no padding
     (1, 2, 22, 8, 2, False, False),     # strips past P, pad 2
     (1, 1, 70, 70, 1, True, True),      # a plane over two load rounds
+    (1, 3, 10, 11, 1, False, False),    # Q odd: one column a lane
+    (2, 4, 9, 7, 0, False, True),       # Q odd, no padding
 ]
 
 
@@ -192,11 +218,12 @@ def test_strip_model_matches_oracle(case, fp32):
 
 def test_plan_of_the_depthwise_layer():
     """128x512x14x14: 18 planes a workgroup with and without the pool, so
-    every thread computes one pass of strips (252 of 256 threads busy
-    with the pool, 2 strips each without), planes padded to 16 / 18 rows."""
+    every thread computes one pass of strips (252 of 256 threads busy:
+    without the pool a two-column strip each, with it a pooled strip each),
+    planes padded to 16 / 18 rows."""
     a = plan(128, 512, 14, 14, 3, 3, 1, 1, 1, 1, 1, 1, False)
-    assert a["strip"] and a["per"] == 18 and a["Hp"] == 16 and a["vec4"]
-    assert -(-a["per"] * a["Qo"] * a["nstrip"] // THREADS) == 2
+    assert a["strip"] and a["pairs"] and a["per"] == 18 and a["Hp"] == 16 and a["vec4"]
+    assert a["per"] * (a["Qo"] // 2) * a["nstrip"] == 252
     a = plan(128, 512, 14, 14, 3, 3, 1, 1, 1, 1, 1, 1, True)
     assert a["strip"] and a["per"] == 18 and a["Hp"] == 18
     assert a["per"] * a["Qo"] * a["nstrip"] <= THREADS
