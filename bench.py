@@ -15,8 +15,8 @@ kernel's own traced duration beside it (`kernel_only`).  `layers` holds
 every layer of the set, each with
   - the step, back to back (events and wall clock) and traced call by call:
     best and median over --iters calls, warm (back to back) and cold (a
-    1 GiB fill before each call evicts the L2 caches and the 256 MB Infinity
-    Cache), per kernel, kernel sum and call span;
+    read of 1 GiB before each call evicts the L2 caches and the 256 MB
+    Infinity Cache), per kernel, kernel sum and call span;
   - the repack and the contraction on their own, and the in-LDS call
     (CIW_FLAG_IMPLICIT) where the library runs the layer that way, each
     with its roofline (the compute unit is the one the traced kernels run
@@ -474,8 +474,10 @@ def short_name(name: str) -> str:
 def kernel_trace(stream, fn, iters: int, flush=None):
     """`iters` calls of fn on `stream` under torch's profiler (the GPU's own
     kernel timestamps); with `flush` (a >= 512 MB device buffer) each call is
-    preceded by a fill of that buffer on the same stream, which evicts the
-    L2 caches and the 256 MB Infinity Cache (the cold regime).  Returns one
+    preceded, on the same stream, by a read of that whole buffer (a sum),
+    which evicts the L2 caches and the 256 MB Infinity Cache and leaves
+    them holding clean lines (the cold regime: a write would leave dirty
+    lines that the measured call would have to write back).  Returns one
     list per call of (kernel, start_us, duration_us) for this library's
     kernels, in launch order."""
     import torch
@@ -486,7 +488,7 @@ def kernel_trace(stream, fn, iters: int, flush=None):
         for i in range(iters):
             if flush is not None:
                 with torch.cuda.stream(stream):
-                    flush.fill_(i & 255)
+                    flush.view(torch.int32).sum()
             fn()
         torch.cuda.synchronize()
     evs = [e for e in prof.events()
@@ -572,7 +574,7 @@ def implicit_call(step: "Step"):
 
 
 def measure_layer2(L: workloads.Layer, steps: int, warmup: int, iters: int, flush,
-                   epilogue: str = "none") -> tuple:
+                   epilogue: str = "none", trace: bool = True, unfused: bool = True) -> tuple:
     """Every measurement of one layer: the step (repack + contraction) timed
     back to back with HIP events and the wall clock; warm and cold kernel
     traces of the step, of the contraction call and of the in-LDS call; the
@@ -589,15 +591,16 @@ def measure_layer2(L: workloads.Layer, steps: int, warmup: int, iters: int, flus
     def one():
         step.transform()
         step.contract()
-    tw = trace_stats(kernel_trace(step.stream, one, iters))
-    tc = trace_stats(kernel_trace(step.stream, one, iters, flush))
-    res["step"]["warm"] = tw
-    res["step"]["cold"] = tc
-    res["step"]["tflops_best_warm"] = round(fl / (tw["span"]["best_us"] * 1e-6) / 1e12, 3)
-    res["step"]["tflops_best_cold"] = round(fl / (tc["span"]["best_us"] * 1e-6) / 1e12, 3)
+    if trace:
+        tw = trace_stats(kernel_trace(step.stream, one, iters))
+        tc = trace_stats(kernel_trace(step.stream, one, iters, flush))
+        res["step"]["warm"] = tw
+        res["step"]["cold"] = tc
+        res["step"]["tflops_best_warm"] = round(fl / (tw["span"]["best_us"] * 1e-6) / 1e12, 3)
+        res["step"]["tflops_best_cold"] = round(fl / (tc["span"]["best_us"] * 1e-6) / 1e12, 3)
 
     # the repack on its own
-    t_tr = trace_stats(kernel_trace(step.stream, step.transform, iters))
+    t_tr = trace_stats(kernel_trace(step.stream, step.transform, iters)) if trace else None
     res["transform"] = {"call_ms": round(tr_ms, 5), "warm": t_tr,
                         "gbs": round(step.transform_bytes() / (tr_ms * 1e-3) / 1e9, 1),
                         "hbm_frac": round(step.transform_bytes() / (tr_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -605,20 +608,28 @@ def measure_layer2(L: workloads.Layer, steps: int, warmup: int, iters: int, flus
 
     # the contraction on the ready window tensor
     step.transform()
-    cw = trace_stats(kernel_trace(step.stream, step.contract, iters))
-    cc = trace_stats(kernel_trace(step.stream, step.contract, iters, flush))
     cbytes = step.contraction_bytes()
-    roof = roofline_entry(fl, cbytes, L.dtype, cw["dominant"], co_ms)
-    roof["scope"] = "call: " + " + ".join(cw["kernels"]) + " (HIP events around back-to-back calls)"
-    roof["kernel_only"] = roofline_entry(fl, cbytes, L.dtype, cw["dominant"], cw["dominant_us"]["median_us"] * 1e-3)
-    roof["kernel_only"]["kernel"] = cw["dominant"]
-    roof["kernel_only"]["scope"] = "dominant kernel's median traced duration (warm)"
+    if trace:
+        cw = trace_stats(kernel_trace(step.stream, step.contract, iters))
+        cc = trace_stats(kernel_trace(step.stream, step.contract, iters, flush))
+        roof = roofline_entry(fl, cbytes, L.dtype, cw["dominant"], co_ms)
+        roof["scope"] = "call: " + " + ".join(cw["kernels"]) + " (HIP events around back-to-back calls)"
+        roof["kernel_only"] = roofline_entry(fl, cbytes, L.dtype, cw["dominant"], cw["dominant_us"]["median_us"] * 1e-3)
+        roof["kernel_only"]["kernel"] = cw["dominant"]
+        roof["kernel_only"]["scope"] = "dominant kernel's median traced duration (warm)"
+    else:
+        cw = cc = None
+        roof = step.contraction_roofline(co_ms)
     roof["traffic"] = stored_traffic(traffic_key(L, epilogue))
     res["contraction"] = {"call_ms": round(co_ms, 5), "warm": cw, "cold": cc, "roofline": roof}
 
     # the in-LDS call (no window tensor in HBM)
     call, nbytes = implicit_call(step)
-    if call is not None:
+    if call is not None and not trace:
+        ms, wall = loop_ms(step.stream, call, steps, warmup)
+        res["in_lds"] = {"call_ms": round(ms, 5), "wall_ms": round(wall, 5), "workspace_bytes": nbytes,
+                         "tflops": round(fl / (ms * 1e-3) / 1e12, 3)}
+    elif call is not None:
         ms, wall = loop_ms(step.stream, call, steps, warmup)
         iw = trace_stats(kernel_trace(step.stream, call, iters))
         ic = trace_stats(kernel_trace(step.stream, call, iters, flush))
@@ -635,6 +646,10 @@ def measure_layer2(L: workloads.Layer, steps: int, warmup: int, iters: int, flus
                          "roofline": roof}
     if epilogue != "none":
         res["epilogue"] = epilogue
+        res["output_bytes"] = step.bytes_y()
+        if unfused:
+            # context: the plain contraction, then torch's ReLU (and pool)
+            res["unfused_contract_ms"] = round(time_unfused(L, epilogue, steps, warmup), 5)
     return res, step
 
 
@@ -745,6 +760,10 @@ def main():
     ap.add_argument("--epilogue", default="none", choices=EPILOGUES,
                     help="fuse ReLU / ReLU + 2x2 max-pool into the contraction")
     ap.add_argument("--no-memory", action="store_true", help="skip the per-layer memory table")
+    ap.add_argument("--no-trace", action="store_true",
+                    help="skip the kernel traces (for runs under rocprofv3, which traces itself)")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="with --epilogue, skip the unfused comparison")
     ap.add_argument("--miopen", action="store_true",
                     help="add MIOpen's convolution (torch conv2d) to the memory table, as context")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -775,8 +794,8 @@ def main():
         print(json.dumps(ablation_report()), flush=True)
         return
 
-    # 1 GiB evicts the L2 caches and the 256 MB Infinity Cache between calls
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    # reading 1 GiB evicts the L2 caches and the 256 MB Infinity Cache
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
     names = [args.workload] if args.headline_only else \
         [args.workload] + [n for n in workloads.LAYER_ORDER if n != args.workload]
     layers, head_step = {}, None
@@ -785,7 +804,8 @@ def main():
         print(f"# measuring {describe(L)} (epilogue {args.epilogue})", file=sys.stderr, flush=True)
         steps = args.steps if name == args.workload else max(10, args.steps // 5)
         warm = args.warmup if name == args.workload else min(args.warmup, 5)
-        r, st = measure_layer2(L, steps, warm, args.iters, flush, args.epilogue)
+        r, st = measure_layer2(L, steps, warm, args.iters, flush, args.epilogue,
+                               trace=not args.no_trace, unfused=not args.no_unfused)
         k32 = time_fp32_kernels(st, steps, warm)
         if k32 is not None:
             r["fp32_kernels_forced"] = k32
