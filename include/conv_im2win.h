@@ -104,8 +104,12 @@ typedef struct {
 
 /* On-the-fly windows.  conv2d_fwd (fp16/bf16): the contraction kernel
  * builds the window rows of each band of output rows in LDS straight from x
- * and never writes the window tensor to memory; the workspace then holds
- * only a re-laid-out copy of the filter (conv2d_implicit_workspace_bytes).
+ * and never writes the window tensor to memory.  For 3x3 filters with
+ * stride_h 1, C a multiple of 16 up to 64, K <= 64, W a multiple of 8 and
+ * no pool, one kernel does everything, filter re-layout included: no
+ * workspace (0 bytes; workspace may be NULL).  For the other layers it
+ * runs, the workspace holds a re-laid-out copy of the filter
+ * (conv2d_implicit_workspace_bytes gives the size either way).
  * conv2d_dw_fwd (any input type): each workgroup stages whole zero-padded
  * input planes in LDS and computes their outputs there; no workspace
  * (workspace may be NULL).  The result is the same sum in another order
@@ -181,8 +185,9 @@ ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
 /* Workspace conv2d_fwd / conv2d_dw_fwd need with CIW_FLAG_IMPLICIT for this
  * layer, output type and epilogue flags (independent of N).  Depthwise
  * (groups == C == K): 0 bytes; CIW_ERR_UNSUPPORTED if a zero-padded input
- * plane and its filter exceed 48 KB of LDS.  Dense: the re-laid-out filter;
- * CIW_ERR_UNSUPPORTED unless the input is fp16/bf16, groups == 1, C is a
+ * plane and its filter exceed 48 KB of LDS.  Dense: 0 bytes for the layers
+ * the single-kernel form runs (see CIW_FLAG_IMPLICIT), else the re-laid-out
+ * filter; CIW_ERR_UNSUPPORTED unless the input is fp16/bf16, groups == 1, C is a
  * multiple of 16, K <= 64, W a multiple of 8, stride_h == 1, the filter is
  * 3x3 with C <= 64 or 1x1 with C in {16, 32, 64}, a stored output row
  * needs at most 4 stores per thread (K*Qs/E <= 1024, where Qs is Q, or Q/2
