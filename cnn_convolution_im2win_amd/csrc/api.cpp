@@ -221,7 +221,9 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
     const bool ready = (flags & CIW_FLAG_WINDOW_READY) != 0;
     size_t imp_need = 0;   // workspace of the in-LDS kernels (may be 0: then ws may be NULL)
     if (implicit) {
-        if (in == CIW_F32 || !implicit_workspace(g, out, epi, &imp_need)) return CIW_ERR_UNSUPPORTED;
+        const bool ok = in == CIW_F32 ? fp32_implicit_workspace(g, epi, &imp_need)
+                                      : implicit_workspace(g, out, epi, &imp_need);
+        if (!ok) return CIW_ERR_UNSUPPORTED;
     }
     const bool ws_needed = !noalloc && !(implicit && imp_need == 0);
     if ((!ready && !x) || !w || !y || (!ws && ws_needed)) return CIW_ERR_INVALID_ARG;
@@ -235,6 +237,9 @@ ciw_status run_conv(const ciw_conv_desc* desc, ciw_dtype in, ciw_dtype out, cons
         if (ws_bytes < imp_need) return CIW_ERR_WORKSPACE;
         if (noalloc && imp_need > 0 && (s = scratch_of_current_device(&ws)) != CIW_OK) return s;
         (void)hipGetLastError();
+        if (in == CIW_F32)
+            return from_hip(launch_conv_fp32_implicit(g, (const float*)x, (const float*)w, (const float*)bias,
+                                                      (float*)y, (float*)ws, epi, (hipStream_t)stream));
         return from_hip(launch_conv_implicit(g, in, out, x, w, bias, y, ws, epi, (hipStream_t)stream));
     }
 
@@ -413,7 +418,9 @@ ciw_status conv2d_implicit_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype 
         return CIW_OK;
     }
     size_t need = 0;
-    if (in_dtype == CIW_F32 || !implicit_workspace(g, out_dtype, epi, &need)) return CIW_ERR_UNSUPPORTED;
+    const bool ok = in_dtype == CIW_F32 ? fp32_implicit_workspace(g, epi, &need)
+                                        : implicit_workspace(g, out_dtype, epi, &need);
+    if (!ok) return CIW_ERR_UNSUPPORTED;
     *bytes = need;
     return CIW_OK;
 }

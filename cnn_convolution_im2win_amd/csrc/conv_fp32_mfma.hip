@@ -36,6 +36,7 @@ constexpr int kMT = 32;          // output channels per workgroup
 constexpr int kTC = 64;          // input channels per slice (at most)
 constexpr int kCh = 16;          // channels per LDS chunk (two pairs per quarter)
 constexpr int kMaxB = 6;         // window float4 loads per thread per chunk
+constexpr int kMaxBI = 10;       // in-LDS form: input elements per thread per chunk
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -49,9 +50,19 @@ struct F32MArgs {
     int BS;          // LDS stride between staged channels of the window (floats)
     int ntask, nimg;
     int relu;
+    // in-LDS form: the block's input rows staged from x, zero-padded
+    int H, W, sh, ph, pw, dh;
+    int Hr, Wpl;     // staged rows and columns per channel
+    int nBI;         // staged elements per chunk (kCh * Hr * Wpl)
 };
 
-template <int R, int S>
+// IMP: the in-LDS form.  xw is then x itself, and a chunk stages, per
+// channel, the zero-padded input rows h0 * stride_h - pad_h .. of its pixel
+// block ([Hr][Wpl] with Wpl the padded columns the windows touch) instead of
+// the block's window rows; the window of output (h, w) at tap (r, q) is the
+// staged element (h * stride_h + r * dil_h, w * stride_w + q * dil_w).  The
+// window tensor is never written.
+template <int R, int S, bool IMP>
 __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
     const float* __restrict__ xw, const float* __restrict__ w, const float* __restrict__ bias,
     float* __restrict__ out, F32MArgs a) {
@@ -99,13 +110,32 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
     const int run4 = rows * a.pitch / 4;         // float4 per channel (pitch is a multiple of 4)
     const int nB4 = kCh * run4;
     const int kBL = (nB4 + kMThreads - 1) / kMThreads;          // window loads per thread (<= kMaxB)
+    // in-LDS form: a thread's staged elements are the same positions in
+    // every chunk (only the channel base moves), so each one's source offset
+    // within its channel's plane (-1: zero padding), channel and LDS offset
+    // are worked out once
+    int bi_src[IMP ? kMaxBI : 1], bi_cl[IMP ? kMaxBI : 1], bi_dst[IMP ? kMaxBI : 1];
+    if constexpr (IMP) {
+        const int per_ch = a.Hr * a.Wpl;
+#pragma unroll
+        for (int u = 0; u < kMaxBI; ++u) {
+            const int e = tid + u * kMThreads;
+            const int cl = e / per_ch, rr = e - cl * per_ch;
+            const int y = rr / a.Wpl, xx = rr - y * a.Wpl;
+            const int iy = h0 * a.sh - a.ph + y, ix = xx - a.pw;
+            bi_cl[u] = e < a.nBI ? cl : kCh;             // kCh: nothing to stage
+            bi_src[u] = (iy >= 0 && iy < a.H && ix >= 0 && ix < a.W) ? iy * a.W + ix : -1;
+            bi_dst[u] = cl * a.BS + y * a.Wpl + xx;
+        }
+    }
     struct Fetched {
         float ra[kAL];
-        float4 rb[kMaxB];
+        float4 rb[IMP ? 1 : kMaxB];
+        float rbi[IMP ? kMaxBI : 1];
     };
     auto fetch = [&](Fetched& f, int ch) {
         float (&ra)[kAL] = f.ra;
-        float4 (&rb)[kMaxB] = f.rb;
+        auto& rb = f.rb;
         const int cc = c0 + ch * kCh;            // first channel of the chunk
         const int nc = min(kCh, c0 + tc - cc);   // channels present
 #pragma unroll
@@ -116,19 +146,30 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
             if (e < kMT * T && k0 + row < a.K && t < nc * RS)
                 ra[u] = w[((size_t)(k0 + row) * a.C + cc) * RS + t];
         }
+        if constexpr (IMP) {
+            const float* xc = xw + ((size_t)n_img * a.C + cc) * ((size_t)a.H * a.W);
 #pragma unroll
-        for (int u = 0; u < kMaxB; ++u) {
-            const int e = tid + u * kMThreads;
-            const int cl = e / run4, o = (e - cl * run4) * 4;
-            rb[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (u < kBL && e < nB4 && cl < nc)
-                rb[u] = *reinterpret_cast<const float4*>(
-                    xw + (((size_t)n_img * a.C + cc + cl) * a.P + h0) * a.pitch + o);
+            for (int u = 0; u < kMaxBI; ++u) {
+                f.rbi[u] = 0.f;
+                if (bi_cl[u] < nc && bi_src[u] >= 0)
+                    f.rbi[u] = xc[(size_t)bi_cl[u] * a.H * a.W + bi_src[u]];
+            }
+            return;
+        } else {
+#pragma unroll
+            for (int u = 0; u < kMaxB; ++u) {
+                const int e = tid + u * kMThreads;
+                const int cl = e / run4, o = (e - cl * run4) * 4;
+                rb[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (u < kBL && e < nB4 && cl < nc)
+                    rb[u] = *reinterpret_cast<const float4*>(
+                        xw + (((size_t)n_img * a.C + cc + cl) * a.P + h0) * a.pitch + o);
+            }
         }
     };
     auto stash = [&](const Fetched& f, int buf) {
         const float (&ra)[kAL] = f.ra;
-        const float4 (&rb)[kMaxB] = f.rb;
+        const auto& rb = f.rb;
         float* As = smem + buf * chunk_floats;
         float* Bs = As + kMT * a.AS;
 #pragma unroll
@@ -137,11 +178,17 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
             const int row = e / T, t = e - row * T;
             if (e < kMT * T) As[row * a.AS + t] = ra[u];
         }
+        if constexpr (IMP) {
 #pragma unroll
-        for (int u = 0; u < kMaxB; ++u) {
-            const int e = tid + u * kMThreads;
-            const int cl = e / run4, o = (e - cl * run4) * 4;
-            if (u < kBL && e < nB4) *reinterpret_cast<float4*>(Bs + cl * a.BS + o) = rb[u];
+            for (int u = 0; u < kMaxBI; ++u)
+                if (bi_cl[u] < kCh) Bs[bi_dst[u]] = f.rbi[u];
+        } else {
+#pragma unroll
+            for (int u = 0; u < kMaxB; ++u) {
+                const int e = tid + u * kMThreads;
+                const int cl = e / run4, o = (e - cl * run4) * 4;
+                if (u < kBL && e < nB4) *reinterpret_cast<float4*>(Bs + cl * a.BS + o) = rb[u];
+            }
         }
     };
 
@@ -151,13 +198,13 @@ __global__ __launch_bounds__(kMThreads, 1) void conv_fp32_mfma_kernel(
         // pixels past the block read its last pixel (never stored)
         const int px = min((3 * pg + t3) * 32 + j, npx - 1);
         const int hh = px / a.Q, ww = px - hh * a.Q;
-        pxoff[t3] = hh * a.pitch + ww * a.sw * R;
+        pxoff[t3] = IMP ? hh * a.sh * a.Wpl + ww * a.sw : hh * a.pitch + ww * a.sw * R;
     }
     int toff[RS];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int q = 0; q < S; ++q) toff[r * S + q] = q * a.dw * R + r;
+        for (int q = 0; q < S; ++q) toff[r * S + q] = IMP ? r * a.dh * a.Wpl + q * a.dw : q * a.dw * R + r;
     f32x16 acc[3];
 #pragma unroll
     for (int t3 = 0; t3 < 3; ++t3)
@@ -292,8 +339,10 @@ struct F32MPlan {
 };
 
 // Layers this kernel runs: fp32, 3x3 or 1x1 filters, an output row of at
-// most 192 pixels, and the staged slice within 160 KB of LDS.
-bool f32m_plan(const Geom& g, int n_images, F32MPlan& pl) {
+// most 192 pixels, and the staged slice within 160 KB of LDS.  imp: the
+// in-LDS form (a chunk's zero-padded input rows at most kMaxBI elements a
+// thread).
+bool f32m_plan(const Geom& g, int n_images, F32MPlan& pl, bool imp = false) {
     if (!((g.R == 3 && g.S == 3) || (g.R == 1 && g.S == 1))) return false;
     if (g.Q > kMaxPix || g.C < 2) return false;
     F32MArgs& a = pl.a;
@@ -312,9 +361,22 @@ bool f32m_plan(const Geom& g, int n_images, F32MPlan& pl) {
     a.TC = tc;
     a.splits = (g.C + tc - 1) / tc;
     a.AS = kCh * RS + 1;                         // odd stride: lanes of a fragment in distinct banks
-    a.BS = a.HB * g.pitchA + 4;
-    // window float4 loads per thread per chunk
-    if ((kCh * (a.HB * g.pitchA / 4) + kMThreads - 1) / kMThreads > kMaxB) return false;
+    a.H = g.H; a.W = g.W; a.sh = g.sh; a.ph = g.ph; a.pw = g.pw; a.dh = g.dh;
+    if (imp) {
+        // the input rows a pixel block's windows span, and the padded columns
+        const int64_t hr = (int64_t)(a.HB - 1) * g.sh + (int64_t)(g.R - 1) * g.dh + 1;
+        const int64_t per_ch = hr * g.Wwin;
+        if (kCh * per_ch > (int64_t)kMaxBI * kMThreads) return false;
+        a.Hr = (int)hr;
+        a.Wpl = g.Wwin;
+        a.BS = (int)per_ch + 4;
+        a.nBI = (int)(kCh * per_ch);
+    } else {
+        a.Hr = a.Wpl = a.nBI = 0;
+        a.BS = a.HB * g.pitchA + 4;
+        // window float4 loads per thread per chunk
+        if ((kCh * (a.HB * g.pitchA / 4) + kMThreads - 1) / kMThreads > kMaxB) return false;
+    }
     const int64_t ntask = others * a.splits;
     if (ntask >= (1ll << 31)) return false;
     a.ntask = (int)ntask;
@@ -323,6 +385,27 @@ bool f32m_plan(const Geom& g, int n_images, F32MPlan& pl) {
     const size_t red = (size_t)4 * 2 * 4 * 3 * 4 * 64 * 4;   // [4][2][4][3][4][64] floats
     pl.lds = std::max(staged, red);
     return pl.lds <= 160 * 1024;
+}
+
+// The contraction kernel (window rows from xw, or the in-LDS form from x),
+// then the slice reduction when the channel sum is split.
+hipError_t launch_f32m(const Geom& g, const F32MPlan& pl, const float* src, const float* w,
+                       const float* bias, float* y, int n_images, float* partials, const Epi& epi,
+                       hipStream_t st, bool imp) {
+    void (*kfn)(const float*, const float*, const float*, float*, F32MArgs) =
+        imp ? (g.R == 3 ? conv_fp32_mfma_kernel<3, 3, true> : conv_fp32_mfma_kernel<1, 1, true>)
+            : (g.R == 3 ? conv_fp32_mfma_kernel<3, 3, false> : conv_fp32_mfma_kernel<1, 1, false>);
+    if (pl.lds > 65536 && allow_dynamic_lds(reinterpret_cast<const void*>(kfn), pl.lds) != hipSuccess)
+        return hipErrorInvalidValue;
+    float* dst = pl.a.splits == 1 ? y : partials;
+    hipLaunchKernelGGL(kfn, dim3((uint32_t)pl.a.ntask), dim3(kMThreads), pl.lds, st, src, w, bias, dst, pl.a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || pl.a.splits == 1) return e;
+    const int64_t per_split = (int64_t)n_images * g.K * g.P * g.Q;
+    hipLaunchKernelGGL(split_reduce_nkp_kernel, dim3((uint32_t)((per_split + 255) / 256)), dim3(256), 0,
+                       st, partials, bias, y, (uint32_t)per_split, pl.a.splits, g.P * g.Q, g.K,
+                       (int)epi.relu);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -339,19 +422,24 @@ hipError_t launch_conv_fp32_mfma(const Geom& g, const float* xw, const float* w,
     if (n_images == 0) return hipSuccess;
     if (epi.pool || !f32m_plan(g, n_images, pl) || pl.a.splits > max_splits) return hipErrorNotSupported;
     pl.a.relu = epi.relu;
-    void (*kfn)(const float*, const float*, const float*, float*, F32MArgs) =
-        g.R == 3 ? conv_fp32_mfma_kernel<3, 3> : conv_fp32_mfma_kernel<1, 1>;
-    if (pl.lds > 65536 && allow_dynamic_lds(reinterpret_cast<const void*>(kfn), pl.lds) != hipSuccess)
-        return hipErrorInvalidValue;
-    float* dst = pl.a.splits == 1 ? y : partials;
-    hipLaunchKernelGGL(kfn, dim3((uint32_t)pl.a.ntask), dim3(kMThreads), pl.lds, st, xw, w, bias, dst, pl.a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || pl.a.splits == 1) return e;
-    const int64_t per_split = (int64_t)n_images * g.K * g.P * g.Q;
-    hipLaunchKernelGGL(split_reduce_nkp_kernel, dim3((uint32_t)((per_split + 255) / 256)), dim3(256), 0,
-                       st, partials, bias, y, (uint32_t)per_split, pl.a.splits, g.P * g.Q, g.K,
-                       (int)epi.relu);
-    return hipGetLastError();
+    return launch_f32m(g, pl, xw, w, bias, y, n_images, partials, epi, st, false);
+}
+
+bool fp32_implicit_workspace(const Geom& g, const Epi& epi, size_t* bytes) {
+    F32MPlan pl;
+    if (epi.pool || !f32m_plan(g, std::max(g.N, 1), pl, true)) return false;
+    const int64_t per_split = (int64_t)std::max(g.N, 1) * g.K * g.P * g.Q;
+    *bytes = pl.a.splits > 1 ? (size_t)pl.a.splits * (size_t)per_split * sizeof(float) : 0;
+    return true;
+}
+
+hipError_t launch_conv_fp32_implicit(const Geom& g, const float* x, const float* w, const float* bias,
+                                     float* y, float* partials, const Epi& epi, hipStream_t st) {
+    F32MPlan pl;
+    if (g.N == 0) return hipSuccess;
+    if (epi.pool || !f32m_plan(g, g.N, pl, true)) return hipErrorNotSupported;
+    pl.a.relu = epi.relu;
+    return launch_f32m(g, pl, x, w, bias, y, g.N, partials, epi, st, true);
 }
 
 }  // namespace ciw

@@ -117,6 +117,13 @@ hipError_t launch_conv_mfma(const Geom& g, ciw_dtype in, ciw_dtype out, const vo
 // kernel (3x3, no pool), else the re-laid-out filter, which
 // launch_conv_implicit writes before the contraction.
 bool implicit_workspace(const Geom& g, ciw_dtype out, const Epi& epi, size_t* bytes);
+// fp32 dense in-LDS form of the matrix-core contraction (no pool): the
+// zero-padded input rows of each pixel block staged in LDS straight from x.
+// Its workspace holds only the channel slices' partial sums (0 bytes when
+// the channel sum is not split); false for layers it does not run.
+bool fp32_implicit_workspace(const Geom& g, const Epi& epi, size_t* bytes);
+hipError_t launch_conv_fp32_implicit(const Geom& g, const float* x, const float* w, const float* bias,
+                                     float* y, float* partials, const Epi& epi, hipStream_t st);
 hipError_t launch_conv_implicit(const Geom& g, ciw_dtype in, ciw_dtype out, const void* x,
                                 const void* w, const void* bias, void* y, void* ws,
                                 const Epi& epi, hipStream_t st);

@@ -164,9 +164,12 @@ def test_unknown_flags():
 
 
 def test_implicit_flag_host_checks():
-    # fp32 has no in-LDS window kernel; the flag combinations it forbids
-    assert call_fwd(valid_desc(), ws_bytes=1 << 30, flags=_lib.CIW_FLAG_IMPLICIT) == \
-        _lib.CIW_ERR_UNSUPPORTED
+    # fp32 in LDS has no pooled form and runs only 3x3 and 1x1 filters (both
+    # refused before any launch); the flag combinations it forbids
+    pooled = _lib.CIW_FLAG_IMPLICIT | _lib.CIW_FLAG_MAXPOOL2
+    assert call_fwd(valid_desc(), ws_bytes=1 << 30, flags=pooled) == _lib.CIW_ERR_UNSUPPORTED
+    assert call_fwd(valid_desc(R=5, S=5, pad_h=2, pad_w=2), ws_bytes=1 << 30,
+                    flags=_lib.CIW_FLAG_IMPLICIT) == _lib.CIW_ERR_UNSUPPORTED
     both = _lib.CIW_FLAG_IMPLICIT | _lib.CIW_FLAG_WINDOW_READY
     assert call_fwd(valid_desc(), ws_bytes=1 << 30, flags=both) == _lib.CIW_ERR_INVALID_ARG
 

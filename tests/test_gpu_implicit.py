@@ -205,7 +205,8 @@ def test_errors():
     assert st(IMP, C=24) == ciw._lib.CIW_ERR_UNSUPPORTED
     assert st(IMP, W=52) == ciw._lib.CIW_ERR_UNSUPPORTED
     assert st(IMP, sh=2) == ciw._lib.CIW_ERR_UNSUPPORTED
-    assert st(IMP, dtype=torch.float32) == ciw._lib.CIW_ERR_UNSUPPORTED
+    assert st(IMP, dtype=torch.float32) == 0             # fp32: the matrix-core in-LDS form
+    assert st(IMP | ciw.CIW_FLAG_MAXPOOL2, dtype=torch.float32) == ciw._lib.CIW_ERR_UNSUPPORTED
     assert st(IMP | ciw.CIW_FLAG_WINDOW_READY) == ciw._lib.CIW_ERR_INVALID_ARG
     assert st(IMP | ciw.CIW_FLAG_GENERIC) == ciw._lib.CIW_ERR_INVALID_ARG
     assert st(IMP, groups=64) == 0                       # depthwise: windows in LDS too
@@ -213,6 +214,77 @@ def test_errors():
     # the row-band kernel, whose re-laid-out filter does not fit in 1 KB
     assert st(IMP, ws_bytes=16) == 0
     assert st(IMP | ciw.CIW_FLAG_MAXPOOL2, ws_bytes=1024) == ciw._lib.CIW_ERR_WORKSPACE
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ fp32 dense
+MID = workloads.LAYERS["mid_3x3_fp32"]
+
+
+def run_materialised_matrix(L, x, w, b, relu=False):
+    """The same layer through the window tensor, the fp32 matrix-core kernel forced."""
+    flags = ciw.CIW_FLAG_FP32_MFMA | (ciw.CIW_FLAG_RELU if relu else 0)
+    return run(L, x, w, b, flags=flags)
+
+
+@pytest.mark.parametrize("relu", [False, True])
+def test_mid_layer_fp32_in_lds_every_output(relu):
+    """The 1x512x13x13 -> 1024 layer in full: every output against the
+    oracle, and bit for bit against the materialised path on the same
+    kernel (same products, same channel slices, same summation order)."""
+    L = MID
+    say(f"fp32 in-LDS: {L.name} relu={relu}")
+    x, w, b = workloads.make_inputs(L)
+    flags = IMP | (ciw.CIW_FLAG_RELU if relu else 0)
+    y = run(L, x, w, b, flags=flags)
+    got = to_host_f64(y)
+    ref = oracle.conv2d(f64(x, "f32"), f64(w, "f32"), f64(b, "f32"), L.stride, L.pad, L.dil, 1)
+    if relu:
+        ref = oracle.relu_pool(ref, relu=True, pool=False)
+    e = rel_err(got, ref)
+    say(f"  rel err {e:.3e}")
+    assert got.shape == ref.shape and np.all(np.isfinite(got)) and e <= TOL["f32"]
+    ym = run_materialised_matrix(L, x, w, b, relu=relu)
+    assert torch.equal(y, ym)
+
+
+FP32_SHAPES = [
+    # N, C, H, W, K, R, stride, pad, dil
+    (1, 16, 32, 32, 32, 3, 1, 1, 1),       # the 1x16x32x32 -> 32 layer's geometry: several pixel blocks
+    (2, 20, 9, 11, 5, 3, (2, 1), 0, 1),    # stride_h 2, ragged last chunk, K < 32
+    (1, 18, 10, 12, 40, 3, (1, 2), 2, 2),  # stride_w 2, dilation 2, padding 2, K not a multiple of 32
+    (3, 33, 7, 7, 70, 1, 1, 0, 1),         # 1x1, odd C
+    (2, 64, 8, 56, 64, 3, 1, 1, 1),        # three pixel blocks of 3 rows
+    (1, 48, 5, 100, 8, 3, 1, 1, 1),        # 100-pixel rows: one row a block
+]
+
+
+@pytest.mark.parametrize("shape", FP32_SHAPES)
+def test_fp32_in_lds_shapes_against_oracle(shape):
+    N, C, H, W, K, R, stride, pad, dil = shape
+    L = MID.replace(name="fp32_shape", N=N, C=C, H=H, W=W, K=K, R=R, S=R,
+                    stride=stride if isinstance(stride, tuple) else (stride, stride),
+                    pad=(pad, pad), dil=(dil, dil), seed=sum(shape[:6]))
+    say(f"fp32 in-LDS shape {shape}")
+    x, w, b = workloads.make_inputs(L)
+    got = to_host_f64(run(L, x, w, b))
+    ref = oracle.conv2d(f64(x, "f32"), f64(w, "f32"), f64(b, "f32"), L.stride, L.pad, L.dil, 1)
+    e = rel_err(got, ref)
+    say(f"  rel err {e:.3e}")
+    assert got.shape == ref.shape and np.all(np.isfinite(got)) and e <= TOL["f32"]
+
+
+def test_fp32_in_lds_workspace():
+    """The workspace holds only the channel slices' partial sums: 8 slices
+    of the 1x512x13x13 -> 1024 output; too small a workspace is refused."""
+    d = ciw.make_desc(MID.x_shape, MID.w_shape, MID.stride, MID.pad, MID.dil, 1)
+    nbytes = ciw.conv2d_implicit_workspace_bytes(d, ciw.CIW_F32, ciw.CIW_F32, IMP)
+    assert nbytes == 8 * 1024 * 13 * 13 * 4
+    x, w, b = (to_dev(a, "f32") for a in workloads.make_inputs(MID))
+    y = torch.empty((1, 1024, 13, 13), dtype=torch.float32, device="cuda")
+    ws = torch.empty(nbytes - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ciw.Im2winError):
+        ciw.conv2d_fwd(x, w, b, y, ws, MID.stride, MID.pad, MID.dil, flags=IMP)
     torch.cuda.synchronize()
 
 
