@@ -392,7 +392,7 @@ inline bool band_plan(const Geom& g, int out_bytes, const Epi& epi, int cus, Ban
     if (g.R != 3 || g.S != 3 || g.C % 16 != 0 || g.C > 64 || g.K > 64 || g.W % 8 != 0 || g.sh != 1 || epi.pool)
         return false;
     if ((int64_t)g.C * g.H * g.W >= ((int64_t)1 << 31)) return false;         // 32-bit offsets in an image
-    if ((int64_t)g.K * g.P * g.Q >= ((int64_t)1 << 31)) return false;
+    if ((int64_t)g.K * g.P * g.Q * out_bytes >= ((int64_t)1 << 32)) return false;   // byte offsets in an image of y
     BandArgs& a = pl.a;
     a.C = g.C; a.K = g.K; a.H = g.H; a.W = g.W; a.P = g.P; a.Q = g.Q;
     a.sw = g.sw; a.ph = g.ph; a.pw = g.pw; a.dh = g.dh; a.dw = g.dw;

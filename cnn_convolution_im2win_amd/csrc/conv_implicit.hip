@@ -2,7 +2,8 @@
 // their window rows in LDS from x: the band kernel (conv_band_impl.hpp: 3x3
 // filters, no pool; no workspace) where it runs the layer, otherwise the
 // row-band kernel of conv_implicit_impl.hpp (workspace: the re-laid-out
-// filter, written by a kernel before the contraction).  Eligibility,
+// filter, written by a kernel before the contraction), otherwise the
+// few-channel kernel of conv_narrow_impl.hpp (no workspace).  Eligibility,
 // workspace and dispatch by input type to the per-type files.
 #include "conv_band_impl.hpp"
 
@@ -33,8 +34,12 @@ bool implicit_workspace(const Geom& g, ciw_dtype out, const Epi& epi, size_t* by
         return true;
     }
     MfImpPlan pl;
-    if (!mf_imp_plan(g, elem_bytes(out), epi, 256, pl)) return false;
-    *bytes = (size_t)2 * pl.steps * 512 * sizeof(uint16_t);
+    if (mf_imp_plan(g, elem_bytes(out), epi, 256, pl)) {
+        *bytes = (size_t)2 * pl.steps * 512 * sizeof(uint16_t);
+        return true;
+    }
+    if (!narrow_supported(g, out, epi)) return false;
+    *bytes = 0;
     return true;
 }
 
@@ -48,7 +53,8 @@ hipError_t launch_conv_implicit(const Geom& g, ciw_dtype in, ciw_dtype out, cons
                              : launch_conv_band_bf16(g, out, x, w, bias, y, epi, st);
     }
     MfImpPlan pl;
-    if (!mf_imp_plan(g, elem_bytes(out), epi, 256, pl)) return hipErrorInvalidValue;
+    if (!mf_imp_plan(g, elem_bytes(out), epi, 256, pl))
+        return launch_conv_narrow(g, in, out, x, w, bias, y, epi, st);
     ImpPermArgs p;
     p.C = g.C; p.K = g.K; p.R = g.R; p.S = g.S; p.CB = pl.CB; p.steps = pl.steps;
     p.total = (uint32_t)(2 * pl.steps * 512);

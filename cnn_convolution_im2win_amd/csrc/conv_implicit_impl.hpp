@@ -90,7 +90,7 @@ struct ImpPermArgs {
     uint32_t total;      // 2 * steps * 512
 };
 
-__global__ __launch_bounds__(kThreads) void mfma_implicit_filter_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((unused)) void mfma_implicit_filter_kernel(
     const uint16_t* __restrict__ w, uint16_t* __restrict__ aperm, ImpPermArgs p) {
     const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
     if (i >= p.total) return;

@@ -910,7 +910,7 @@ struct PermArgs {
     uint32_t total;                // nph * 2 * steps * 512
 };
 
-__global__ __launch_bounds__(kThreads) void mfma_filter_perm_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((unused)) void mfma_filter_perm_kernel(
     const uint16_t* __restrict__ w, uint16_t* __restrict__ aperm, PermArgs p) {
     const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
     if (i >= p.total) return;
@@ -955,7 +955,7 @@ int gcd_int(int x, int y) {
 // fits without the epilogue decides whether the filter is re-laid out, so
 // an epilogue may only turn a fitting plan down (to the generic kernel),
 // never accept one the plain plan rejects.
-bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl, const Epi& epi = Epi{}) {
+[[maybe_unused]] bool mf_row_plan(const Geom& g, int out_bytes, MfRowPlan& pl, const Epi& epi = Epi{}) {
     if (g.K > 64 || g.dw != 1) return false;
     MfRowArgs& a = pl.a;
     // window start stride and length in elements, in 64 bits (a huge

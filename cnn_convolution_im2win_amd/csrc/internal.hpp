@@ -114,8 +114,9 @@ hipError_t launch_conv_mfma(const Geom& g, ciw_dtype in, ciw_dtype out, const vo
 // fp16/bf16 dense contraction that builds its window rows in LDS from x
 // (no window tensor in memory).  implicit_workspace is false for layers no
 // such kernel runs; otherwise *bytes is the workspace: 0 for the band
-// kernel (3x3, no pool), else the re-laid-out filter, which
-// launch_conv_implicit writes before the contraction.
+// kernel (3x3, no pool) and for the few-channel kernel below, else the
+// re-laid-out filter of the row-band kernel, which launch_conv_implicit
+// writes before the contraction.
 bool implicit_workspace(const Geom& g, ciw_dtype out, const Epi& epi, size_t* bytes);
 // fp32 dense in-LDS form of the matrix-core contraction (no pool): the
 // zero-padded input rows of each pixel block staged in LDS straight from x.
@@ -127,6 +128,14 @@ hipError_t launch_conv_fp32_implicit(const Geom& g, const float* x, const float*
 hipError_t launch_conv_implicit(const Geom& g, ciw_dtype in, ciw_dtype out, const void* x,
                                 const void* w, const void* bias, void* y, void* ws,
                                 const Epi& epi, hipStream_t st);
+// fp16/bf16 dense in-LDS form for layers with few input channels and an
+// even horizontal stride (C R <= 22, stride_w even, dil_w 1, no pool: the
+// 3-channel 7x7 stride-2 stem).  No workspace; implicit_workspace and
+// launch_conv_implicit take it for the layers the two kernels above do not
+// run.
+bool narrow_supported(const Geom& g, ciw_dtype out, const Epi& epi);
+hipError_t launch_conv_narrow(const Geom& g, ciw_dtype in, ciw_dtype out, const void* x, const void* w,
+                              const void* bias, void* y, const Epi& epi, hipStream_t st);
 
 // Depthwise convolution with the windows built in LDS from x (no window
 // tensor, no workspace); dw_implicit_supported is false when a padded

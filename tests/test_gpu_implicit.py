@@ -288,6 +288,106 @@ def test_fp32_in_lds_workspace():
     torch.cuda.synchronize()
 
 
+# ------------------------------------------------------------ few input channels
+STEM = workloads.LAYERS["stem_7x7_s2_bf16"]
+
+
+def test_stem_full_size_every_output():
+    """The 128x3x224x224 -> 64 7x7 stride-2 layer in the launch configuration
+    the benchmark times (bands of 28 rows, 7 steps of 4): every output
+    against the oracle, and against the materialised path."""
+    L = STEM
+    say("few-channel in-LDS: stem full size, every output")
+    x, w, b = workloads.make_inputs(L)
+    y = run(L, x, w, b)
+    got = to_host_f64(y)
+    ref = oracle.conv2d(f64(x, "bf16"), f64(w, "bf16"), f64(b, "bf16"), L.stride, L.pad, L.dil, 1)
+    check(got, ref, "stem full size")
+    explicit = to_host_f64(run(L, x, w, b, flags=0))
+    check(got, explicit, "against the materialised path")
+
+
+@pytest.mark.parametrize("n", [1, 24])
+def test_stem_reduced_batch_every_output(n):
+    """One image (bands of one row) and 24 images (bands of 5 rows: a step
+    of 4 rows, then one of 1)."""
+    L = STEM.replace(N=n, seed=30 + n)
+    say(f"few-channel in-LDS: stem N={n}, every output")
+    x, w, b = workloads.make_inputs(L)
+    got = to_host_f64(run(L, x, w, b))
+    ref = oracle.conv2d(f64(x, "bf16"), f64(w, "bf16"), f64(b, "bf16"), L.stride, L.pad, L.dil, 1)
+    check(got, ref, f"N={n}")
+
+
+# (N, C, H, W, K, R, S, stride, pad, dil_h): filter halves, ragged blocks and
+# steps, both strip alignments (d = 0, 1), trailing-entry masks, stride and
+# dilation, and each store form (staged runs, 4-pixel runs, single pixels)
+NARROW_SHAPES = [
+    (2, 3, 23, 40, 40, 7, 7, (2, 2), (3, 3), 1),    # Q = 20: 4-pixel stores for 16-bit outputs
+    (1, 2, 30, 64, 24, 5, 5, (1, 2), (2, 2), 1),    # 5x5 (d = 0, three trailing entries), K <= 32
+    (1, 4, 26, 32, 33, 5, 6, (3, 2), (1, 1), 2),    # S = 6, stride_h 3, dil_h 2, Q = 15: single pixels
+    (1, 1, 17, 16, 8, 7, 7, (2, 4), (0, 3), 1),     # one channel, stride_w 4, no row padding
+    (2, 3, 12, 8, 64, 3, 7, (2, 2), (1, 5), 1),     # pad_w 5 (L = 8), 9 pairs: the 6-step form
+    (40, 3, 64, 64, 64, 7, 7, (2, 2), (3, 3), 1),   # bands of 3 rows (the last of 2), 32-pixel rows
+    (128, 3, 64, 256, 48, 7, 7, (2, 2), (3, 3), 1),  # bands of 8 rows: two steps of 4 through the ring
+]
+
+
+@pytest.mark.parametrize("shape", NARROW_SHAPES)
+@pytest.mark.parametrize("dtype,out", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"), ("f16", "f32")])
+def test_narrow_shapes_against_oracle(shape, dtype, out):
+    N, C, H, W, K, R, S, stride, pad, dh = shape
+    L = STEM.replace(name="narrow", N=N, C=C, H=H, W=W, K=K, R=R, S=S, stride=stride, pad=pad,
+                     dil=(dh, 1), dtype=dtype, out_dtype=out, x_dist=("normal", 0.0, 1.0),
+                     b_dist=("uniform", -0.1, 0.1), seed=sum(shape[:7]))
+    say(f"few-channel in-LDS {shape} {dtype}->{out}")
+    x, w, b = workloads.make_inputs(L)
+    got = to_host_f64(run(L, x, w, b))
+    ref = oracle.conv2d(f64(x, dtype), f64(w, dtype), f64(b, dtype), L.stride, L.pad, L.dil, 1)
+    check(got, ref, f"{shape} {dtype}->{out}")
+
+
+def test_stem_relu_no_bias():
+    L = STEM.replace(N=3, seed=41)
+    x, w, _ = workloads.make_inputs(L)
+    got = to_host_f64(run(L, x, w, None, flags=IMP | ciw.CIW_FLAG_RELU))
+    conv = oracle.conv2d(f64(x, "bf16"), f64(w, "bf16"), None, L.stride, L.pad, L.dil, 1)
+    check(got, oracle.relu_pool(conv, relu=True, pool=False), "relu")
+    assert np.all(got >= 0)
+
+
+def test_stem_non_finite_inputs_stay_in_their_windows():
+    """Infinities and a NaN in x reach exactly the outputs whose windows
+    hold them: a strip's entries from other windows are masked, so they
+    never meet a zero filter tap (0 x Inf)."""
+    L = STEM.replace(N=2, H=40, W=48, seed=43)
+    x, w, b = workloads.make_inputs(L)
+    x = x.copy()
+    # bf16 bit patterns: +Inf, -Inf, +Inf, NaN
+    for (n, c, h, col), v in (((0, 0, 3, 10), 0x7F80), ((0, 1, 17, 33), 0xFF80),
+                              ((1, 2, 39, 47), 0x7F80), ((1, 1, 0, 0), 0x7FC0)):
+        x[n, c, h, col] = v
+    got = to_host_f64(run(L, x, w, b))
+    ref = oracle.conv2d(f64(x, "bf16"), f64(w, "bf16"), f64(b, "bf16"), L.stride, L.pad, L.dil, 1)
+    assert (~np.isfinite(ref)).sum() > 0
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    np.testing.assert_array_equal(np.isinf(got), np.isinf(ref))
+    np.testing.assert_array_equal(np.sign(got[np.isinf(got)]), np.sign(ref[np.isinf(ref)]))
+    fin = np.isfinite(ref)
+    assert rel_err(got[fin], ref[fin]) <= TOL["f16"]
+
+
+def test_stem_flags_and_workspace():
+    """No workspace; the fused pool is refused (UNSUPPORTED) rather than
+    run through the materialised path."""
+    d = ciw.make_desc(STEM.x_shape, STEM.w_shape, STEM.stride, STEM.pad, STEM.dil, 1)
+    for out in (ciw.CIW_BF16, ciw.CIW_F32):
+        assert ciw.conv2d_implicit_workspace_bytes(d, ciw.CIW_BF16, out, IMP) == 0
+        assert ciw.conv2d_implicit_workspace_bytes(d, ciw.CIW_BF16, out, IMP | ciw.CIW_FLAG_RELU) == 0
+    with pytest.raises(ciw.Im2winError):
+        ciw.conv2d_implicit_workspace_bytes(d, ciw.CIW_BF16, ciw.CIW_BF16, IMP | ciw.CIW_FLAG_MAXPOOL2)
+
+
 # ------------------------------------------------------------ depthwise
 DW = workloads.LAYERS["dw_3x3_fp32"]
 
