@@ -30,7 +30,8 @@ ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "transform.hip", "conv_fp32.hip", "conv_fp32_mfma.hip", "conv_mfma.hip", "conv_mfma_f16.hip",
            "conv_mfma_bf16.hip", "conv_dw.hip", "conv_dw_implicit.hip", "conv_implicit.hip", "conv_implicit_f16.hip",
-           "conv_implicit_bf16.hip", "conv_band_f16.hip", "conv_band_bf16.hip", "conv_narrow.hip"]
+           "conv_implicit_bf16.hip", "conv_band_f16.hip", "conv_band_bf16.hip", "conv_narrow.hip",
+           "conv_narrow_f16.hip", "conv_narrow_bf16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [

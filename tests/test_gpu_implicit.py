@@ -324,7 +324,7 @@ def test_stem_reduced_batch_every_output(n):
 # dilation, and each store form (staged runs, 4-pixel runs, single pixels)
 NARROW_SHAPES = [
     (2, 3, 23, 40, 40, 7, 7, (2, 2), (3, 3), 1),    # Q = 20: 4-pixel stores for 16-bit outputs
-    (1, 2, 30, 64, 24, 5, 5, (1, 2), (2, 2), 1),    # 5x5 (d = 0, three trailing entries), K <= 32
+    (1, 2, 30, 64, 24, 5, 5, (1, 2), (2, 1), 1),    # 5x5 (a trailing entry masked), K <= 32
     (1, 4, 26, 32, 33, 5, 6, (3, 2), (1, 1), 2),    # S = 6, stride_h 3, dil_h 2, Q = 15: single pixels
     (1, 1, 17, 16, 8, 7, 7, (2, 4), (0, 3), 1),     # one channel, stride_w 4, no row padding
     (2, 3, 12, 8, 64, 3, 7, (2, 2), (1, 5), 1),     # pad_w 5 (L = 8), 9 pairs: the 6-step form

@@ -1,12 +1,12 @@
 """CPU model of the few-channel in-LDS kernel (conv_mfma_narrow_kernel,
 csrc/conv_narrow_impl.hpp): the fp16/bf16 contraction for layers such as the
 3-channel 7x7 stride-2 stem.  It keeps a ring of zero-padded input rows in
-LDS ([slot][channel][column], plus a zero row a slot), reduces in (channel,
+LDS ([slot][channel][column]), reduces in (channel,
 filter row, filter column) order, and reads each lane's 8 entries of an MFMA
 step as one strip of a row, masked to the filter's columns.
 
 The model mirrors the plan and replays, for every band of a layer, the
-prologue (padding and zero rows cleared, the first step's rows copied in,
+prologue (padding columns cleared, the first step's rows copied in,
 the filter staged) and every step (each block's fragment reads, the next
 step's rows copied into the ring, output stores).  It checks:
   * every LDS access lies inside the kernel's allocation and inside the slot
@@ -14,8 +14,9 @@ step's rows copied into the ring, output stores).  It checks:
   * a slot is read only while it holds the row the read needs (each slot is
     tagged with the input row it holds), never a row the step does not have,
     and no copy writes a slot that the same step reads;
-  * copies never write padding columns or zero rows, and every entry a
-    fragment keeps was written;
+  * copies never write padding columns, and every entry a fragment keeps
+    was written; only the last step's second pair may be missing (C R odd),
+    and its fragment is cleared;
   * every global load lies inside x, and every output is stored exactly
     once, inside y;
   * the outputs multiplied out from the fragments the kernel would read
@@ -31,7 +32,8 @@ import oracle
 import workloads
 
 THREADS = 256
-MAX_IT, MAX_IT0, MAX_FILT = 3, 8, 8
+WAVES = THREADS // 64
+MAX_IT, MAX_IT0, MAX_FILT = 6, 8, 6
 LDS = 80 * 1024
 
 
@@ -48,7 +50,7 @@ def narrow_plan(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, pool=False, cus=256
         return None
     L = ceil_div(pw, 4) * 4
     d = (L - pw) & 1
-    if S + d > 8:
+    if S + d > 8 or S + d < 6:
         return None
     P = (H + 2 * ph - dh * (R - 1) - 1) // sh + 1
     Q = (W + 2 * pw - dw * (S - 1) - 1) // sw + 1
@@ -61,16 +63,17 @@ def narrow_plan(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, pool=False, cus=256
     keep = [d <= e < d + S for e in range(8)]
     cols = max(L + W, (Q - 1) * sw + col0 + 8)
     RB = ceil_div(cols, 8) * 8 * 2
-    slot_bytes = (C + 1) * RB
-    if slot_bytes * span > LDS:
+    slot_bytes = C * RB
+    if slot_bytes * (2 * span - 1) > LDS:
         return None
     wv = W // 8
     filt_elems = K * CR * S
-    filt_bytes = ceil_div(filt_elems * 2, 16) * 16
-    if filt_bytes // 16 > MAX_FILT * THREADS:
+    filt_bytes = ceil_div(filt_elems * 2, 16) * 16 + 32   # 16 bytes of slack below and above
+    if filt_elems * 2 // 16 > MAX_FILT * THREADS:
         return None
     eb = out_bytes
-    tiles = 4 * (1024 // (32 * eb)) * (32 * eb + 16)
+    tiles = WAVES * 64 * (32 * eb + 16)
+    region = max(filt_bytes, tiles)   # the staged filter, then the output tiles
     Nn = max(N, 1)
     nb = max(1, min(P, ceil_div(2 * cus, Nn)))
     band = ceil_div(P, nb)
@@ -80,8 +83,8 @@ def narrow_plan(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, pool=False, cus=256
     for sr in range(min(band, 16), 0, -1):
         nr = (2 * sr - 1) * sh + span
         r0 = (sr - 1) * sh + span
-        need = nr * slot_bytes + filt_bytes + tiles
-        if nr <= 255 and need <= LDS and sr * sh * per_row <= MAX_IT * THREADS and \
+        need = (nr + span - 1) * slot_bytes + region   # ring and mirror slots
+        if need <= LDS and sr * sh * per_row <= MAX_IT * THREADS and \
                 r0 * per_row <= MAX_IT0 * THREADS:
             SR, NR, lds = sr, nr, need
             break
@@ -90,10 +93,10 @@ def narrow_plan(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, pool=False, cus=256
     return dict(N=N, C=C, H=H, W=W, K=K, R=R, S=S, P=P, Q=Q, sh=sh, sw=sw, ph=ph, pw=pw, dh=dh,
                 CR=CR, span=span, L=L, d=d, col0=col0, keep=keep, RB=RB, slot_bytes=slot_bytes,
                 NR=NR, SR=SR, wv=wv, nl=L // 4, nr=(RB // 2 - L - W) // 4, band=band,
-                nbands=nbands, ntask=N * nbands, filt_elems=filt_elems,
-                filt_off=NR * slot_bytes, tile_off=NR * slot_bytes + filt_bytes, lds=lds,
-                staged=Q % (16 // eb) == 0, vec=Q % 4 == 0, out_bytes=eb,
-                KS=6 if ceil_div(CR, 2) <= 6 else 11)
+                nbands=nbands, ntask=N * nbands, filt_elems=filt_elems, filt_bytes=filt_bytes,
+                ring_bytes=NR * slot_bytes, mirror_lim=(span - 1) * slot_bytes,
+                filt_off=(NR + span - 1) * slot_bytes, tiles=tiles, lds=lds,
+                staged=Q % (16 // eb) == 0, vec=Q % 4 == 0, out_bytes=eb, KS=ceil_div(CR, 2))
 
 
 def replay(pl, x, wf, bias=None):
@@ -103,25 +106,39 @@ def replay(pl, x, wf, bias=None):
     CR, span, L, d, col0, keep = (pl[k] for k in ("CR", "span", "L", "d", "col0", "keep"))
     RB, SB, NR, SR, wv, KS = (pl[k] for k in ("RB", "slot_bytes", "NR", "SR", "wv", "KS"))
     per_row = C * wv
-    assert pl["filt_off"] + 2 * pl["filt_elems"] <= pl["tile_off"]
-    assert pl["tile_off"] + 4 * (1024 // (32 * pl["out_bytes"])) * (32 * pl["out_bytes"] + 16) <= pl["lds"] <= LDS
-    assert KS * 2 >= CR and (span - 1) < NR
+    assert pl["filt_off"] + 16 + 2 * pl["filt_elems"] + 16 <= pl["filt_off"] + pl["filt_bytes"] <= pl["lds"]
+    assert pl["filt_off"] + pl["tiles"] <= pl["lds"] <= LDS
+    assert 2 * KS - 1 <= CR <= 2 * KS and (span - 1) < NR
     y = np.full((N, K, P, Q), np.nan)
     written = np.zeros((N, K, P, Q), dtype=np.int64)
-    # filter fragments F[ct][ks][lane] (8 entries), built as the kernel builds them
+    kmask = np.array(keep)
+    assert kmask[2:6].all(), "only a fragment's first and last words are masked"
+    # filter fragments F[ct][ks][lane] (8 entries), built as the kernel builds
+    # them: the staged filter starts 16 bytes into its region (unwritten
+    # half-words are NaN), entry 0 of (k, u) is half-word (k C R + u) S - d + 8,
+    # read as aligned words, shifted into place, masked to the taps
+    fbytes = pl["filt_bytes"]
+    staged = np.full(fbytes // 2, np.nan)
+    staged[8:8 + pl["filt_elems"]] = wf.reshape(-1)
     F = np.zeros((2, KS, 64, 8))
     for ct in range(2):
         for ks in range(KS):
             for lane in range(64):
                 k, u = 32 * ct + lane % 32, 2 * ks + lane // 32
-                for e in range(8):
-                    s = e - d
-                    if k < K and u < CR and 0 <= s < S:
-                        F[ct, ks, lane, e] = wf[k, u // R, u % R, s]
+                ok = k < K and u < CR
+                e0 = (k * CR + u) * S - d + 8 if ok else 8
+                word = e0 >> 1   # five aligned words from there, shifted into place
+                assert 0 <= 4 * word and 4 * (word + 5) <= fbytes, "a filter read leaves the region"
+                vals = staged[e0:e0 + 8]
+                if ok:
+                    assert not np.isnan(vals[kmask]).any()
+                    F[ct, ks, lane] = np.where(kmask, vals, 0.0)
+                    for e in range(8):   # the taps the entries must hold
+                        if kmask[e]:
+                            assert vals[e] == wf[k, u // R, u % R, e - d]
     bk = np.zeros(64)
     if bias is not None:
         bk[:K] = bias
-    kmask = np.array(keep)
     for task in range(pl["ntask"]):
         n, bi = divmod(task, pl["nbands"])
         h0 = bi * pl["band"]
@@ -130,38 +147,33 @@ def replay(pl, x, wf, bias=None):
         orow = lambda t: min(t * SR, rows)
         rb = lambda t: (orow(t + 1) - 1) * sh + span
         xr0 = h0 * sh - ph
-        ring = np.full(NR * SB // 2, np.nan)         # LDS ring, one entry per 16-bit element
-        wr = np.zeros(NR * SB // 2, dtype=bool)      # entry written
-        pad = np.zeros(NR * SB // 2, dtype=bool)     # padding columns and zero rows
-        tag = np.full(NR, -1)                         # band input row a slot holds
+        NS = NR + span - 1                            # ring slots and their mirrors
+        ring = np.full(NS * SB // 2, np.nan)         # LDS ring, one entry per 16-bit element
+        wr = np.zeros(NS * SB // 2, dtype=bool)      # entry written
+        pad = np.zeros(NS * SB // 2, dtype=bool)     # padding columns
+        tag = np.full(NS, -1)                         # band input row a slot holds
 
-        # zeros: per slot, each channel row's nl + nr padding words, then the zero row
+        # zeros: per slot, each channel row's nl + nr padding words
         per_c = pl["nl"] + pl["nr"]
-        units = C * per_c + RB // 8
-        for it in range(NR * units):
+        units = C * per_c
+        for it in range(NS * units):
             slot, u = divmod(it, units)
-            off = slot * SB
-            if u < C * per_c:
-                c, k = divmod(u, per_c)
-                off += c * RB + (8 * k if k < pl["nl"] else 2 * (L + W) + 8 * (k - pl["nl"]))
-                lo = slot * SB + c * RB
-                assert lo <= off and off + 8 <= lo + RB
-                col = (off - lo) // 2
-                assert col + 4 <= L or col >= L + W, "zeroes an input column"
-            else:
-                off += C * RB + 8 * (u - C * per_c)
-                assert slot * SB + C * RB <= off and off + 8 <= (slot + 1) * SB
+            c, k = divmod(u, per_c)
+            off = slot * SB + c * RB + (8 * k if k < pl["nl"] else 2 * (L + W) + 8 * (k - pl["nl"]))
+            lo = slot * SB + c * RB
+            assert lo <= off and off + 8 <= lo + RB
+            col = (off - lo) // 2
+            assert col + 4 <= L or col >= L + W, "zeroes an input column"
             assert off % 8 == 0
             ring[off // 2:off // 2 + 4] = 0.0
             wr[off // 2:off // 2 + 4] = True
             pad[off // 2:off // 2 + 4] = True
-        # every padding column and zero-row entry was cleared
-        for slot in range(NR):
-            for c in range(C + 1):
+        # every padding column was cleared
+        for slot in range(NS):
+            for c in range(C):
                 row = slot * SB // 2 + c * RB // 2 + np.arange(RB // 2)
                 cols = np.arange(RB // 2)
-                want = (c == C) | (cols < L) | (cols >= L + W)
-                assert np.array_equal(pad[row], want)
+                assert np.array_equal(pad[row], (cols < L) | (cols >= L + W))
 
         def copy_rows(j0, j1, max_per_thread):
             nitems = (j1 - j0) * per_row
@@ -174,18 +186,20 @@ def replay(pl, x, wf, bias=None):
                 dst = slot * SB + c * RB + (L + 8 * vv) * 2
                 lo = slot * SB + c * RB
                 assert dst % 8 == 0 and lo <= dst and dst + 16 <= lo + RB
-                idx = dst // 2 + np.arange(8)
-                assert not pad[idx].any(), "a copy writes a padding column or zero row"
-                wr[idx] = True
                 xrow = xr0 + j
-                if 0 <= xrow < H:
-                    goff = 2 * (c * H * W + xrow * W + 8 * vv)
-                    assert 0 <= goff and goff + 16 <= 2 * C * H * W
-                    ring[idx] = x[n, c, xrow, 8 * vv:8 * vv + 8]
-                else:
-                    ring[idx] = 0.0
+                # every item's load is issued, from row 0 where the row is padding
+                goff = 2 * (c * H * W + (xrow if 0 <= xrow < H else 0) * W + 8 * vv)
+                assert 0 <= goff and goff + 16 <= 2 * C * H * W
+                vals = x[n, c, xrow, 8 * vv:8 * vv + 8] if 0 <= xrow < H else 0.0
+                for d_ in ([dst, dst + pl["ring_bytes"]] if dst < pl["mirror_lim"] else [dst]):
+                    idx = d_ // 2 + np.arange(8)
+                    assert not pad[idx].any(), "a copy writes a padding column"
+                    ring[idx] = vals
+                    wr[idx] = True
             for j in range(j0, j1):
                 tag[j % NR] = j
+                if j % NR < span - 1:
+                    tag[j % NR + NR] = j   # the mirror slot
 
         copy_rows(0, rb(0), MAX_IT0)
         for t in range(nsteps):
@@ -206,10 +220,9 @@ def replay(pl, x, wf, bias=None):
                     colb = (q * sw + col0) * 2
                     for ks in range(KS):
                         u = 2 * ks + g
-                        c, r = (u // R, u % R) if u < CR else (C, 0)
-                        s = s0 + r * dh
-                        if s >= NR:
-                            s -= NR
+                        c, r = (u // R, u % R) if u < CR else (0, 0)
+                        s = s0 + r * dh            # no wrap: the mirror slots continue the ring
+                        assert s < NS
                         off = s * SB + c * RB + colb
                         lo = s * SB + c * RB
                         assert off % 4 == 0 and lo <= off and off + 16 <= lo + RB
@@ -221,8 +234,9 @@ def replay(pl, x, wf, bias=None):
                             need.add(s)
                             assert wr[off // 2:off // 2 + 8][kmask].all(), "keeps an unwritten entry"
                         else:
-                            assert np.all(pad[off // 2:off // 2 + 8]), "an unused pair reads outside the zero row"
-                        vals = np.where(kmask, vals, 0.0)
+                            assert ks == KS - 1 and g == 1, "only the last step's second pair may be unused"
+                        tailm = not (ks == KS - 1 and u >= CR)
+                        vals = np.where(kmask & tailm, vals, 0.0)
                         for ct in range(2):
                             # lane (ml, g) is row m = ml of the window operand and column
                             # n = ml of the filter operand, both with k = 8 g + e
@@ -240,17 +254,32 @@ def replay(pl, x, wf, bias=None):
                     y[n, kk[:, None], h0 + hh[None, :], ww[None, :]] = acc[ct][np.ix_(pm, km)].T
                     np.add.at(written, (n, kk[:, None], h0 + hh[None, :], ww[None, :]), 1)
                 if pl["staged"]:
+                    # the wave's tile: 64 channel rows of 32 outputs; every
+                    # lane writes its 4-output runs of both halves, then reads
+                    # NRD 16-byte pieces and stores them
                     eb = pl["out_bytes"]
-                    rpr, ostr = 1024 // (32 * eb), 32 * eb + 16
-                    lpr = 64 // rpr
+                    ostr, cpr = 32 * eb + 16, 2 * eb
+                    wave = b % 4
+                    assert (wave + 1) * 64 * ostr <= pl["tiles"]
+                    written_t = np.zeros((64, 32 * eb), dtype=bool)
                     for lane in range(64):
-                        rr, seg = lane // lpr, lane % lpr
-                        assert rr * ostr + 16 * seg + 16 <= rpr * ostr
-                        p = 32 * b + seg * (16 // eb)
-                        if p < npx:   # a 16-byte run never crosses the step's end
-                            assert p + 16 // eb <= npx
+                        ml, g = lane % 32, lane // 32
+                        for ct in range(2 if K > 32 else 1):
+                            for jq in range(4):
+                                o = (8 * jq + 4 * g) * eb
+                                written_t[32 * ct + ml, o:o + 4 * eb] = True
+                    for lane in range(64):
+                        for r in range(64 * cpr // 64):
+                            piece = lane + 64 * r
+                            kk, seg = divmod(piece, cpr)
+                            assert kk * ostr + 16 * seg + 16 <= 64 * ostr
+                            p = 32 * b + seg * (16 // eb)
+                            if kk < K and p < npx:   # a stored piece was written, never crosses the step's end
+                                assert p + 16 // eb <= npx
+                                assert written_t[kk, 16 * seg:16 * seg + 16].all()
             if t + 1 < nsteps:
                 new = {j % NR for j in range(rb(t), rb(t + 1))}
+                new |= {s_ + NR for s_ in new if s_ < span - 1}
                 assert not (new & need), "a copy overwrites a slot the step reads"
                 copy_rows(rb(t), rb(t + 1), MAX_IT)
     assert np.all(written == 1), "an output is stored twice or never"
@@ -261,10 +290,12 @@ SHAPES = [
     # (N, C, H, W, K, R, S, stride, pad, dil_h, cus)
     (1, 3, 40, 224, 64, 7, 7, (2, 2), (3, 3), 1, 1),    # the stem's rows and filter, a few bands
     (2, 3, 23, 40, 40, 7, 7, (2, 2), (3, 3), 1, 2),     # K not a multiple of 32, ragged rows
-    (1, 2, 30, 64, 24, 5, 5, (1, 2), (2, 2), 1, 1),     # 5x5, d = 0, stride_h 1
+    (1, 2, 30, 64, 24, 5, 5, (1, 2), (2, 1), 1, 1),     # 5x5 (pad_w 1: a trailing entry masked), stride_h 1
     (1, 4, 26, 32, 33, 5, 6, (3, 2), (1, 1), 2, 1),     # dilation_h 2, stride_h 3, S = 6
     (1, 1, 17, 16, 8, 7, 7, (2, 4), (0, 3), 1, 1),      # one channel, stride_w 4, no row padding
     (2, 3, 12, 8, 64, 3, 7, (2, 2), (1, 5), 1, 2),      # pad_w 5 (L = 8, d = 1), 6 pairs
+    (2, 3, 112, 64, 64, 7, 7, (2, 2), (3, 3), 1, 1),    # one band an image: the ring wraps, mirrors read
+    (2, 2, 70, 48, 24, 5, 6, (1, 2), (2, 1), 2, 1),     # the same with stride_h 1, dil_h 2
 ]
 
 
@@ -308,13 +339,15 @@ def test_narrow_plan_of_the_stem():
     L = workloads.LAYERS["stem_7x7_s2_bf16"]
     pl = narrow_plan(L.N, L.C, L.H, L.W, L.K, 7, 7, 2, 2, 3, 3, 1, 1)
     # four bands of 28 rows an image (512 workgroups, two per CU), steps of
-    # 4 rows (14 blocks of 32 pixels), 21 ring slots of 3 channel rows and a
-    # zero row of 232 columns, 11 steps of 16 reduction entries
+    # 8 rows (28 blocks of 32 pixels, 7 a wave) and a last one of 4, 37 ring
+    # slots and 6 mirror slots of 3 channel rows of 232 columns, 11 steps of
+    # 16 reduction entries
     assert (pl["band"], pl["nbands"], pl["ntask"], pl["SR"], pl["NR"], pl["KS"]) == \
-        (28, 4, 512, 4, 21, 11)
+        (28, 4, 512, 8, 37, 11)
     assert (pl["L"], pl["d"], pl["col0"], pl["RB"]) == (4, 1, 0, 464)
     assert pl["keep"] == [False] + [True] * 7
-    assert pl["staged"] and pl["lds"] == 21 * 4 * 464 + 18816 + 4 * 16 * 80 <= LDS
+    # the filter's region then holds the four waves' 64-row output tiles
+    assert pl["staged"] and pl["lds"] == 43 * 3 * 464 + 4 * 64 * 80 <= LDS
 
 
 m = pytest.importorskip("cnn_convolution_im2win_amd")
