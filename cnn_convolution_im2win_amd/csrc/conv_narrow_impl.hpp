@@ -84,6 +84,7 @@ struct NarrowArgs {
     int filt_off;            // LDS byte offset of the staged filter; after the prologue,
                              // of the per-wave output tiles
     int filt_elems;          // K C R S
+    uint32_t zero;           // 0
     uint32_t plane_x, plane_y;
     FastDiv fdQ, fdNR, fdRow, fdWv;   // divisors Q, NR, C * W / 8, W / 8
 };
@@ -151,10 +152,13 @@ __global__ __launch_bounds__(kNarrowThreads, 2) void conv_mfma_narrow_kernel(
         const int xrow = xr0 + (int)j;
         const bool inside = xrow >= 0 && xrow < a.H;
         // every lane issues its load (from row 0 where the item is padding
-        // or past the rows), so the number of loads in flight is fixed
+        // or past the rows), so the number of loads in flight is fixed and
+        // the waits for them can be counted.  Padding is cleared with a
+        // zero the compiler cannot see (a.zero), so it cannot skip the load.
         const uint4 v = *reinterpret_cast<const uint4*>(
             ximg + 2u * ((uint32_t)c * a.plane_x + (uint32_t)((inside ? xrow : 0) * a.W + 8 * vv)));
-        return inside ? v : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t km = inside ? ~0u : a.zero;
+        return make_uint4(v.x & km, v.y & km, v.z & km, v.w & km);
     };
     auto store_item = [&](const uint4& v, int dst) {
         if (dst < 0) return;
@@ -184,6 +188,12 @@ __global__ __launch_bounds__(kNarrowThreads, 2) void conv_mfma_narrow_kernel(
         const int r0 = rb(0);
 #pragma unroll
         for (int k = 0; k < kNarrowMaxIt0; ++k) pv[k] = load_item(0, r0, tid + k * kNarrowThreads, pd[k]);
+        // the filter's chunks are needed here: waiting for them (and, the
+        // loads returning in order, for nothing issued later) before the
+        // zeroing below; left to itself the compiler would load each chunk
+        // where it is stored and wait for every row as well
+#pragma unroll
+        for (int k = 0; k < kNarrowMaxFilt; ++k) asm volatile("" : "+v"(fv[k].x), "+v"(fv[k].y), "+v"(fv[k].z), "+v"(fv[k].w));
         // zeros: per slot (mirrors included), each channel row's nl + nr padding words
         const int per_c = a.nl + a.nr;
         const int units = a.C * per_c;
@@ -467,6 +477,7 @@ inline bool narrow_plan(const Geom& g, int out_bytes, const Epi& epi, int cus, N
     a.nl = L / 4;
     a.nr = (int)((RB / 2 - L - g.W) / 4);
     a.filt_elems = g.K * CR * g.S;
+    a.zero = 0;
     if ((int64_t)a.filt_elems * 2 / 16 > (int64_t)kNarrowMaxFilt * kNarrowThreads) return false;
     // staged filter with 16 bytes below it and 16 above (read by the
     // fragments of the first and last (k, c, r) rows); then the per-wave
