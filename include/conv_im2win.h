@@ -102,22 +102,30 @@ typedef struct {
                                        [N][K][P/2][Q/2] (floor; an odd last row or column
                                        is dropped).  CIW_ERR_INVALID_ARG if P or Q < 2. */
 
-/* On-the-fly windows.  conv2d_fwd (fp16/bf16): the contraction kernel
- * builds the window rows of each band of output rows in LDS straight from x
- * and never writes the window tensor to memory.  For 3x3 filters with
- * stride_h 1, C a multiple of 16 up to 64, K <= 64, W a multiple of 8 and
- * no pool, one kernel does everything, filter re-layout included: no
- * workspace (0 bytes; workspace may be NULL).  For the other layers it
- * runs, the workspace holds a re-laid-out copy of the filter
- * (conv2d_implicit_workspace_bytes gives the size either way).
- * conv2d_dw_fwd (any input type): each workgroup stages whole zero-padded
- * input planes in LDS and computes their outputs there; no workspace
- * (workspace may be NULL).  The result is the same sum in another order
- * (the im2win paper's memory concern, §III-B and the processing strategies
- * of §IV-D1, taken to its end: no window tensor).  Layers these kernels do
- * not run return CIW_ERR_UNSUPPORTED, see conv2d_implicit_workspace_bytes.
- * Not allowed with CIW_FLAG_WINDOW_READY or CIW_FLAG_GENERIC
- * (CIW_ERR_INVALID_ARG). */
+/* On-the-fly windows: the contraction builds its windows in LDS straight
+ * from x and never writes the window tensor to memory (the im2win paper's
+ * memory concern, §III-B and the processing strategies of §IV-D1, taken to
+ * its end).  The result is the same sum in another order.
+ *   conv2d_fwd, fp16/bf16 input, one of three kernels:
+ *   - 3x3 filters, stride_h 1, C a multiple of 16 up to 64, K <= 64, W a
+ *     multiple of 8, no pool: one kernel, filter re-layout included, no
+ *     workspace;
+ *   - the other layers with C a multiple of 16 that the row-band kernel
+ *     runs (see conv2d_implicit_workspace_bytes), with the fused pool: the
+ *     workspace holds a re-laid-out copy of the filter;
+ *   - layers with few input channels and an even horizontal stride (C R <=
+ *     22, such as the 3-channel 7x7 stride-2 stem), no pool: one kernel,
+ *     filter included, no workspace;
+ *   conv2d_fwd, fp32: the matrix-core kernel with each pixel block's
+ *     zero-padded input rows staged in LDS (3x3 and 1x1 filters, no pool);
+ *     the workspace holds only the channel slices' partial sums (0 bytes
+ *     when the channel sum is not split);
+ *   conv2d_dw_fwd (any input type): each workgroup stages whole zero-padded
+ *     input planes in LDS and computes their outputs there; no workspace.
+ * conv2d_implicit_workspace_bytes gives the workspace (0 bytes: workspace
+ * may be NULL); layers none of these kernels run return
+ * CIW_ERR_UNSUPPORTED.  Not allowed with CIW_FLAG_WINDOW_READY or
+ * CIW_FLAG_GENERIC (CIW_ERR_INVALID_ARG). */
 #define CIW_FLAG_IMPLICIT     0x20u
 /* fp32 dense (conv2d_fwd) kernel choice.  By default the contraction runs
  * on the matrix cores (v_mfma_f32_32x32x2_f32) when that kernel runs the
@@ -183,18 +191,27 @@ ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
                                   int64_t n_images, size_t* bytes);
 
 /* Workspace conv2d_fwd / conv2d_dw_fwd need with CIW_FLAG_IMPLICIT for this
- * layer, output type and epilogue flags (independent of N).  Depthwise
- * (groups == C == K): 0 bytes; CIW_ERR_UNSUPPORTED if a zero-padded input
- * plane and its filter exceed 48 KB of LDS.  Dense: 0 bytes for the layers
- * the single-kernel form runs (see CIW_FLAG_IMPLICIT), else the re-laid-out
- * filter; CIW_ERR_UNSUPPORTED unless the input is fp16/bf16, groups == 1, C is a
- * multiple of 16, K <= 64, W a multiple of 8, stride_h == 1, the filter is
- * 3x3 with C <= 64 or 1x1 with C in {16, 32, 64}, a stored output row
- * needs at most 4 stores per thread (K*Qs/E <= 1024, where Qs is Q, or Q/2
- * with CIW_FLAG_MAXPOOL2, and E the largest power of two that divides Qs
- * with E * output element bytes <= 16), K times the output plane has
- * fewer than 2^31 elements, and an image of x has fewer than 2^31 bytes.
- * The fused ReLU and 2x2 max-pool are supported. */
+ * layer, output type and epilogue flags.  CIW_ERR_UNSUPPORTED for layers no
+ * in-LDS kernel runs.
+ * Depthwise (groups == C == K): 0 bytes; unsupported if a zero-padded input
+ * plane and its filter exceed 48 KB of LDS.
+ * Dense fp16/bf16 (groups == 1), the first kernel that runs the layer:
+ *   - 0 bytes: 3x3 filter, stride_h 1, C a multiple of 16 up to 64, K <= 64,
+ *     W a multiple of 8, no CIW_FLAG_MAXPOOL2;
+ *   - the re-laid-out filter: C a multiple of 16, K <= 64, W a multiple of 8,
+ *     stride_h == 1, a 3x3 filter with C <= 64 or 1x1 with C in {16, 32, 64},
+ *     a stored output row needing at most 4 stores per thread (K*Qs/E <=
+ *     1024, where Qs is Q, or Q/2 with CIW_FLAG_MAXPOOL2, and E the largest
+ *     power of two that divides Qs with E * output element bytes <= 16);
+ *     ReLU and the 2x2 max-pool fused;
+ *   - 0 bytes: C R <= 22, K <= 64, stride_w even, dil_w == 1, W a multiple of
+ *     8, 6 <= S + d <= 8 where d = (L - pad_w) mod 2 and L is pad_w rounded
+ *     up to a multiple of 4, no CIW_FLAG_MAXPOOL2 (ReLU fused);
+ *   all with K times the output plane and an image of x below 2^31 elements.
+ * Dense fp32: 3x3 or 1x1 filter, Q <= 192, C >= 2, no CIW_FLAG_MAXPOOL2,
+ *   and the zero-padded input rows of one 16-channel chunk of a pixel block
+ *   at most 5120 elements; the workspace is the channel slices' partial sums,
+ *   splits x N x K x P x Q x 4 bytes (0 when the sum is not split). */
 ciw_status conv2d_implicit_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
                                            ciw_dtype out_dtype, uint32_t flags, size_t* bytes);
 
@@ -226,7 +243,8 @@ ciw_status conv2d_fwd(const ciw_conv_desc* desc, ciw_dtype in_dtype, ciw_dtype o
  * per GPU, held from the first call on that GPU until the process ends; the
  * batch is processed in chunks of as many images as fit in it (see
  * conv2d_workspace_bytes), with CIW_FLAG_IMPLICIT the array holds the
- * re-laid-out filter.  Same arguments, flags and results as conv2d_fwd
+ * in-LDS path's workspace (the re-laid-out filter or the fp32 partial
+ * sums; nothing for the single-kernel forms).  Same arguments, flags and results as conv2d_fwd
  * otherwise.  Errors (before anything is enqueued): CIW_ERR_WORKSPACE if
  * one image's workspace (or the CIW_FLAG_IMPLICIT workspace) exceeds the
  * array; CIW_ERR_INVALID_ARG with CIW_FLAG_WINDOW_READY (the array cannot
