@@ -208,6 +208,21 @@ def stored_traffic(workload: str):
     return None if entry is None else entry.get("bytes_per_call")
 
 
+SETTLE_S = 0.5   # untimed back-to-back calls before a layer's first timed loop
+
+
+def settle(fn, seconds: float = SETTLE_S):
+    """Call fn back to back for about `seconds` (untimed): the GPU's clocks
+    ramp up under load over a few hundred milliseconds, and a timed loop of
+    a few dozen 30 us steps started from idle would measure the ramp."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+
+
 def loop_ms(stream, fn, steps: int, warmup: int):
     """Mean time per iteration of `fn` over `steps` back-to-back iterations:
     HIP events recorded on `stream` just before the first and just after
@@ -242,6 +257,7 @@ def time_steps(step: Step, steps: int, warmup: int):
     def one():
         step.transform()
         step.contract()
+    settle(one)
     gpu_ms, wall_ms = loop_ms(step.stream, one, steps, warmup)
     tr_ms, _ = loop_ms(step.stream, step.transform, steps, 2)
     co_ms, _ = loop_ms(step.stream, step.contract, steps, 2)
@@ -860,6 +876,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(head["step"]["ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -28,7 +28,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libconv_im2win.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "transform.hip", "conv_fp32.hip", "conv_fp32_mfma.hip", "conv_mfma.hip", "conv_mfma_f16.hip",
+SOURCES = ["api.cpp", "transform.hip", "conv_fp32.hip", "conv_fp32_mfma.hip", "conv_fp32_m16.hip", "conv_mfma.hip", "conv_mfma_f16.hip",
            "conv_mfma_bf16.hip", "conv_dw.hip", "conv_dw_implicit.hip", "conv_implicit.hip", "conv_implicit_f16.hip",
            "conv_implicit_bf16.hip", "conv_band_f16.hip", "conv_band_bf16.hip", "conv_narrow.hip",
            "conv_narrow_f16.hip", "conv_narrow_bf16.hip"]

@@ -507,6 +507,8 @@ hipError_t launch_conv_fp32(const Geom& g, const float* xw, const float* w, cons
     // default when its channel sum splits into at least 4 slices (below
     // that the layer is too small to fill the GPU through it, and the
     // vector kernel was measured faster)
+    if (kernel != FP32_VECTOR && !generic && !epi.pool && fp32_m16_tasks(g, n_images, false) > 0)
+        return launch_conv_fp32_m16(g, xw, w, bias, y, n_images, epi, false, st);
     if (kernel != FP32_VECTOR && !generic && !epi.pool && max_splits > 1) {
         const int ms = fp32_mfma_splits(g, n_images);
         if (ms > 0 && ms <= max_splits && (kernel == FP32_MATRIX || ms >= 4))

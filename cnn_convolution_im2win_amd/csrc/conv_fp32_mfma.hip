@@ -426,6 +426,10 @@ hipError_t launch_conv_fp32_mfma(const Geom& g, const float* xw, const float* w,
 }
 
 bool fp32_implicit_workspace(const Geom& g, const Epi& epi, size_t* bytes) {
+    if (!epi.pool && fp32_m16_tasks(g, std::max(g.N, 1), true) > 0) {   // the whole-sum kernel: no workspace
+        *bytes = 0;
+        return true;
+    }
     F32MPlan pl;
     if (epi.pool || !f32m_plan(g, std::max(g.N, 1), pl, true)) return false;
     const int64_t per_split = (int64_t)std::max(g.N, 1) * g.K * g.P * g.Q;
@@ -437,6 +441,8 @@ hipError_t launch_conv_fp32_implicit(const Geom& g, const float* x, const float*
                                      float* y, float* partials, const Epi& epi, hipStream_t st) {
     F32MPlan pl;
     if (g.N == 0) return hipSuccess;
+    if (!epi.pool && fp32_m16_tasks(g, g.N, true) > 0)
+        return launch_conv_fp32_m16(g, x, w, bias, y, g.N, epi, true, st);
     if (epi.pool || !f32m_plan(g, g.N, pl, true)) return hipErrorNotSupported;
     pl.a.relu = epi.relu;
     return launch_f32m(g, pl, x, w, bias, y, g.N, partials, epi, st, true);

@@ -100,6 +100,15 @@ hipError_t launch_conv_fp32_mfma(const Geom& g, const float* xw, const float* w,
                                  float* y, int n_images, float* partials, int max_splits,
                                  const Epi& epi, hipStream_t st);
 
+// fp32 dense contraction on the matrix cores with the whole channel sum in
+// one workgroup (16 output channels x 48 pixels; 3x3 and 1x1 filters, C a
+// multiple of 4, no pooling): no partial sums, one kernel, no workspace.
+// Over a CHW window tensor xw, or with imp in its in-LDS form over x.
+// fp32_m16_tasks is its workgroup count, 0 for layers it does not run.
+int fp32_m16_tasks(const Geom& g, int n_images, bool imp);
+hipError_t launch_conv_fp32_m16(const Geom& g, const float* xw, const float* w, const float* bias,
+                                float* y, int n_images, const Epi& epi, bool imp, hipStream_t st);
+
 // fp16/bf16 dense contraction over an HWC window tensor on the matrix cores.
 // The row kernel multiplies a re-laid-out copy of the filter (`aperm`,
 // mfma_prep_bytes(g) bytes, written by launch_mfma_prep once per call);

@@ -114,11 +114,13 @@ def test_plan_of_the_mid_layer():
 
 
 m = pytest.importorskip("cnn_convolution_im2win_amd")
+from tests.test_fp32_m16_model import plan as m16_plan  # noqa: E402
 
 
 def test_eligibility_matches_library():
-    """The fp32 layers the model's plan accepts are exactly those for which
-    the library accepts CIW_FLAG_IMPLICIT."""
+    """The fp32 layers this model's plan or the whole-sum kernel's in-LDS
+    plan accepts are exactly those for which the library accepts
+    CIW_FLAG_IMPLICIT."""
     rng = np.random.default_rng(11)
     for _ in range(80):
         C = int(rng.choice([1, 2, 3, 16, 48, 512]))
@@ -136,4 +138,6 @@ def test_eligibility_matches_library():
         except m.Im2winError:
             ok = False
         pl = plan(C, H, W, K, R, R, sh, sw, pad, pad, dil, dil)
-        assert (pl is not None) == ok, (C, H, W, K, R, sh, sw, pad, dil)
+        # the whole-sum kernel's in-LDS form takes the layers it fits first
+        whole = m16_plan(2, C, H, W, K, R, R, sh, sw, pad, pad, dil, dil, imp=True)
+        assert (pl is not None or whole is not None) == ok, (C, H, W, K, R, sh, sw, pad, dil)

@@ -218,6 +218,7 @@ def test_errors():
 
 
 # ------------------------------------------------------------ fp32 dense
+from tests.test_fp32_m16_model import plan as m16_plan  # noqa: E402
 MID = workloads.LAYERS["mid_3x3_fp32"]
 
 
@@ -231,7 +232,7 @@ def run_materialised_matrix(L, x, w, b, relu=False):
 def test_mid_layer_fp32_in_lds_every_output(relu):
     """The 1x512x13x13 -> 1024 layer in full: every output against the
     oracle, and bit for bit against the materialised path on the same
-    kernel (same products, same channel slices, same summation order)."""
+    kernel (the whole-sum kernel both ways: same products, same order)."""
     L = MID
     say(f"fp32 in-LDS: {L.name} relu={relu}")
     x, w, b = workloads.make_inputs(L)
@@ -256,6 +257,7 @@ FP32_SHAPES = [
     (3, 33, 7, 7, 70, 1, 1, 0, 1),         # 1x1, odd C
     (2, 64, 8, 56, 64, 3, 1, 1, 1),        # three pixel blocks of 3 rows
     (1, 48, 5, 100, 8, 3, 1, 1, 1),        # 100-pixel rows: one row a block
+    (1, 12, 10, 12, 16, 3, (1, 2), 2, 2),  # whole-sum kernel in LDS: stride_w 2, dilation 2, 13 staged rows
 ]
 
 
@@ -272,19 +274,31 @@ def test_fp32_in_lds_shapes_against_oracle(shape):
     e = rel_err(got, ref)
     say(f"  rel err {e:.3e}")
     assert got.shape == ref.shape and np.all(np.isfinite(got)) and e <= TOL["f32"]
+    # where the whole-sum kernel runs the layer both ways, the in-LDS form
+    # equals the materialised one bit for bit (same products, same order)
+    sh, sw = L.stride
+    both = all(m16_plan(N, C, H, W, K, R, R, sh, sw, pad, pad, dil, dil, imp=v) is not None
+               for v in (False, True))
+    if both:
+        y_imp = run(L, x, w, b)
+        assert torch.equal(y_imp, run_materialised_matrix(L, x, w, b))
 
 
 def test_fp32_in_lds_workspace():
-    """The workspace holds only the channel slices' partial sums: 8 slices
-    of the 1x512x13x13 -> 1024 output; too small a workspace is refused."""
+    """The mid layer runs through the whole-sum kernel: no workspace.  A
+    layer with C not a multiple of 4 takes the split kernel, whose workspace
+    holds the channel slices' partial sums; too small a one is refused."""
     d = ciw.make_desc(MID.x_shape, MID.w_shape, MID.stride, MID.pad, MID.dil, 1)
+    assert ciw.conv2d_implicit_workspace_bytes(d, ciw.CIW_F32, ciw.CIW_F32, IMP) == 0
+    L = MID.replace(name="odd_c", C=510)
+    d = ciw.make_desc(L.x_shape, L.w_shape, L.stride, L.pad, L.dil, 1)
     nbytes = ciw.conv2d_implicit_workspace_bytes(d, ciw.CIW_F32, ciw.CIW_F32, IMP)
-    assert nbytes == 8 * 1024 * 13 * 13 * 4
-    x, w, b = (to_dev(a, "f32") for a in workloads.make_inputs(MID))
+    assert nbytes > 0 and nbytes % (1024 * 13 * 13 * 4) == 0
+    x, w, b = (to_dev(a, "f32") for a in workloads.make_inputs(L))
     y = torch.empty((1, 1024, 13, 13), dtype=torch.float32, device="cuda")
     ws = torch.empty(nbytes - 256, dtype=torch.uint8, device="cuda")
     with pytest.raises(ciw.Im2winError):
-        ciw.conv2d_fwd(x, w, b, y, ws, MID.stride, MID.pad, MID.dil, flags=IMP)
+        ciw.conv2d_fwd(x, w, b, y, ws, L.stride, L.pad, L.dil, flags=IMP)
     torch.cuda.synchronize()
 
 
