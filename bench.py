@@ -447,6 +447,7 @@ def time_fp32_kernels(step: Step, steps: int, warmup: int):
             st = step.fn(*args)
             if st != 0:
                 raise RuntimeError(f"conv2d_fwd ({name}): status {st}")
+        settle(call, 0.2)
         ms, _ = loop_ms(step.stream, call, steps, warmup)
         out[name] = {"contract_ms": round(ms, 5),
                      "contract_tflops": round(step.flops() / (ms * 1e-3) / 1e12, 3)}
@@ -641,6 +642,8 @@ def measure_layer2(L: workloads.Layer, steps: int, warmup: int, iters: int, flus
 
     # the in-LDS call (no window tensor in HBM)
     call, nbytes = implicit_call(step)
+    if call is not None:
+        settle(call)   # (the traces before ran cold passes: 1 GiB reads between calls)
     if call is not None and not trace:
         ms, wall = loop_ms(step.stream, call, steps, warmup)
         res["in_lds"] = {"call_ms": round(ms, 5), "wall_ms": round(wall, 5), "workspace_bytes": nbytes,

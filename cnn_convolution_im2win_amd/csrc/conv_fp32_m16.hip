@@ -57,7 +57,7 @@ struct M16Args {
     int kblocks;      // 16-channel output blocks
     int nimg;         // images
     int ntask;
-    int cpw, ngr;     // channels per wave (a multiple of 4), groups per wave
+    int gA, gB;       // channel groups of waves 0-3 and of waves 4-7
     int nrow;         // window rows staged per channel (rows 48 pixels span, at most)
     int rq4;          // 16-byte pieces of a channel's staged rows: nrow * pitch / 4
     int AS;           // LDS row stride of a group's filter rows (floats)
@@ -66,18 +66,21 @@ struct M16Args {
     int relu;
     // in-LDS form: the staged zero-padded input rows of the group's channels
     int H, W, sh, ph, pw, dh;
-    int Hr, Wpl;      // staged rows and columns a channel
+    int Hr;           // staged rows a channel
+    int npc;          // 16-byte pieces of a channel's staged rows (at most)
+    int zoff;         // a channel's zero run: (R - 1) * dil_h * W + 1 zeros
 };
 
-// RS: filter taps (9 or 1); NP: loads (and LDS stores) per lane per group:
-// 16-byte filter and window pieces, or with IMP 4-byte input elements (after
-// the filter's 16-byte pieces); D (even): groups whose loads are in flight.
+// RS: filter taps (9 or 1); NP: 16-byte loads (and LDS stores) per lane per
+// group of its window pieces (with the filter's), or with IMP of its input
+// rows (after the filter's); D (even): groups whose loads are in flight.
 // IMP: the in-LDS form.  xw is then x itself: a group stages, per channel,
-// the zero-padded input rows its 48 pixels' windows span ([Hr][Wpl], Wpl
-// the padded columns the windows touch), and the window element of output
-// (h, w) at tap (r, q) is the staged element (h * stride_h + r * dil_h,
-// w * stride_w + q * dil_w), rows counted from the first pixel's.  The
-// window tensor is never written.
+// the input rows its 48 pixels' windows span, Hr rows of W elements end to
+// end as in x (rows outside the image stay zero), and the window element of
+// output (h, w) at tap (r, q) is staged row (h - h0) * stride_h + r * dil_h
+// (h0 the first pixel's row), column w * stride_w - pad_w + q * dil_w, or 0
+// where that column is outside the image.  The window tensor is never
+// written.
 template <int RS, int NP, int D, bool IMP>
 __global__ __launch_bounds__(kT, 1) void conv_fp32_mfma16_kernel(
     const float* __restrict__ xw, const float* __restrict__ w, const float* __restrict__ bias,
@@ -103,8 +106,13 @@ __global__ __launch_bounds__(kT, 1) void conv_fp32_mfma16_kernel(
     const int p0 = pg * kPix;
     const int h_lo = p0 / a.Q;
 
-    const int c_lo = wave * a.cpw;
-    const int ngr = max(0, min(a.ngr, (a.C - c_lo) / kG));   // C is a multiple of 4
+    // Waves 0-3 take gA groups of 4 channels each and waves 4-7 gB <= gA:
+    // waves t and t + 4 share a SIMD, and the older one is issued first
+    // whenever both are ready, so it gets through its groups faster (with
+    // equal shares the younger one was measured finishing 20% of the
+    // kernel later).
+    const int c_lo = wave < 4 ? wave * a.gA * kG : (4 * a.gA + (wave - 4) * a.gB) * kG;
+    const int ngr = max(0, min(wave < 4 ? a.gA : a.gB, (a.C - c_lo) / kG));   // C is a multiple of 4
 
     // Per-lane load plan, the same for every group (only the channel base
     // moves).  A group is 16 * RS filter pieces (row k, piece f of the
@@ -119,36 +127,44 @@ __global__ __launch_bounds__(kT, 1) void conv_fp32_mfma16_kernel(
     // slot past the buffer.  Each load address is a per-lane pointer moved
     // by a per-lane step each group; it stops at the wave's last group, so
     // the loads issued past it stay in bounds.
-    // With IMP the filter's pieces take kNA 16-byte loads and the group's
-    // 4 x Hr x W input elements NP 4-byte loads; an element of a row outside
-    // the image is not loaded from there (its LDS slot is zeroed once: the
-    // padding sits at the same positions for every group).
+    // With IMP the filter's pieces take the first kNA loads and the input
+    // rows the next NP: a channel's staged rows inside the image are nv
+    // elements end to end in x (so are they in LDS, from delta on, which
+    // puts them on 16-byte boundaries), cut into 16-byte pieces, the last
+    // one moved back to end at the last element (it then overlaps the one
+    // before and may sit off a 16-byte boundary).  Staged rows outside the
+    // image are zeroed once: they sit at the same positions for every group.
     const int nA = kM * RS;
     const int nP = nA + kG * a.rq4;
     constexpr int kNA = (kM * RS + 63) / 64;
-    constexpr int kNL = IMP ? kNA : NP;    // 16-byte loads a group
-    constexpr int kNX = IMP ? NP : 1;      // 4-byte loads a group (IMP)
+    constexpr int kNL = IMP ? kNA + NP : NP;    // 16-byte loads a group
     const float* src[kNL];
     uint32_t step[kNL], dst[kNL];
-    const float* xsrc[kNX];
-    uint32_t xdst[kNX];
     const int g0 = ngr > 0 ? c_lo : 0;   // first channel loaded (a wave with no channels reads channel 0)
+    // IMP: the staged rows inside the image, [r_lo, r_hi]; delta puts row
+    // r_lo's first element on a 16-byte boundary
+    const int r_lo = IMP ? max(0, a.ph - h_lo * a.sh) : 0;
+    const int r_hi = IMP ? min(a.Hr - 1, a.H - 1 + a.ph - h_lo * a.sh) : 0;
+    const int nv = IMP ? max(0, r_hi - r_lo + 1) * a.W : 0;
+    const int delta = IMP ? (4 - (r_lo * a.W) % 4) % 4 : 0;
     if constexpr (IMP) {
-        const int per_ch = a.Hr * a.W, nX = kG * per_ch;
+        const int npc = (nv + 3) / 4;
 #pragma unroll
-        for (int u = 0; u < kNX; ++u) {
-            const int e = min(lane + 64 * u, nX - 1);
-            const int ch = e / per_ch, rem = e - ch * per_ch;
-            const int r = rem / a.W, col = rem - r * a.W;
-            const int ih = h_lo * a.sh - a.ph + r;
-            const bool ok = lane + 64 * u < nX && ih >= 0 && ih < a.H;
-            xsrc[u] = xw + (((size_t)n_img * a.C + g0 + ch) * a.H + min(max(ih, 0), a.H - 1)) * a.W + col;
-            xdst[u] = ok ? 4u * (uint32_t)(kM * a.AS + ch * a.BS + r * a.Wpl + a.pw + col)
-                         : 4u * (uint32_t)(a.buf + lane);
+        for (int u = 0; u < NP; ++u) {
+            const int e = lane + 64 * u;
+            const int ch = e / a.npc, i = e - ch * a.npc;
+            const bool ok = ch < kG && i < npc;           // (then nv >= W >= 4)
+            const int start = ok ? min(4 * i, nv - 4) : 0;
+            const int ih0 = h_lo * a.sh - a.ph + r_lo;    // image row of staged row r_lo
+            src[kNA + u] = ok ? xw + (((size_t)n_img * a.C + g0 + ch) * a.H + ih0) * a.W + start
+                              : xw + ((size_t)n_img * a.C + g0) * a.H * a.W;
+            step[kNA + u] = (uint32_t)(kG * a.H * a.W * 4);
+            dst[kNA + u] = ok ? 4u * (uint32_t)(kM * a.AS + ch * a.BS + delta + r_lo * a.W + start)
+                              : 4u * (uint32_t)a.buf + 16u * lane;
         }
     }
 #pragma unroll
-    for (int u = 0; u < kNL; ++u) {
+    for (int u = 0; u < (IMP ? kNA : NP); ++u) {
         const int e = lane + 64 * u;
         if (e < nA || IMP) {
             const int ec = min(e, nA - 1);
@@ -171,29 +187,18 @@ __global__ __launch_bounds__(kT, 1) void conv_fp32_mfma16_kernel(
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     struct Fetched {
         u32x4 r[kNL];
-        uint32_t x[kNX];
     };
-    const uint32_t xstep = (uint32_t)(kG * a.H * a.W * 4);
     // the loads of the next group (group j: the pointers sit at group
     // min(j, ngr - 1))
     int at = 0;   // group the pointers sit at
     auto fetch = [&](Fetched& f) {
 #pragma unroll
         for (int u = 0; u < kNL; ++u) f.r[u] = *reinterpret_cast<const u32x4*>(src[u]);
-        if constexpr (IMP) {
-#pragma unroll
-            for (int u = 0; u < kNX; ++u) f.x[u] = *reinterpret_cast<const uint32_t*>(xsrc[u]);
-        }
         const bool adv = at + 1 < ngr;
         at += adv ? 1 : 0;
 #pragma unroll
         for (int u = 0; u < kNL; ++u)
             src[u] = reinterpret_cast<const float*>(reinterpret_cast<const char*>(src[u]) + (adv ? step[u] : 0u));
-        if constexpr (IMP) {
-#pragma unroll
-            for (int u = 0; u < kNX; ++u)
-                xsrc[u] = reinterpret_cast<const float*>(reinterpret_cast<const char*>(xsrc[u]) + (adv ? xstep : 0u));
-        }
     };
     // the wave's buffer: filter rows [16][AS], then the window rows [4][BS],
     // then 64 16-byte slots that lanes with no piece write (so every store
@@ -202,10 +207,6 @@ __global__ __launch_bounds__(kT, 1) void conv_fp32_mfma16_kernel(
     auto stash = [&](const Fetched& f) {
 #pragma unroll
         for (int u = 0; u < kNL; ++u) *reinterpret_cast<u32x4*>(wbase + dst[u]) = f.r[u];
-        if constexpr (IMP) {
-#pragma unroll
-            for (int u = 0; u < kNX; ++u) *reinterpret_cast<uint32_t*>(wbase + xdst[u]) = f.x[u];
-        }
     };
     if constexpr (IMP) {
         // the staged rows' padding: zero once (no group writes it)
@@ -215,20 +216,30 @@ __global__ __launch_bounds__(kT, 1) void conv_fp32_mfma16_kernel(
 
     // the lane's window offsets: pixel tile t3, column m of the tile (past
     // the image's last pixel: that pixel, read but never stored)
-    int pxoff[kTiles];
+    constexpr int S = RS == 9 ? 3 : 1;
+    constexpr int R = S;
+    // off[t3][q]: the lane's window element of tile t3, filter row 0,
+    // filter column q (the window tensor's R values of a column adjacent;
+    // in LDS, staged row (h - h0) * stride_h, column w * stride_w - pad_w
+    // + q * dil_w), filter row r rstep * r further on.  In LDS a column
+    // outside the image points at the channel's zero run instead, which
+    // holds zeros at every filter row's distance.
+    int off[kTiles][S];
 #pragma unroll
     for (int t3 = 0; t3 < kTiles; ++t3) {
         const int px = min(p0 + 16 * t3 + m, a.PQ - 1);
         const int hh = px / a.Q, ww = px - hh * a.Q;
-        pxoff[t3] = IMP ? (hh - h_lo) * a.sh * a.Wpl + ww * a.sw : (hh - h_lo) * a.pitch + ww * a.sw * a.R;
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+            if constexpr (IMP) {
+                const int col = ww * a.sw - a.pw + q * a.dw;
+                off[t3][q] = col >= 0 && col < a.W ? delta + (hh - h_lo) * a.sh * a.W + col : a.zoff;
+            } else {
+                off[t3][q] = (hh - h_lo) * a.pitch + (ww * a.sw + q * a.dw) * a.R;
+            }
+        }
     }
-    constexpr int S = RS == 9 ? 3 : 1;
-    constexpr int R = S;
-    int toff[RS];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int q = 0; q < S; ++q) toff[r * S + q] = IMP ? r * a.dh * a.Wpl + q * a.dw : q * a.dw * R + r;
+    const int rstep = IMP ? a.dh * a.W : 1;
 
     f32x4 acc[kTiles];
 #pragma unroll
@@ -248,7 +259,9 @@ __global__ __launch_bounds__(kT, 1) void conv_fp32_mfma16_kernel(
 #pragma unroll
         for (int t3 = 0; t3 < kTiles; ++t3)
 #pragma unroll
-            for (int t = 0; t < RS; ++t) o.bv[t3][t] = Bp[pxoff[t3] + toff[t]];
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int q = 0; q < S; ++q) o.bv[t3][r * S + q] = Bp[off[t3][q] + r * rstep];
     };
     auto multiply = [&](const Ops& o) {
 #pragma unroll
@@ -267,7 +280,7 @@ __global__ __launch_bounds__(kT, 1) void conv_fp32_mfma16_kernel(
 #pragma unroll
         for (int i = 0; i < kSteps; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);          // MFMA
-            if (i < 2) __builtin_amdgcn_sched_group_barrier(0x200, (kNL + (IMP ? kNX : 0) + 1) / 2, 0);   // DS write
+            if (i < 2) __builtin_amdgcn_sched_group_barrier(0x200, (kNL + 1) / 2, 0);   // DS write
             else __builtin_amdgcn_sched_group_barrier(0x100, kRper, 0);               // DS read
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);          // VMEM read
         }
@@ -345,7 +358,7 @@ template <int RS, bool IMP>
 using M16Fn = void (*)(const float*, const float*, const float*, float*, M16Args);
 
 template <int NP, bool IMP>
-constexpr int depth_of() { return IMP ? 4 : depth_for<NP>(); }
+constexpr int depth_of() { return depth_for<IMP ? NP + 3 : NP>(); }
 
 template <int RS, bool IMP>
 M16Fn<RS, IMP> m16_kernel(int np) {
@@ -382,15 +395,21 @@ bool m16_plan(const Geom& g, int n_images, bool imp, M16Plan& pl) {
     a.nrow = std::min(g.P, (kPix - 1) / g.Q + 2);
     a.AS = kG * RS;
     if (imp) {
+        // pieces of 4 elements need rows of at least 4
+        if (g.W < 4) return false;
         const int64_t hr = (int64_t)(a.nrow - 1) * g.sh + (int64_t)(g.R - 1) * g.dh + 1;
-        const int64_t per_ch = hr * g.Wwin;
-        const int64_t nx = (int64_t)kG * hr * g.W;
-        if (nx > (int64_t)kMaxP * 64 || per_ch > (1 << 20)) return false;
+        const int64_t per_ch = hr * g.W;                // staged elements a channel
+        const int64_t npc = (per_ch + 3) / 4;
+        const int64_t np = (kG * npc + 63) / 64;
+        if (np + (kM * RS + 63) / 64 > kMaxP || per_ch > (1 << 20)) return false;
         a.Hr = (int)hr;
-        a.Wpl = g.Wwin;
+        a.npc = (int)npc;
         a.rq4 = 0;
-        a.BS = (int)round_up(per_ch, 4) + 4;
-        pl.np = (int)((nx + 63) / 64);
+        // [shift <= 3][staged rows][<= 3][zero run], the run read for taps in
+        // the horizontal padding
+        a.zoff = (int)round_up(per_ch + 3, 4);
+        a.BS = a.zoff + (int)round_up((int64_t)(g.R - 1) * g.dh * g.W + 1, 4) + 4;
+        pl.np = (int)np;
         // 32-bit offsets: the step between groups of x
         if ((int64_t)kG * g.H * g.W * 4 >= ((int64_t)1 << 32)) return false;
     } else {
@@ -399,12 +418,15 @@ bool m16_plan(const Geom& g, int n_images, bool imp, M16Plan& pl) {
         const int64_t pieces = (int64_t)kM * RS + (int64_t)kG * a.rq4;
         if (pieces > (int64_t)kMaxP * 64) return false;
         pl.np = (int)((pieces + 63) / 64);
-        a.Hr = a.Wpl = 0;
+        a.Hr = a.npc = a.zoff = 0;
         a.BS = a.nrow * g.pitchA + 4;
         if ((int64_t)kG * g.P * g.pitchA * 4 >= ((int64_t)1 << 32)) return false;
     }
-    a.cpw = (int)round_up((g.C + kWaves - 1) / kWaves, kG);
-    a.ngr = a.cpw / kG;
+    // the groups split over the waves, an eighth of a wave's share moved
+    // from each of waves 4-7 to its SIMD partner
+    const int ngr = (g.C / kG + kWaves - 1) / kWaves;
+    a.gA = ngr + ngr / 8;
+    a.gB = ngr - ngr / 8;
     a.buf = kM * a.AS + kG * a.BS;
     if (a.buf < kTiles * 4 * 64) a.buf = kTiles * 4 * 64;   // room for the final sums
     a.nimg = n_images;

@@ -2,8 +2,9 @@
 (conv_fp32_mfma16_kernel, csrc/conv_fp32_m16.hip).
 
 A workgroup owns 16 output channels x 48 consecutive output pixels of one
-image and the whole channel sum; wave v streams channels [v cpw, (v + 1) cpw)
-in groups of 4 (the 16x16x4 MFMA's reduction width): the group's filter rows
+image and the whole channel sum; wave v streams its own contiguous channel range
+in groups of 4 (the 16x16x4 MFMA's reduction width; waves 0-3 take an eighth
+more groups than waves 4-7): the group's filter rows
 (16 rows x 4 R S floats, 16-byte pieces) and the rows of the CHW window
 tensor its 48 pixels span (nrow rows of each of the 4 channels, 16-byte
 pieces) go into the wave's own LDS buffer; lane (m, kk) then reads filter
@@ -18,10 +19,13 @@ group wrote), and multiplies the outputs out from the replayed buffers in
 the kernel's order: they must match the oracle's convolution.
 
 The in-LDS form (IMP) is replayed too: a group's filter pieces as above, then
-its 4 x Hr x W input elements from x (4-byte loads; elements of rows outside
-the image are not stored, their slots stay zero from the one clearing at the
-start), and the window element of pixel (h, w) at tap (r, q) read at staged
-row (h - h_lo) stride_h + r dil_h, column w stride_w + q dil_w."""
+each channel's staged rows inside the image, end to end as in x, in 16-byte
+pieces (the last one moved back to end at the last element), stored from a
+shift that puts them on 16-byte boundaries; rows outside the image and the
+channel's zero run stay zero from the one clearing at the start; the window
+element of pixel (h, w) at tap (r, q) is read at staged row (h - h_lo)
+stride_h + r dil_h, column w stride_w - pad_w + q dil_w, or from the zero
+run where that column is outside the image."""
 import numpy as np
 import pytest
 
@@ -48,12 +52,17 @@ def plan(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, imp=False):
     a["nrow"] = min(P, (PIX - 1) // Q + 2)
     a["imp"] = imp
     if imp:
-        Hr = (a["nrow"] - 1) * sh + (R - 1) * dh + 1
-        nx = G * Hr * W
-        if nx > MAX_P * 64 or Hr * Wwin > (1 << 20) or G * H * W * 4 >= 2 ** 32:
+        if W < 4:
             return None
-        a.update(Hr=Hr, Wpl=Wwin, rq4=0, BS=-(-Hr * Wwin // 4) * 4 + 4, np=-(-nx // 64),
-                 H=H, W=W, sh=sh, ph=ph, pw=pw, dh=dh)
+        Hr = (a["nrow"] - 1) * sh + (R - 1) * dh + 1
+        per_ch = Hr * W
+        npc = -(-per_ch // 4)
+        np_ = -(-G * npc // 64)
+        if np_ + -(-M * R * S // 64) > MAX_P or per_ch > (1 << 20) or G * H * W * 4 >= 2 ** 32:
+            return None
+        zoff = -(-(per_ch + 3) // 4) * 4
+        a.update(Hr=Hr, npc=npc, rq4=0, zoff=zoff, BS=zoff + -(-((R - 1) * dh * W + 1) // 4) * 4 + 4,
+                 np=np_, H=H, W=W, sh=sh, ph=ph, pw=pw, dh=dh)
     else:
         if a["nrow"] * pitch % 4:
             return None
@@ -63,8 +72,8 @@ def plan(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, imp=False):
             return None
         a["np"] = -(-pieces // 64)
         a["BS"] = a["nrow"] * pitch + 4
-    a["cpw"] = -(-(-(-C // WAVES)) // G) * G
-    a["ngr"] = a["cpw"] // G
+    ngr = -(-(C // G) // WAVES)
+    a["gA"], a["gB"] = ngr + ngr // 8, ngr - ngr // 8
     a["AS"] = G * RS
     a["buf"] = max(M * a["AS"] + G * a["BS"], TILES * 4 * 64)
     a["ntask"] = N * a["pgroups"] * a["kblocks"]
@@ -87,12 +96,7 @@ def replay(xw, w, a, N, C, K, R, S, sw, dw):
     stored = np.zeros((N, K, PQ), dtype=int)
     lanes = np.arange(64)
     m, kk = lanes & 15, lanes >> 4
-    if imp:
-        toff = np.array([r * a["dh"] * a["Wpl"] + q * dw for r in range(R) for q in range(S)])
-        span = a["Hr"] * a["Wpl"]          # a channel's staged elements
-    else:
-        toff = np.array([q * dw * R + r for r in range(R) for q in range(S)])
-        span = nrow * pitch
+    span = a["BS"] if imp else nrow * pitch     # a channel's readable words
     for task in range(a["ntask"]):
         pg = task % a["pgroups"]
         rest = task // a["pgroups"]
@@ -103,14 +107,24 @@ def replay(xw, w, a, N, C, K, R, S, sw, dw):
         px = np.minimum(p0 + 16 * np.arange(TILES)[:, None] + m[None, :], PQ - 1)   # [tile][lane]
         hh, ww = px // Q, px % Q
         assert np.all(hh - h_lo < nrow) and np.all(hh - h_lo >= 0)
+        # off[t3][q][lane]: filter row 0, column q; row r is rstep * r further on
         if imp:
-            pxoff = (hh - h_lo) * a["sh"] * a["Wpl"] + ww * sw
+            r_lo = max(0, a["ph"] - h_lo * a["sh"])
+            r_hi = min(a["Hr"] - 1, a["H"] - 1 + a["ph"] - h_lo * a["sh"])
+            nv = max(0, r_hi - r_lo + 1) * a["W"]
+            delta = (4 - (r_lo * a["W"]) % 4) % 4
+            col = ww[:, None, :] * sw - a["pw"] + np.arange(S)[None, :, None] * dw
+            inside = (col >= 0) & (col < a["W"])
+            off = np.where(inside, delta + (hh - h_lo)[:, None, :] * a["sh"] * a["W"] + col, a["zoff"])
+            rstep = a["dh"] * a["W"]
         else:
-            pxoff = (hh - h_lo) * pitch + ww * sw * R
+            off = (hh - h_lo)[:, None, :] * pitch + (ww[:, None, :] * sw + np.arange(S)[None, :, None] * dw) * R
+            rstep = 1
         red = np.zeros((WAVES, TILES, 64, 4))
         for v in range(WAVES):
-            c_lo = v * a["cpw"]
-            ngr = max(0, min(a["ngr"], (C - c_lo) // G))
+            gA, gB = a["gA"], a["gB"]
+            c_lo = (v * gA if v < 4 else 4 * gA + (v - 4) * gB) * G
+            ngr = max(0, min(gA if v < 4 else gB, (C - c_lo) // G))
             acc = np.zeros((TILES, 16, 16))     # [tile][channel row][pixel col]
             # one buffer a wave: filter rows [16][AS], window rows [4][BS], then
             # 64 dummy 16-byte slots; the in-LDS form clears the window rows once
@@ -157,24 +171,27 @@ def replay(xw, w, a, N, C, K, R, S, sw, dw):
                         wrote[dst:dst + 4] += 1
                 if imp:
                     H, W = a["H"], a["W"]
-                    per_ch = a["Hr"] * W
-                    nX = G * per_ch
+                    npc = -(-nv // 4)
+                    ih0 = h_lo * a["sh"] - a["ph"] + r_lo
                     for u in range(a["np"]):
                         for l in range(64):
                             e = l + 64 * u
-                            ch, rem = divmod(min(e, nX - 1), per_ch)
-                            r, col = divmod(rem, W)
-                            ih = h_lo * a["sh"] - a["ph"] + r
-                            ok = e < nX and 0 <= ih < H
-                            src = ((n * C + g0 + ch) * H + min(max(ih, 0), H - 1)) * W + col + j * G * H * W
-                            assert 0 <= src < xflat.size
+                            ch, i = divmod(e, a["npc"])
+                            ok = ch < G and i < npc
                             if ok:
-                                dst = M * AS + ch * BS + r * a["Wpl"] + a["pw"] + col
-                                assert dst < M * AS + ch * BS + span
-                                wrote[dst] += 1
+                                assert nv >= 4
+                                start = min(4 * i, nv - 4)
+                                src = ((n * C + g0 + ch) * H + ih0) * W + start + j * G * H * W
+                                dst = M * AS + ch * BS + delta + r_lo * W + start
+                                # inside the channel's staged rows, before its zero run
+                                assert M * AS + ch * BS <= dst and dst + 4 <= M * AS + ch * BS + a["zoff"]
+                                assert dst + 4 <= M * AS + ch * BS + delta + (r_hi + 1) * W
+                                wrote[dst:dst + 4] = 1
                             else:
-                                dst = buf + l
-                            buf_arr[dst] = xflat[src]
+                                src = ((n * C + g0) * H) * W + j * G * H * W
+                                dst = buf + 4 * l
+                            assert 0 <= src and src + 4 <= xflat.size
+                            buf_arr[dst:dst + 4] = xflat[src:src + 4]
                 Abuf, Bbuf = buf_arr[:M * AS], buf_arr[M * AS:M * AS + G * BS]
                 wrote_a, wrote_b = wrote[:M * AS], wrote[M * AS:M * AS + G * BS]
                 assert wrote_a.max() <= 1 and wrote_b.max() <= 1
@@ -184,7 +201,7 @@ def replay(xw, w, a, N, C, K, R, S, sw, dw):
                 assert np.all(wrote_a[aidx] == 1)
                 av = Abuf[aidx]
                 for t3 in range(TILES):
-                    bidx = kk[:, None] * BS + pxoff[t3][:, None] + toff[None, :]     # [lane][t]
+                    bidx = np.stack([kk * BS + off[t3][t % S] + (t // S) * rstep for t in range(RS)], axis=1)
                     assert np.all(bidx >= kk[:, None] * BS) and np.all(bidx < kk[:, None] * BS + span)
                     if not imp:
                         assert np.all(wrote_b[bidx] == 1)
@@ -256,17 +273,18 @@ def test_m16_model_matches_oracle(shape, imp):
 
 def test_plan_of_the_mid_layer():
     """1x512x13x13 -> 1024: 4 pixel groups x 64 channel blocks = 256
-    workgroups; 64 channels (16 groups) a wave; 5 window rows of 48 floats a
+    workgroups; 18 groups of 4 channels for each of waves 0-3, 14 for each of
+    waves 4-7; 5 window rows of 48 floats a
     channel: 144 + 240 16-byte pieces a group, 6 loads a lane; 58 KB of LDS."""
     a = plan(1, 512, 13, 13, 1024, 3, 3, 1, 1, 1, 1, 1, 1)
     assert (a["pgroups"], a["kblocks"], a["ntask"]) == (4, 64, 256)
-    assert (a["cpw"], a["ngr"], a["nrow"], a["pitch"], a["np"]) == (64, 16, 5, 48, 6)
+    assert (a["gA"], a["gB"], a["nrow"], a["pitch"], a["np"]) == (18, 14, 5, 48, 6)
     assert a["lds"] == 8 * (16 * 36 + 4 * 244 + 256) * 4
 
 
 def test_plan_of_the_mid_layer_in_lds():
-    """In LDS: 7 staged rows of 15 columns a channel (91 input elements),
-    364 elements a group: 6 four-byte loads a lane beside the filter's 3."""
+    """In LDS: 7 staged rows of 13 elements a channel, 23 16-byte pieces, 92
+    a group: 2 loads a lane beside the filter's 3; a 27-word zero run."""
     a = plan(1, 512, 13, 13, 1024, 3, 3, 1, 1, 1, 1, 1, 1, imp=True)
-    assert (a["Hr"], a["Wpl"], a["np"], a["BS"]) == (7, 15, 6, 112)
-    assert a["lds"] == 8 * (16 * 36 + 4 * 112 + 256) * 4
+    assert (a["Hr"], a["npc"], a["np"], a["zoff"], a["BS"]) == (7, 23, 2, 96, 128)
+    assert a["lds"] == 8 * (16 * 36 + 4 * 128 + 256) * 4
