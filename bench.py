@@ -208,15 +208,15 @@ def stored_traffic(workload: str):
     return None if entry is None else entry.get("bytes_per_call")
 
 
-SETTLE_S = 0.5   # untimed back-to-back calls before a layer's first timed loop
+SETTLE_S = 0.5   # untimed back-to-back calls before a layer's first timed loop (--settle)
 
 
-def settle(fn, seconds: float = SETTLE_S):
+def settle(fn, seconds: float = None):
     """Call fn back to back for about `seconds` (untimed): the GPU's clocks
     ramp up under load over a few hundred milliseconds, and a timed loop of
     a few dozen 30 us steps started from idle would measure the ramp."""
     import torch
-    t_end = time.perf_counter() + seconds
+    t_end = time.perf_counter() + (SETTLE_S if seconds is None else min(seconds, SETTLE_S))
     while time.perf_counter() < t_end:
         for _ in range(20):
             fn()
@@ -766,6 +766,7 @@ def ablation_report(runs: int = 5, calls: int = 50) -> dict:
 
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
@@ -790,11 +791,15 @@ def main():
     ap.add_argument("--layer-cpu-seconds", type=float, default=3.0,
                     help="CPU time of each other layer's oracle sample and of the im2col point")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed back-to-back calls before each layer's timed loops "
+                         "(0 under a profiler, whose records would grow with them)")
     ap.add_argument("--ablation", action="store_true",
                     help="time the ablation variant libraries instead (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
+    SETTLE_S = max(0.0, args.settle)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

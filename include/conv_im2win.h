@@ -116,10 +116,13 @@ typedef struct {
  *   - layers with few input channels and an even horizontal stride (C R <=
  *     22, such as the 3-channel 7x7 stride-2 stem), no pool: one kernel,
  *     filter included, no workspace;
- *   conv2d_fwd, fp32: the matrix-core kernel with each pixel block's
- *     zero-padded input rows staged in LDS (3x3 and 1x1 filters, no pool);
- *     the workspace holds only the channel slices' partial sums (0 bytes
- *     when the channel sum is not split);
+ *   conv2d_fwd, fp32 (3x3 and 1x1 filters, no pool), one of two kernels:
+ *   - C a multiple of 4: the whole-sum matrix-core kernel (16 output
+ *     channels x 48 pixels and the whole channel sum a workgroup) with each
+ *     group of 4 channels' input rows staged in LDS; no workspace;
+ *   - otherwise the split matrix-core kernel with each pixel block's
+ *     zero-padded input rows staged in LDS; the workspace holds only the
+ *     channel slices' partial sums (0 bytes when the sum is not split);
  *   conv2d_dw_fwd (any input type): each workgroup stages whole zero-padded
  *     input planes in LDS and computes their outputs there; no workspace.
  * conv2d_implicit_workspace_bytes gives the workspace (0 bytes: workspace
@@ -128,15 +131,18 @@ typedef struct {
  * CIW_FLAG_GENERIC (CIW_ERR_INVALID_ARG). */
 #define CIW_FLAG_IMPLICIT     0x20u
 /* fp32 dense (conv2d_fwd) kernel choice.  By default the contraction runs
- * on the matrix cores (v_mfma_f32_32x32x2_f32) when that kernel runs the
- * layer (3x3 and 1x1 filters, output rows of at most 192 pixels, no
- * CIW_FLAG_MAXPOOL2) and its plan splits the channel sum into at least 4
- * slices (a channel sum long enough to fill the GPU); otherwise on the
- * vector ALUs.  CIW_FLAG_FP32_MFMA forces the matrix cores wherever that
- * kernel runs the layer, CIW_FLAG_FP32_VALU forces the vector ALUs (both:
- * CIW_ERR_INVALID_ARG).  Either way the sum is deterministic (slices added
- * in a fixed order) and the same sum in another order.  Ignored for
- * fp16/bf16; CIW_FLAG_GENERIC and CIW_FLAG_NO_SPLIT imply the vector ALUs. */
+ * on the matrix cores: with the whole channel sum in one workgroup
+ * (v_mfma_f32_16x16x4_f32, 16 output channels x 48 pixels; 3x3 and 1x1
+ * filters, C a multiple of 4, no CIW_FLAG_MAXPOOL2; one kernel, no partial
+ * sums), else with the channel sum split over workgroups
+ * (v_mfma_f32_32x32x2_f32; 3x3 and 1x1 filters, output rows of at most 192
+ * pixels, no pool) where that plan has at least 4 slices; otherwise on the
+ * vector ALUs.  CIW_FLAG_FP32_MFMA forces the matrix cores wherever one of
+ * those kernels runs the layer, CIW_FLAG_FP32_VALU forces the vector ALUs
+ * (both: CIW_ERR_INVALID_ARG).  Every sum is deterministic (fixed orders)
+ * and the same sum in another order.  Ignored for fp16/bf16;
+ * CIW_FLAG_GENERIC implies the vector ALUs; with CIW_FLAG_NO_SPLIT only the
+ * whole-sum kernel or the vector ALUs run. */
 #define CIW_FLAG_FP32_MFMA    0x40u
 #define CIW_FLAG_FP32_VALU    0x80u
 
@@ -208,10 +214,16 @@ ciw_status conv2d_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
  *     8, 6 <= S + d <= 8 where d = (L - pad_w) mod 2 and L is pad_w rounded
  *     up to a multiple of 4, no CIW_FLAG_MAXPOOL2 (ReLU fused);
  *   all with K times the output plane and an image of x below 2^31 elements.
- * Dense fp32: 3x3 or 1x1 filter, Q <= 192, C >= 2, no CIW_FLAG_MAXPOOL2,
- *   and the zero-padded input rows of one 16-channel chunk of a pixel block
- *   at most 5120 elements; the workspace is the channel slices' partial sums,
- *   splits x N x K x P x Q x 4 bytes (0 when the sum is not split). */
+ * Dense fp32, 3x3 or 1x1 filter, no CIW_FLAG_MAXPOOL2, the first kernel
+ *   that runs the layer:
+ *   - 0 bytes: C a multiple of 4, W >= 4, and the input rows that 48
+ *     consecutive output pixels span, rows = (n - 1) stride_h + (R - 1)
+ *     dil_h + 1 with n = min(P, floor(47 / Q) + 2), with rows * W <= 448
+ *     for 3x3 (576 for 1x1);
+ *   - Q <= 192, C >= 2, and the zero-padded input rows of one 16-channel
+ *     chunk of a pixel block at most 5120 elements; the workspace is the
+ *     channel slices' partial sums, splits x N x K x P x Q x 4 bytes (0 when
+ *     the sum is not split). */
 ciw_status conv2d_implicit_workspace_bytes(const ciw_conv_desc* desc, ciw_dtype in_dtype,
                                            ciw_dtype out_dtype, uint32_t flags, size_t* bytes);
 
