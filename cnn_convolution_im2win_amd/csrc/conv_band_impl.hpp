@@ -77,7 +77,10 @@ __device__ __forceinline__ void store4<float>(float* p, float a0, float a1, floa
     *reinterpret_cast<float4*>(p) = make_float4(a0, a1, a2, a3);
 }
 
-template <typename TIn, typename TOut, int CB>
+// DV (stride_w = dil_w = 1, Q even): each (filter row, 16-channel block)
+// reads the fragments of filter columns 0 and 2 only; column 1's is taken
+// from the neighbouring lanes of those (see below), a third fewer LDS reads.
+template <typename TIn, typename TOut, int CB, bool DV>
 __global__ __launch_bounds__(kBandThreads, 1) void conv_mfma_band_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const TIn* __restrict__ bias, TOut* __restrict__ y, BandArgs a) {
@@ -279,21 +282,70 @@ __global__ __launch_bounds__(kBandThreads, 1) void conv_mfma_band_kernel(
             f32x16 acc;
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[e] = bk;   // the bias seeds the sum
-            constexpr int PF = 3;   // window fragments read ahead
-            uint4 bq[PF];
+            if constexpr (DV) {
+                // With stride_w = dil_w = 1 the window column of filter
+                // column 1 at pixel m is filter column 0's at pixel m + 1
+                // and filter column 2's at pixel m - 1, whenever those
+                // pixels are in m's output row.  So lane m takes column 1's
+                // fragment from lane m + 1's column-0 fragment (a whole-wave
+                // DPP shift), or, where m is the last pixel of its row or of
+                // the lane's 32-lane half, from lane m - 1's column-2
+                // fragment.  (With Q even neither neighbour is missing: a
+                // block's first pixel never ends a row and its last never
+                // starts one.)  The products and their order are those of
+                // the reads the fragments replace.
+                const bool next = ml != 31 && wc != a.Q - 1;
+                auto from_next = [&](uint32_t v) {
+                    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x130, 0xf, 0xf, true);
+                };
+                auto from_prev = [&](uint32_t v) {
+                    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x138, 0xf, 0xf, true);
+                };
+                auto frag_rqc = [&](int r, int q, int cb) {
+                    return *reinterpret_cast<const uint4*>(lds + base[r] + coff[q] + 32 * cb);
+                };
+                uint4 f0 = frag_rqc(0, 0, 0), f2 = frag_rqc(0, 2, 0);
 #pragma unroll
-            for (int s = 0; s < PF; ++s) bq[s] = frag(s);
+                for (int r = 0; r < R; ++r) {
 #pragma unroll
-            for (int s = 0; s < STEPS; ++s) {
-                const uint4 bv = bq[s % PF];
-                if (s + PF < STEPS) bq[s % PF] = frag(s + PF);
-                acc = mfma32<TIn>(bv, F[s], acc);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+                    for (int cb = 0; cb < CB; ++cb) {
+                        // both shifts run in every lane: a DPP move under a
+                        // partial exec mask reads nothing from the lanes
+                        // masked off, so the choice is made on the values
+                        const uint4 sn = {from_next(f0.x), from_next(f0.y), from_next(f0.z), from_next(f0.w)};
+                        const uint4 sp = {from_prev(f2.x), from_prev(f2.y), from_prev(f2.z), from_prev(f2.w)};
+                        uint4 f1;
+                        f1.x = next ? sn.x : sp.x;
+                        f1.y = next ? sn.y : sp.y;
+                        f1.z = next ? sn.z : sp.z;
+                        f1.w = next ? sn.w : sp.w;
+                        const int rn = cb + 1 < CB ? r : r + 1, cn = cb + 1 < CB ? cb + 1 : 0;
+                        acc = mfma32<TIn>(f0, F[(r * S + 0) * CB + cb], acc);
+                        const uint4 f0n = rn < R ? frag_rqc(rn, 0, cn) : f0;
+                        acc = mfma32<TIn>(f1, F[(r * S + 1) * CB + cb], acc);
+                        acc = mfma32<TIn>(f2, F[(r * S + 2) * CB + cb], acc);
+                        const uint4 f2n = rn < R ? frag_rqc(rn, 2, cn) : f2;
+                        f0 = f0n;
+                        f2 = f2n;
+                    }
+                }
+            } else {
+                constexpr int PF = 3;   // window fragments read ahead
+                uint4 bq[PF];
 #pragma unroll
-            for (int s = 0; s < STEPS; ++s) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (s + PF < STEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                for (int s = 0; s < PF; ++s) bq[s] = frag(s);
+#pragma unroll
+                for (int s = 0; s < STEPS; ++s) {
+                    const uint4 bv = bq[s % PF];
+                    if (s + PF < STEPS) bq[s % PF] = frag(s + PF);
+                    acc = mfma32<TIn>(bv, F[s], acc);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+                for (int s = 0; s < STEPS; ++s) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (s + PF < STEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
             }
             if (a.relu) {
 #pragma unroll
@@ -457,8 +509,10 @@ inline bool band_plan(const Geom& g, int out_bytes, const Epi& epi, int cus, Ban
 template <typename TIn, typename TOut, int CB>
 hipError_t launch_band_one(const BandPlan& pl, const void* x, const void* w, const void* bias,
                            void* y, hipStream_t st) {
+    // column-1 fragments from the neighbouring lanes where the geometry allows
+    const bool dv = pl.a.sw == 1 && pl.a.dw == 1 && pl.a.Q % 2 == 0;
     void (*kfn)(const uint16_t*, const uint16_t*, const TIn*, TOut*, BandArgs) =
-        conv_mfma_band_kernel<TIn, TOut, CB>;
+        dv ? conv_mfma_band_kernel<TIn, TOut, CB, true> : conv_mfma_band_kernel<TIn, TOut, CB, false>;
     if (pl.lds_bytes > 65536 && allow_dynamic_lds(reinterpret_cast<const void*>(kfn), pl.lds_bytes) != hipSuccess)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(kfn, dim3((uint32_t)pl.a.ntask), dim3(kBandThreads), pl.lds_bytes, st,

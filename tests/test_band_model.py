@@ -75,7 +75,7 @@ def band_plan(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, pool=False, cus=256, 
     ostage_off = lds
     if staged:
         lds += tiles
-    return dict(staged=staged, ostage_off=ostage_off, out_bytes=out_bytes, N=N, C=C, H=H, W=W, K=K, P=P, Q=Q, sw=sw, ph=ph, pw=pw, dh=dh, dw=dw, span=span,
+    return dict(dv=(sw == 1 and dw == 1 and Q % 2 == 0), staged=staged, ostage_off=ostage_off, out_bytes=out_bytes, N=N, C=C, H=H, W=W, K=K, P=P, Q=Q, sw=sw, ph=ph, pw=pw, dh=dh, dw=dw, span=span,
                 SR=SR, SR0=SR0, NR=NR, CS=CS, wb=wb, row_bytes=row_bytes, wv=wv, band=band,
                 nbands=nbands, ntask=N * nbands, nkh=nkh, CB=CB, cg=cg,
                 filt_off=(SR0 + span - 1) * row_bytes, lds=lds)
@@ -151,6 +151,19 @@ def replay(pl, x, wf):
                     pls = np.minimum(32 * b + np.arange(32), npx - 1)
                     pb = pix0 + pls
                     i, wc = pb // Q, pb % Q
+                    valid = 32 * b + np.arange(32) < npx
+                    # DV: filter column 1's fragment comes from lane m + 1's
+                    # column-0 fragment, or lane m - 1's column-2 fragment
+                    nxt = (np.arange(32) != 31) & (wc != Q - 1)
+                    src = np.where(nxt, np.arange(32) + 1, np.arange(32) - 1)
+                    if pl["dv"]:
+                        inb = (src >= 0) & (src < 32)
+                        assert np.all(inb[valid]), "takes a fragment from the other half or outside the wave"
+                        s = np.clip(src, 0, 31)
+                        q_src = np.where(nxt, 0, 2)
+                        # same output row, and the source's column equals the direct read's
+                        assert np.all((i[s] == i)[valid])
+                        assert np.all((wc[s] * sw + q_src * dw == wc * sw + dw)[valid])
                     acc = np.zeros((32, 32))
                     for r in range(3):
                         j = i + r * dh
@@ -168,6 +181,15 @@ def replay(pl, x, wf):
                                     off = slot * rb_bytes + (col * CS + 2 * cb + g) * 16
                                     assert np.all(off + 16 <= (slot + 1) * rb_bytes)
                                     frag = ring[slot, col, c0:c0 + 8]        # [32 pixels][8]
+                                    if pl["dv"] and q == 1:
+                                        # the kernel never reads column 1; use what the
+                                        # DPP shifts hand over (0 from outside the half)
+                                        fa = ring[slot, wc * sw, c0:c0 + 8]
+                                        fb = ring[slot, wc * sw + 2 * dw, c0:c0 + 8]
+                                        z = np.zeros((1, 8))
+                                        from_next = np.concatenate([fa[1:], z])
+                                        from_prev = np.concatenate([z, fb[:-1]])
+                                        frag = np.where(nxt[:, None], from_next, from_prev)
                                     assert not np.isnan(frag).any(), "reads an unwritten chunk"
                                     kk = np.arange(32 * kh, 32 * kh + 32)
                                     fk = np.zeros((32, 8))
