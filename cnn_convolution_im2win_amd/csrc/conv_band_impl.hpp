@@ -28,9 +28,10 @@
 //     once written: the window tensor's traffic (twice its size) is gone.
 // The filter is re-laid out inside the kernel: in the prologue each wave
 // reads one (output-channel half, 16-channel block) slice of the KCRS
-// filter with 16-byte loads, permutes it in registers into MFMA fragment
-// order and writes it to LDS, from where every wave takes its 36 fragments.
-// No workspace and no separate kernel are needed.
+// filter with consecutive 16-byte loads, passes it through its own LDS area
+// so that each lane gets its channels' taps, permutes them in registers
+// into MFMA fragment order and writes them to LDS, from where every wave
+// takes its 36 fragments.  No workspace and no separate kernel are needed.
 // The reduction is ordered (filter row, filter column, channel), a
 // reordering of the paper's window order; the sum is the same sum in
 // another order, accumulated in fp32, with the bias added in fp32 first
@@ -59,7 +60,8 @@ struct BandArgs {
     int staged;          // stores go through the per-wave LDS tile: 16 bytes per lane,
                          // whole 64-byte channel runs (16 / element size divides Q)
     int ostage_off;      // LDS byte offset of the per-wave output tiles
-    int filt_off;        // LDS byte offset of the prologue's filter staging
+    int filt_off;        // LDS byte offset of the prologue's filter staging (the
+                         // filter's raw pieces lie below it, from offset 0)
     uint32_t plane_x;    // H * W
     uint32_t plane_y;    // P * Q
     FastDiv fdQ, fdNR;
@@ -188,32 +190,51 @@ __global__ __launch_bounds__(kBandThreads, 1) void conv_mfma_band_kernel(
     // LDS above the first step's slots and read into registers while the
     // rows arrive; only after every wave has read it (the first step's
     // barrier) may the other slots be touched.
-    // filter slice of wave (fkh, fcb): lane holds F[k][c0 .. c0 + 7][0 .. 8],
-    // k = 32 fkh + ml, c0 = 16 fcb + 8 g, 72 consecutive halves of KCRS
+    // Filter slice of wave (fkh, fcb): F[32 fkh + 0 .. 31][16 fcb + 0 .. 15]
+    // [taps], 32 runs of 16 RS halves of KCRS (one an output channel, C RS
+    // halves apart), PPR 16-byte pieces each.  Load i of lane L takes piece
+    // 64 i + L of the slice (run (64 i + L) / PPR), so each load instruction
+    // reads about 1 KB of consecutive bytes rather than 32 scattered runs;
+    // the pieces go to the wave's own LDS area in that order (at the bottom
+    // of LDS: the first step's slots, written only after the filter's
+    // barrier) and each lane reads back its RS pieces: F[k][c0 .. c0 + 7]
+    // [taps], k = 32 fkh + ml, c0 = 16 fcb + 8 g.
+    constexpr int PPR = 2 * RS;
     const bool stager = wave < a.nkh * CB;
     const int fkh = stager ? wave % a.nkh : 0, fcb = stager ? wave / a.nkh : 0;
-    uint32_t raw[4 * RS];
-    {
-        const int k = 32 * fkh + ml;
-        if (stager && k < a.K) {
-            const uint4* src = reinterpret_cast<const uint4*>(w + ((size_t)k * a.C + 16 * fcb + 8 * g) * RS);
+    uint32_t fq[4 * RS];   // the lane's pieces, as words
 #pragma unroll
-            for (int i = 0; i < RS; ++i) {
-                const uint4 u = src[i];
-                raw[4 * i] = u.x; raw[4 * i + 1] = u.y; raw[4 * i + 2] = u.z; raw[4 * i + 3] = u.w;
-            }
-        } else {
+    for (int i = 0; i < 4 * RS; ++i) fq[i] = 0u;
+    if (stager) {
 #pragma unroll
-            for (int i = 0; i < 4 * RS; ++i) raw[i] = 0u;
+        for (int i = 0; i < RS; ++i) {
+            const int j = 64 * i + lane;
+            const int run = j / PPR;
+            const int k = min(32 * fkh + run, a.K - 1);   // channels past K: dropped below
+            const uint4 u =
+                *reinterpret_cast<const uint4*>(w + ((size_t)k * a.C + 16 * fcb) * RS + 8 * (j - run * PPR));
+            fq[4 * i] = u.x; fq[4 * i + 1] = u.y; fq[4 * i + 2] = u.z; fq[4 * i + 3] = u.w;
         }
     }
     const int r0 = rb(0);
     uint4 pv[8];
     int pdst = -1;
     load_item(pv, pdst, 0, r0, tid);
-    zero_pads(0, r0);
     if (stager) {
-        auto half_at = [&](int i) -> uint32_t { return (raw[i >> 1] >> (16 * (i & 1))) & 0xffffu; };
+        unsigned char* fraw = lds + wave * (32 * PPR * 16);
+#pragma unroll
+        for (int i = 0; i < RS; ++i)
+            *reinterpret_cast<uint4*>(fraw + (64 * i + lane) * 16) =
+                make_uint4(fq[4 * i], fq[4 * i + 1], fq[4 * i + 2], fq[4 * i + 3]);
+        // (LDS operations of one wave complete in order: no barrier)
+        uint32_t raw[4 * RS];
+#pragma unroll
+        for (int i = 0; i < RS; ++i) {
+            const uint4 u = *reinterpret_cast<const uint4*>(fraw + (ml * PPR + RS * g + i) * 16);
+            raw[4 * i] = u.x; raw[4 * i + 1] = u.y; raw[4 * i + 2] = u.z; raw[4 * i + 3] = u.w;
+        }
+        const uint32_t fkeep = 32 * fkh + ml < a.K ? 0xffffu : 0u;
+        auto half_at = [&](int i) -> uint32_t { return (raw[i >> 1] >> (16 * (i & 1))) & fkeep; };
         // fragment of tap t: channels c0 + 2d, c0 + 2d + 1 in dword d
 #pragma unroll
         for (int t = 0; t < RS; ++t) {
@@ -224,12 +245,13 @@ __global__ __launch_bounds__(kBandThreads, 1) void conv_mfma_band_kernel(
                 make_uint4(d[0], d[1], d[2], d[3]);
         }
     }
-    __syncthreads();   // the staged filter is complete
+    __syncthreads();   // the staged filter is complete; the raw pieces are dead
     // the fragments are read while the first rows are still arriving
     uint4 F[STEPS];
 #pragma unroll
     for (int s = 0; s < STEPS; ++s)
         F[s] = *reinterpret_cast<const uint4*>(lds + a.filt_off + ((kh * STEPS + s) * 64 + lane) * 16);
+    zero_pads(0, r0);
     const float bk = (bias != nullptr && 32 * kh + ml < a.K) ? to_f32(bias[32 * kh + ml]) : 0.f;
     store_item(pv, pdst);
     // the second step's rows: issued once the first step's have arrived (all
@@ -458,6 +480,7 @@ inline bool band_plan(const Geom& g, int out_bytes, const Epi& epi, int cus, Ban
     a.nkh = g.K > 32 ? 2 : 1;
     const int CB = g.C / 16;
     const int64_t filt_bytes = (int64_t)a.nkh * 9 * CB * 64 * 16;
+    const int64_t raw_bytes = (int64_t)a.nkh * CB * 32 * 18 * 16;   // the stager waves' raw pieces
     const int64_t lds_max = 160 * 1024;
     // bands: one per CU in total where the batch allows, at least 8 rows each
     const int64_t N = std::max(g.N, 1);
@@ -478,7 +501,7 @@ inline bool band_plan(const Geom& g, int out_bytes, const Epi& epi, int cus, Ban
         int sr0 = std::max(1, sr / 2);
         while (sr0 > 1 && (sr0 + a.span - 1) * per_row > kBandThreads) --sr0;
         const int64_t r0 = sr0 + a.span - 1;
-        const int64_t lds = std::max(nr * row_bytes, r0 * row_bytes + filt_bytes);
+        const int64_t lds = std::max(nr * row_bytes, std::max(r0 * row_bytes, raw_bytes) + filt_bytes);
         if (lds <= lds_max && sr * per_row <= kBandThreads && r0 * per_row <= kBandThreads) {
             a.SR = sr;
             a.SR0 = sr0;
@@ -488,7 +511,7 @@ inline bool band_plan(const Geom& g, int out_bytes, const Epi& epi, int cus, Ban
     }
     if (a.SR == 0) return false;
     a.row_bytes = (int)row_bytes;
-    a.filt_off = (int)((a.SR0 + a.span - 1) * row_bytes);
+    a.filt_off = (int)std::max<int64_t>((a.SR0 + a.span - 1) * row_bytes, raw_bytes);
     a.relu = epi.relu ? 1 : 0;
     a.vec = g.Q % 4 == 0 ? 1 : 0;
     // per-wave output tiles (1 KB of outputs a round, rows padded by 16 B)

@@ -51,6 +51,7 @@ def band_plan(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, pool=False, cus=256, 
     nkh = 2 if K > 32 else 1
     CB = C // 16
     filt_bytes = nkh * 9 * CB * 64 * 16
+    raw_bytes = nkh * CB * 32 * 18 * 16          # the stager waves' raw filter pieces
     Nn = max(N, 1)
     nb = max(1, min(P, (cus + Nn - 1) // Nn))
     band = max((P + nb - 1) // nb, min(P, 8))
@@ -63,7 +64,7 @@ def band_plan(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, pool=False, cus=256, 
         while sr0 > 1 and (sr0 + span - 1) * per_row > THREADS:
             sr0 -= 1
         r0 = sr0 + span - 1
-        need = max(nr * row_bytes, r0 * row_bytes + filt_bytes)
+        need = max(nr * row_bytes, max(r0 * row_bytes, raw_bytes) + filt_bytes)
         if need <= LDS_MAX and sr * per_row <= THREADS and r0 * per_row <= THREADS:
             SR, SR0, NR, lds = sr, sr0, nr, need
             break
@@ -78,7 +79,7 @@ def band_plan(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, pool=False, cus=256, 
     return dict(dv=(sw == 1 and dw == 1 and Q % 2 == 0), staged=staged, ostage_off=ostage_off, out_bytes=out_bytes, N=N, C=C, H=H, W=W, K=K, P=P, Q=Q, sw=sw, ph=ph, pw=pw, dh=dh, dw=dw, span=span,
                 SR=SR, SR0=SR0, NR=NR, CS=CS, wb=wb, row_bytes=row_bytes, wv=wv, band=band,
                 nbands=nbands, ntask=N * nbands, nkh=nkh, CB=CB, cg=cg,
-                filt_off=(SR0 + span - 1) * row_bytes, lds=lds)
+                filt_off=max((SR0 + span - 1) * row_bytes, raw_bytes), raw_bytes=raw_bytes, lds=lds)
 
 
 def replay(pl, x, wf):
@@ -250,6 +251,47 @@ def test_band_model_against_oracle(shape):
     ref = oracle.conv2d(x, w, None, (1, sw), (pad, pad), (dil, dil), 1)
     assert y.shape == ref.shape
     np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("C,K", [(16, 8), (32, 40), (48, 64), (64, 64), (64, 33), (16, 64)])
+def test_band_filter_pieces(C, K):
+    """The prologue's coalesced filter copy: load i of lane L of stager wave
+    (fkh, fcb) takes 16-byte piece 64 i + L of the wave's slice, the pieces
+    go to the wave's LDS area in that order, and lane (ml, g) reads back
+    pieces ml PPR + RS g + i.  Replayed on a KCRS filter of distinct values:
+    every load lies inside the filter, every raw area lies below the
+    fragment staging, and each lane's read-back is F[k][c0 .. c0 + 7][taps]
+    (k = 32 fkh + ml, c0 = 16 fcb + 8 g), the lanes past K dropped."""
+    pl = band_plan(2, C, 12, 16, K, 3, 3, 1, 1, 1, 1, 1, 1)
+    assert pl is not None
+    RS, PPR = 9, 18
+    nkh, CB = pl["nkh"], pl["CB"]
+    wflat = np.arange(K * C * RS, dtype=np.int64)     # halves of KCRS, each its own index
+    area = 32 * PPR * 16
+    assert nkh * CB * area == pl["raw_bytes"] <= pl["filt_off"]
+    assert pl["filt_off"] + nkh * RS * CB * 1024 <= pl["lds"]
+    for wave in range(nkh * CB):
+        fkh, fcb = wave % nkh, wave // nkh
+        lds = np.full(area // 2, -1, dtype=np.int64)   # the wave's area, in halves
+        for i in range(RS):
+            for lane in range(64):
+                j = 64 * i + lane
+                run = j // PPR
+                k = min(32 * fkh + run, K - 1)
+                h0 = (k * C + 16 * fcb) * RS + 8 * (j - run * PPR)   # first half of the load
+                assert h0 % 8 == 0 and 0 <= h0 and h0 + 8 <= K * C * RS
+                lds[(64 * i + lane) * 8:(64 * i + lane) * 8 + 8] = wflat[h0:h0 + 8]
+        assert (lds >= 0).all()
+        for lane in range(64):
+            ml, g = lane % 32, lane // 32
+            got = np.concatenate([lds[(ml * PPR + RS * g + i) * 8:(ml * PPR + RS * g + i) * 8 + 8]
+                                  for i in range(RS)])
+            k = 32 * fkh + ml
+            if k >= K:
+                continue                                 # masked to zero by the perm
+            c0 = 16 * fcb + 8 * g
+            want = wflat.reshape(K, C, RS)[k, c0:c0 + 8, :].reshape(-1)
+            assert np.array_equal(got, want), (wave, lane)
 
 
 def test_band_plan_of_the_fp16_layer():
