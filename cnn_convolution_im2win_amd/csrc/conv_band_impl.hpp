@@ -196,9 +196,9 @@ __global__ __launch_bounds__(kBandThreads, 1) void conv_mfma_band_kernel(
     // 64 i + L of the slice (run (64 i + L) / PPR), so each load instruction
     // reads about 1 KB of consecutive bytes rather than 32 scattered runs;
     // the pieces go to the wave's own LDS area in that order (at the bottom
-    // of LDS: the first step's slots, written only after the filter's
-    // barrier) and each lane reads back its RS pieces: F[k][c0 .. c0 + 7]
-    // [taps], k = 32 fkh + ml, c0 = 16 fcb + 8 g.
+    // of LDS, below the fragment staging: ring slots that no wave writes
+    // before the filter's barrier) and each lane reads back its RS pieces:
+    // F[k][c0 .. c0 + 7][taps], k = 32 fkh + ml, c0 = 16 fcb + 8 g.
     constexpr int PPR = 2 * RS;
     const bool stager = wave < a.nkh * CB;
     const int fkh = stager ? wave % a.nkh : 0, fcb = stager ? wave / a.nkh : 0;
