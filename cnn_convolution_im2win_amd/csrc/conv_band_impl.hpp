@@ -413,8 +413,7 @@ __global__ __launch_bounds__(kBandThreads, 1) void conv_mfma_band_kernel(
                     const int kk = 32 * kh + rd * RPR + rr;
                     const int p = 32 * b + seg * (16 / EB);    // pixel of the step
                     if (kk < a.K && p < npx)
-                        *reinterpret_cast<uint4*>(yband + (uint32_t)EB * ((uint32_t)kk * a.plane_y +
-                                                                        (uint32_t)(pix0 + p))) = v;
+                        store_stream(yband + (uint32_t)EB * ((uint32_t)kk * a.plane_y + (uint32_t)(pix0 + p)), v);
                 }
             } else if (k < a.K) {
                 // byte offset of the lane's channel at the step's first pixel
@@ -425,22 +424,20 @@ __global__ __launch_bounds__(kBandThreads, 1) void conv_mfma_band_kernel(
                     if (a.vec) {
                         if (p < npx) {
                             if constexpr (EB == 2)
-                                *reinterpret_cast<uint2*>(yband + (yoff + 2u * (uint32_t)p)) =
-                                    make_uint2(pk[2 * jq], pk[2 * jq + 1]);
+                                store_stream(yband + (yoff + 2u * (uint32_t)p), make_uint2(pk[2 * jq], pk[2 * jq + 1]));
                             else
-                                *reinterpret_cast<uint4*>(yband + (yoff + 4u * (uint32_t)p)) =
-                                    make_uint4(pk[4 * jq], pk[4 * jq + 1], pk[4 * jq + 2], pk[4 * jq + 3]);
+                                store_stream(yband + (yoff + 4u * (uint32_t)p),
+                                             make_uint4(pk[4 * jq], pk[4 * jq + 1], pk[4 * jq + 2], pk[4 * jq + 3]));
                         }
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (p + e < npx) {
                                 if constexpr (EB == 2)
-                                    *reinterpret_cast<uint16_t*>(yband + (yoff + 2u * (uint32_t)(p + e))) =
-                                        (uint16_t)(pk[2 * jq + (e >> 1)] >> (16 * (e & 1)));
+                                    store_stream(yband + (yoff + 2u * (uint32_t)(p + e)),
+                                                 (uint16_t)(pk[2 * jq + (e >> 1)] >> (16 * (e & 1))));
                                 else
-                                    *reinterpret_cast<uint32_t*>(yband + (yoff + 4u * (uint32_t)(p + e))) =
-                                        pk[4 * jq + e];
+                                    store_stream(yband + (yoff + 4u * (uint32_t)(p + e)), pk[4 * jq + e]);
                             }
                     }
                 }

@@ -57,4 +57,28 @@ __device__ __forceinline__ T zero_elem() {
     return from_f32<T>(0.0f);
 }
 
+// Stores marked non-temporal (the nt bit: the lines are not kept in the
+// caches for reuse).  Whether they pay is measured per kernel: the band
+// kernel's output stores (whole 64-byte runs; its input rows are re-read
+// from L2 by the neighbouring band) are faster this way, while the
+// few-channel and depthwise in-LDS kernels' stores were much slower, so
+// those keep plain stores.
+typedef uint32_t u32x4_vec __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_vec __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void store_stream(void* p, uint4 v) {
+    const u32x4_vec t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4_vec*>(p));
+}
+__device__ __forceinline__ void store_stream(void* p, uint2 v) {
+    const u32x2_vec t = {v.x, v.y};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x2_vec*>(p));
+}
+__device__ __forceinline__ void store_stream(void* p, uint32_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+__device__ __forceinline__ void store_stream(void* p, uint16_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<uint16_t*>(p));
+}
+
 }  // namespace ciw
