@@ -677,7 +677,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_mfma_rows_kernel(
                     take();
                     nxt = vec_at(src);
                 }
-                store_stream(dp, cur);   // non-temporal: measured faster on the stem's 205 MB
+                *reinterpret_cast<uint4*>(dp) = cur;
                 cur = nxt;
             }
         } else {

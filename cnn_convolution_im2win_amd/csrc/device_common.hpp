@@ -60,10 +60,11 @@ __device__ __forceinline__ T zero_elem() {
 // Stores marked non-temporal (the nt bit: the lines are not kept in the
 // caches for reuse).  Whether they pay is measured per kernel: the band
 // kernel's output stores (whole 64-byte runs; its input rows are re-read
-// from L2 by the neighbouring band) and the materialised row kernel's
-// 16-byte output stores are faster this way, while the few-channel and
-// depthwise in-LDS kernels' stores and the repack's window-tensor stores
-// (read again right after) were much slower, so those keep plain stores.
+// from L2 by the neighbouring band) are faster this way.  The few-channel
+// and depthwise in-LDS kernels' stores and the repack's window-tensor
+// stores (read again right after) were much slower, and the materialised
+// row kernel's faster in one layer's full call but slower on its own, so
+// those keep plain stores.
 typedef uint32_t u32x4_vec __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_vec __attribute__((ext_vector_type(2)));
 
