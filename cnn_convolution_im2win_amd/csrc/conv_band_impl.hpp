@@ -184,12 +184,13 @@ __global__ __launch_bounds__(kBandThreads, 1) void conv_mfma_band_kernel(
     };
 
     // ---- prologue.  Loads are issued in the order they are needed: the
-    // filter slice (mostly L2 hits), the first step's rows (ring slots
-    // [0, rb(0))), and once those are in, the second step's rows (kept in
-    // registers until the end of the first step).  The filter is staged in
-    // LDS above the first step's slots and read into registers while the
-    // rows arrive; only after every wave has read it (the first step's
-    // barrier) may the other slots be touched.
+    // filter slice; once it is in, the first step's rows (ring slots
+    // [0, rb(0)); every CU asks for the same filter at the start, and rows
+    // requested alongside it delay it); once those are in, the second
+    // step's rows (kept in registers until the end of the first step).  The
+    // filter is staged in LDS above the first step's slots and read into
+    // registers while the rows arrive; only after every wave has read it
+    // (the first step's barrier) may the other slots be touched.
     // Filter slice of wave (fkh, fcb): F[32 fkh + 0 .. 31][16 fcb + 0 .. 15]
     // [taps], 32 runs of 16 RS halves of KCRS (one an output channel, C RS
     // halves apart), PPR 16-byte pieces each.  Load i of lane L takes piece
@@ -219,7 +220,6 @@ __global__ __launch_bounds__(kBandThreads, 1) void conv_mfma_band_kernel(
     const int r0 = rb(0);
     uint4 pv[8];
     int pdst = -1;
-    load_item(pv, pdst, 0, r0, tid);
     if (stager) {
         unsigned char* fraw = lds + wave * (32 * PPR * 16);
 #pragma unroll
@@ -245,6 +245,7 @@ __global__ __launch_bounds__(kBandThreads, 1) void conv_mfma_band_kernel(
                 make_uint4(d[0], d[1], d[2], d[3]);
         }
     }
+    load_item(pv, pdst, 0, r0, tid);
     __syncthreads();   // the staged filter is complete; the raw pieces are dead
     // the fragments are read while the first rows are still arriving
     uint4 F[STEPS];
