@@ -245,13 +245,24 @@ def loop_ms(stream, fn, steps: int, warmup: int):
     return e0.elapsed_time(e1) / steps, wall
 
 
+CALL_REPS = 5   # repetitions of a per-call loop; the median is reported
+
+
+def call_ms(stream, fn, steps: int, warmup: int, reps: int = CALL_REPS):
+    """Per-call time of `fn`: `reps` runs of `loop_ms` (K calls back to back
+    between two HIP events), returning (median, best) of the runs' means, so
+    that one slow burst on a shared box does not decide the figure."""
+    runs = sorted(loop_ms(stream, fn, steps, warmup if i == 0 else 1)[0] for i in range(reps))
+    return runs[len(runs) // 2], runs[0]
+
+
 def time_steps(step: Step, steps: int, warmup: int):
     """K timed steps, each the two C-ABI calls on the step's stream,
     bracketed by a device synchronisation on both sides (wall clock) and by
-    one pair of HIP events on that stream.  Then the mean duration of each
-    call on its own: K transform calls back to back, and K contraction calls
-    back to back on the window tensor the last transform left (HIP events
-    around each loop).  (Replaying the calls as HIP graphs was measured
+    one pair of HIP events on that stream.  Then each call on its own: K
+    transform calls back to back, and K contraction calls back to back on the
+    window tensor the last transform left (HIP events around each loop; the
+    median of CALL_REPS such loops).  (Replaying the calls as HIP graphs was measured
     slower here than launching them directly, so the step launches them
     directly.)"""
     def one():
@@ -259,8 +270,8 @@ def time_steps(step: Step, steps: int, warmup: int):
         step.contract()
     settle(one)
     gpu_ms, wall_ms = loop_ms(step.stream, one, steps, warmup)
-    tr_ms, _ = loop_ms(step.stream, step.transform, steps, 2)
-    co_ms, _ = loop_ms(step.stream, step.contract, steps, 2)
+    tr_ms, _ = call_ms(step.stream, step.transform, steps, 2)
+    co_ms, _ = call_ms(step.stream, step.contract, steps, 2)
     return wall_ms, gpu_ms, tr_ms, co_ms
 
 
@@ -448,7 +459,7 @@ def time_fp32_kernels(step: Step, steps: int, warmup: int):
             if st != 0:
                 raise RuntimeError(f"conv2d_fwd ({name}): status {st}")
         settle(call, 0.2)
-        ms, _ = loop_ms(step.stream, call, steps, warmup)
+        ms, _ = call_ms(step.stream, call, steps, warmup)
         out[name] = {"contract_ms": round(ms, 5),
                      "contract_tflops": round(step.flops() / (ms * 1e-3) / 1e12, 3)}
     return out
@@ -645,11 +656,13 @@ def measure_layer2(L: workloads.Layer, steps: int, warmup: int, iters: int, flus
     if call is not None:
         settle(call)   # (the traces before ran cold passes: 1 GiB reads between calls)
     if call is not None and not trace:
-        ms, wall = loop_ms(step.stream, call, steps, warmup)
+        _, wall = loop_ms(step.stream, call, steps, warmup)
+        ms, _ = call_ms(step.stream, call, steps, 1)
         res["in_lds"] = {"call_ms": round(ms, 5), "wall_ms": round(wall, 5), "workspace_bytes": nbytes,
                          "tflops": round(fl / (ms * 1e-3) / 1e12, 3)}
     elif call is not None:
-        ms, wall = loop_ms(step.stream, call, steps, warmup)
+        _, wall = loop_ms(step.stream, call, steps, warmup)
+        ms, _ = call_ms(step.stream, call, steps, 1)
         iw = trace_stats(kernel_trace(step.stream, call, iters))
         ic = trace_stats(kernel_trace(step.stream, call, iters, flush))
         ibytes = step.bytes_x() + step.bytes_w() + step.bytes_b() + step.bytes_y()
