@@ -104,6 +104,14 @@ __global__ __launch_bounds__(kT, 1) void conv_fp32_mfma16_kernel(
     const int kb = rest / a.nimg;
     const int k0 = kb * kM;
     const int p0 = pg * kPix;
+    // the bias of the thread's (at most two) outputs of the final sum,
+    // requested now so that its latency is not paid at the end
+    static_assert(kM * kPix <= 2 * kT, "two final-sum outputs a thread");
+    float bpre[2] = {0.f, 0.f};
+    if (bias != nullptr) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bpre[j] = bias[min(k0 + min(tid + j * kT, kM * kPix - 1) / kPix, a.K - 1)];
+    }
     const int h_lo = p0 / a.Q;
 
     // Waves 0-3 take gA groups of 4 channels each and waves 4-7 gB <= gA:
@@ -333,7 +341,10 @@ __global__ __launch_bounds__(kT, 1) void conv_fp32_mfma16_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) reinterpret_cast<float*>(wbase)[(t3 * 4 + i) * 64 + lane] = acc[t3][i];
     __syncthreads();
-    for (int o = tid; o < kM * kPix; o += kT) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int o = tid + j * kT;
+        if (o >= kM * kPix) break;
         const int ch = o / kPix, px = o - ch * kPix;
         const int t3 = px >> 4, l = 16 * (ch >> 2) + (px & 15), i = ch & 3;
         float s = 0.f;
@@ -341,7 +352,7 @@ __global__ __launch_bounds__(kT, 1) void conv_fp32_mfma16_kernel(
         for (int v = 0; v < kWaves; ++v) s += smem[v * (a.buf + 256) + (t3 * 4 + i) * 64 + l];
         const int k = k0 + ch, p = p0 + px;
         if (k < a.K && p < a.PQ) {
-            if (bias) s += bias[k];
+            if (bias) s += bpre[j];
             if (a.relu) s = fmaxf(s, 0.f);
             y[((size_t)n_img * a.K + k) * a.PQ + p] = s;
         }
