@@ -82,8 +82,10 @@ def band_plan(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, pool=False, cus=256, 
                 filt_off=max((SR0 + span - 1) * row_bytes, raw_bytes), raw_bytes=raw_bytes, lds=lds)
 
 
-def replay(pl, x, wf):
-    """Replay every band; returns y (fp64) built from the ring contents."""
+def replay(pl, x, wf, dv_rule=None):
+    """Replay every band; returns y (fp64) built from the ring contents.
+    dv_rule (tests only) replaces the kernel's choice of neighbour lane for
+    filter column 1: a function (ml, wc, Q) -> bool array, True for m + 1."""
     N, C, H, W, K, P, Q = (pl[k] for k in ("N", "C", "H", "W", "K", "P", "Q"))
     CS, NR, SR, span, wb, cg, wv = (pl[k] for k in ("CS", "NR", "SR", "span", "wb", "cg", "wv"))
     SR0 = pl["SR0"]
@@ -156,6 +158,8 @@ def replay(pl, x, wf):
                     # DV: filter column 1's fragment comes from lane m + 1's
                     # column-0 fragment, or lane m - 1's column-2 fragment
                     nxt = (np.arange(32) != 31) & (wc != Q - 1)
+                    if dv_rule is not None:
+                        nxt = dv_rule(np.arange(32), wc, Q)
                     src = np.where(nxt, np.arange(32) + 1, np.arange(32) - 1)
                     if pl["dv"]:
                         inb = (src >= 0) & (src < 32)
@@ -292,6 +296,39 @@ def test_band_filter_pieces(C, K):
             c0 = 16 * fcb + 8 * g
             want = wflat.reshape(K, C, RS)[k, c0:c0 + 8, :].reshape(-1)
             assert np.array_equal(got, want), (wave, lane)
+
+
+# Plausible mistakes in the neighbour-lane rule; each must be caught (by the
+# source-column check or by the comparison with the oracle) on some layer.
+DV_MUTANTS = {
+    "ignores row ends": lambda ml, wc, Q: ml != 31,
+    "ignores the half's last lane": lambda ml, wc, Q: wc != Q - 1,
+    "always the previous lane": lambda ml, wc, Q: np.zeros(32, dtype=bool),
+    "off by one at the row end": lambda ml, wc, Q: (ml != 31) & (wc != Q - 2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DV_MUTANTS))
+def test_band_model_catches_wrong_neighbour_rule(name):
+    caught = False
+    for shape in SHAPES:
+        N, C, H, W, K, sw, pad, dil = shape
+        pl = band_plan(N, C, H, W, K, 3, 3, 1, sw, pad, pad, dil, dil)
+        if not pl["dv"]:
+            continue
+        rng = np.random.default_rng(sum(shape))
+        x = rng.standard_normal((N, C, H, W))
+        w = rng.standard_normal((K, C, 3, 3))
+        try:
+            y = replay(pl, x, w, dv_rule=DV_MUTANTS[name])
+        except AssertionError:
+            caught = True
+            break
+        ref = oracle.conv2d(x, w, None, (1, sw), (pad, pad), (dil, dil), 1)
+        if not np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max()):
+            caught = True
+            break
+    assert caught, f"the model accepts the mutant rule: {name}"
 
 
 def test_band_plan_of_the_fp16_layer():
