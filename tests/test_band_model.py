@@ -257,19 +257,17 @@ def test_band_model_against_oracle(shape):
     np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
 
-@pytest.mark.parametrize("C,K", [(16, 8), (32, 40), (48, 64), (64, 64), (64, 33), (16, 64)])
-def test_band_filter_pieces(C, K):
-    """The prologue's coalesced filter copy: load i of lane L of stager wave
-    (fkh, fcb) takes 16-byte piece 64 i + L of the wave's slice, the pieces
-    go to the wave's LDS area in that order, and lane (ml, g) reads back
-    pieces ml PPR + RS g + i.  Replayed on a KCRS filter of distinct values:
-    every load lies inside the filter, every raw area lies below the
-    fragment staging, and each lane's read-back is F[k][c0 .. c0 + 7][taps]
-    (k = 32 fkh + ml, c0 = 16 fcb + 8 g), the lanes past K dropped."""
+def filter_copy_check(C, K, piece_of=None):
+    """Replay the prologue's coalesced filter copy for one layer (see
+    test_band_filter_pieces); piece_of(ml, g, i) (tests only) replaces the
+    kernel's read-back index ml PPR + RS g + i.  Raises AssertionError on
+    any mismatch or out-of-range access."""
     pl = band_plan(2, C, 12, 16, K, 3, 3, 1, 1, 1, 1, 1, 1)
     assert pl is not None
     RS, PPR = 9, 18
     nkh, CB = pl["nkh"], pl["CB"]
+    if piece_of is None:
+        piece_of = lambda ml, g, i: ml * PPR + RS * g + i
     wflat = np.arange(K * C * RS, dtype=np.int64)     # halves of KCRS, each its own index
     area = 32 * PPR * 16
     assert nkh * CB * area == pl["raw_bytes"] <= pl["filt_off"]
@@ -288,14 +286,37 @@ def test_band_filter_pieces(C, K):
         assert (lds >= 0).all()
         for lane in range(64):
             ml, g = lane % 32, lane // 32
-            got = np.concatenate([lds[(ml * PPR + RS * g + i) * 8:(ml * PPR + RS * g + i) * 8 + 8]
-                                  for i in range(RS)])
+            pieces = [piece_of(ml, g, i) for i in range(RS)]
+            assert all(0 <= q < 32 * PPR for q in pieces), "reads outside the wave's area"
+            got = np.concatenate([lds[q * 8:q * 8 + 8] for q in pieces])
             k = 32 * fkh + ml
             if k >= K:
                 continue                                 # masked to zero by the perm
             c0 = 16 * fcb + 8 * g
             want = wflat.reshape(K, C, RS)[k, c0:c0 + 8, :].reshape(-1)
             assert np.array_equal(got, want), (wave, lane)
+
+
+@pytest.mark.parametrize("C,K", [(16, 8), (32, 40), (48, 64), (64, 64), (64, 33), (16, 64)])
+def test_band_filter_pieces(C, K):
+    """The prologue's coalesced filter copy: load i of lane L of stager wave
+    (fkh, fcb) takes 16-byte piece 64 i + L of the wave's slice, the pieces
+    go to the wave's LDS area in that order, and lane (ml, g) reads back
+    pieces ml PPR + RS g + i.  Replayed on a KCRS filter of distinct values:
+    every load lies inside the filter, every raw area lies below the
+    fragment staging, and each lane's read-back is F[k][c0 .. c0 + 7][taps]
+    (k = 32 fkh + ml, c0 = 16 fcb + 8 g), the lanes past K dropped."""
+    filter_copy_check(C, K)
+
+
+@pytest.mark.parametrize("name,piece_of", [
+    ("channel halves swapped", lambda ml, g, i: ml * 18 + 9 * (1 - g) + i),
+    ("run stride of a half", lambda ml, g, i: ml * 9 + 9 * g + i),
+    ("pieces reversed", lambda ml, g, i: ml * 18 + 9 * g + (8 - i)),
+])
+def test_band_filter_copy_mutants_caught(name, piece_of):
+    with pytest.raises(AssertionError):
+        filter_copy_check(64, 64, piece_of)
 
 
 # Plausible mistakes in the neighbour-lane rule; each must be caught (by the
